@@ -1,0 +1,8 @@
+"""CPU float64 oracle for the Mamba2 SSD varlen scan.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product path. It shares no code with
+the HIP library.
+"""
+from .oracle import (load, ssd_varlen, varlen_metadata, checkpoint_plan,  # noqa: F401
+                     num_threads)

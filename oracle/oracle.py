@@ -1,0 +1,124 @@
+"""ctypes wrapper over liboracle.so (float64 CPU reference; test infrastructure).
+
+Inputs are widened to float64 here (bfloat16 and float32 widen exactly), so the
+oracle sees exactly the values the GPU sees.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build_oracle
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_F64P = ctypes.POINTER(ctypes.c_double)
+_cache = {}
+
+
+def load(path=LIB):
+    """Load (building if absent) the oracle library at `path`."""
+    if path in _cache:
+        return _cache[path]
+    if not os.path.exists(path):
+        if path != LIB:
+            raise FileNotFoundError(path)
+        build_oracle()
+    lib = ctypes.CDLL(path)
+    lib.oracle_ssd_varlen.restype = ctypes.c_int
+    lib.oracle_ssd_varlen.argtypes = [
+        ctypes.c_int32, _I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _I32P, ctypes.c_int32, _F64P,
+        _F64P, _F64P, ctypes.c_int32]
+    lib.oracle_varlen_metadata.restype = ctypes.c_int
+    lib.oracle_varlen_metadata.argtypes = [ctypes.c_int32, _I32P, ctypes.c_int32, ctypes.c_int32,
+                                           _I32P, _I32P, _I32P, _I32P, _I32P]
+    lib.oracle_checkpoint_plan.restype = ctypes.c_int
+    lib.oracle_checkpoint_plan.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32, _I32P,
+                                           _I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           _I32P, _I32P]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _cache[path] = lib
+    return lib
+
+
+def _np(a, dtype):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):          # torch tensor (any float dtype) -> numpy
+        a = a.detach().cpu()
+        a = a.double().numpy() if dtype == np.float64 else a.numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def _p(a, ptype):
+    return None if a is None else a.ctypes.data_as(ptype)
+
+
+def num_threads(lib=None):
+    return (lib or load()).oracle_num_threads()
+
+
+def ssd_varlen(x, dt, dt_bias, A, B, C, D, cu_seqlens, initial_states=None, has_initial_state=None,
+               chunk_size=0, nthreads=0, lib=None):
+    """Token-by-token float64 recurrence. Returns (y, final_states, chunk_states|None)."""
+    lib = lib or load()
+    x, dt, B, C = (_np(v, np.float64) for v in (x, dt, B, C))
+    dt_bias, A, D, init = (_np(v, np.float64) for v in (dt_bias, A, D, initial_states))
+    cu = _np(cu_seqlens, np.int32)
+    has = _np(has_initial_state, np.int32)
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    S = cu.shape[0] - 1
+    y = np.empty((T, H, P), np.float64)
+    final = np.empty((S, H, P, N), np.float64)
+    chunk_states = None
+    if chunk_size:
+        lens = np.diff(cu.astype(np.int64))
+        nch = int(((lens + chunk_size - 1) // chunk_size).sum())
+        chunk_states = np.full((nch, H, P, N), np.nan, np.float64)
+    rc = lib.oracle_ssd_varlen(S, _p(cu, _I32P), H, P, N, G, _p(x, _F64P), _p(dt, _F64P),
+                               _p(dt_bias, _F64P), _p(A, _F64P), _p(B, _F64P), _p(C, _F64P),
+                               _p(D, _F64P), _p(init, _F64P), _p(has, _I32P), int(chunk_size),
+                               _p(chunk_states, _F64P), _p(y, _F64P), _p(final, _F64P),
+                               int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_ssd_varlen failed ({rc})")
+    return y, final, chunk_states
+
+
+def varlen_metadata(cu_seqlens, chunk_size, max_chunks, lib=None):
+    """Chunk grid by enumeration: dict of int32 arrays + nchunks."""
+    lib = lib or load()
+    cu = _np(cu_seqlens, np.int32)
+    S = cu.shape[0] - 1
+    off = np.empty(max_chunks + 1, np.int32)
+    sidx = np.empty(max_chunks, np.int32)
+    start = np.empty(S + 1, np.int32)
+    order = np.empty(max(S, 1), np.int32)
+    n = np.zeros(1, np.int32)
+    rc = lib.oracle_varlen_metadata(S, _p(cu, _I32P), int(chunk_size), int(max_chunks),
+                                    _p(off, _I32P), _p(sidx, _I32P), _p(start, _I32P),
+                                    _p(n, _I32P), _p(order, _I32P))
+    if rc != 0:
+        raise ValueError(f"oracle_varlen_metadata failed ({rc})")
+    return dict(chunk_offsets=off, chunk_seq_idx=sidx, seq_chunk_start=start,
+                nchunks=int(n[0]), seq_order=order[:S])
+
+
+def checkpoint_plan(cu_seqlens, seq_chunk_start, max_chunks, block_table, block_size, chunk_size,
+                    num_computed_tokens=None, lib=None):
+    """Block-checkpoint plan: (ckpt_src [S,max_blocks], chunk_state_dst [max_chunks])."""
+    lib = lib or load()
+    cu = _np(cu_seqlens, np.int32)
+    start = _np(seq_chunk_start, np.int32)
+    bt = _np(block_table, np.int32)
+    ncomp = _np(num_computed_tokens, np.int32)
+    S, maxb = bt.shape
+    src = np.empty((S, maxb), np.int32)
+    dst = np.empty(max_chunks, np.int32)
+    rc = lib.oracle_checkpoint_plan(S, _p(cu, _I32P), _p(start, _I32P), int(max_chunks),
+                                    _p(ncomp, _I32P), _p(bt, _I32P), maxb, int(block_size),
+                                    int(chunk_size), _p(src, _I32P), _p(dst, _I32P))
+    if rc != 0:
+        raise ValueError(f"oracle_checkpoint_plan failed ({rc})")
+    return src, dst

@@ -1,0 +1,253 @@
+/*
+ * ssd_oracle.c -- plain, slow, obviously correct CPU reference for the Mamba2
+ * SSD varlen scan, in float64.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it. It shares no code, header, table or helper with the HIP library.
+ *
+ * Sources (the pages are three public vLLM pull requests):
+ *  - "[Model] Mamba2 varlen and metadata refactor" (vLLM PR #21467), Purpose:
+ *    tokens of all requests are packed along one axis, (seqlen, hiddendim),
+ *    with cu_seqlens marking where each request starts; metadata is built once.
+ *  - "[Bugfix] Mamba2 SSD varlen bug fix initstates decay, improve test, assert
+ *    chunk pwr 2" (vLLM PR #21783), Purpose: the initial (or previous-chunk)
+ *    state must carry exactly the decay accumulated up to and including the
+ *    current token; chunk_size must be a power of two and does not change the
+ *    result.
+ *  - "[Model Runner V2] Automatic prefix caching for GDN hybrid models"
+ *    (vLLM PR #54637), Purpose and the diff fragment of the block-checkpoint
+ *    scatter: per-chunk states are exported, and the state at each cache-block
+ *    boundary is written to block_table slots; sequences whose computed prefix
+ *    is not chunk-aligned get no interior checkpoints; the source chunk is
+ *    clamped to the sequence's own chunks.
+ *
+ * The recurrence itself (the pages print no formula; this is the plainest
+ * reading of the problem statement, with ZOH decay and Euler input):
+ *     delta_t = softplus(dt[t,h] + dt_bias[h])
+ *     h_t     = exp(delta_t * A[h]) * h_{t-1} + delta_t * x_t (outer) B_t
+ *     y_t     = h_t . C_t + D[h] * x_t
+ * run token by token per (sequence, head) from the sequence's initial state
+ * (or zero). The chunked scan is an exact re-association of this map, so the
+ * oracle does not chunk: chunk_size only decides where states are recorded.
+ *
+ * Layouts (row-major): x, y (T,H,P); dt (T,H); B, C (T,G,N); states (.,H,P,N).
+ * Head h reads group g = h / (H/G).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Softplus, identity above 20 (the usual threshold; never reached by the
+ * workloads' dt distribution). */
+static double oracle_softplus(double u)
+{
+    if (u > 20.0)
+        return u;
+    return log1p(exp(u));
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * The recurrence oracle.
+ *   chunk_size > 0 and chunk_states != NULL: after the last token of every
+ *   chunk (chunks cut per sequence from its first token, chunk_size tokens
+ *   each, the last one possibly shorter) the state is copied to
+ *   chunk_states[c], c = the chunk's index in the packed batch.
+ *   has_init == NULL with init != NULL means every sequence has one;
+ *   init == NULL means all start from zero. dt_bias / D may be NULL (zero).
+ * Returns 0, or -1 on bad shapes.
+ */
+int oracle_ssd_varlen(int32_t nseqs, const int32_t *cu_seqlens, int32_t nheads, int32_t headdim,
+                      int32_t dstate, int32_t ngroups, const double *x, const double *dt,
+                      const double *dt_bias, const double *A, const double *B, const double *C,
+                      const double *D, const double *init, const int32_t *has_init,
+                      int32_t chunk_size, double *chunk_states, double *y, double *final_states,
+                      int32_t nthreads)
+{
+    const int64_t H = nheads, P = headdim, N = dstate, G = ngroups;
+    if (nseqs < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0)
+        return -1;
+    const int64_t heads_per_group = H / G;
+
+    /* index of each sequence's first chunk (only used to place chunk states) */
+    int64_t *first_chunk = (int64_t *)calloc((size_t)nseqs + 1, sizeof(int64_t));
+    if (!first_chunk)
+        return -1;
+    for (int32_t s = 0; s < nseqs; ++s) {
+        int64_t len = (int64_t)cu_seqlens[s + 1] - cu_seqlens[s];
+        int64_t nch = chunk_size > 0 ? (len + chunk_size - 1) / chunk_size : 0;
+        first_chunk[s + 1] = first_chunk[s] + nch;
+    }
+
+    const int64_t npairs = (int64_t)nseqs * H;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int64_t pair = 0; pair < npairs; ++pair) {
+        const int64_t s = pair / H, h = pair % H;
+        const int64_t g = h / heads_per_group;
+        double *S = (double *)malloc((size_t)(P * N) * sizeof(double));
+        if (!S)
+            continue;
+        const int start_from_init = init != NULL && (has_init == NULL || has_init[s] != 0);
+        for (int64_t i = 0; i < P * N; ++i)
+            S[i] = start_from_init ? init[((s * H + h) * P) * N + i] : 0.0;
+
+        const int64_t t0 = cu_seqlens[s], t1 = cu_seqlens[s + 1];
+        for (int64_t t = t0; t < t1; ++t) {
+            const double u = dt[t * H + h] + (dt_bias ? dt_bias[h] : 0.0);
+            const double delta = oracle_softplus(u);
+            const double decay = exp(delta * A[h]);
+            const double *xt = x + (t * H + h) * P;
+            const double *Bt = B + (t * G + g) * N;
+            const double *Ct = C + (t * G + g) * N;
+            /* state update: h_t = decay * h_{t-1} + delta * x_t (outer) B_t */
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t n = 0; n < N; ++n)
+                    S[p * N + n] = decay * S[p * N + n] + delta * xt[p] * Bt[n];
+            /* output: y_t = h_t . C_t + D * x_t (the state already holds token t) */
+            double *yt = y + (t * H + h) * P;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    acc += Ct[n] * S[p * N + n];
+                yt[p] = acc + (D ? D[h] : 0.0) * xt[p];
+            }
+            /* record the state after the last token of each chunk */
+            if (chunk_size > 0 && chunk_states != NULL) {
+                const int64_t local = t - t0;
+                if ((local + 1) % chunk_size == 0 || t == t1 - 1) {
+                    const int64_t c = first_chunk[s] + local / chunk_size;
+                    memcpy(chunk_states + ((c * H + h) * P) * N, S, (size_t)(P * N) * sizeof(double));
+                }
+            }
+        }
+        memcpy(final_states + ((s * H + h) * P) * N, S, (size_t)(P * N) * sizeof(double));
+        free(S);
+    }
+    free(first_chunk);
+    return 0;
+}
+
+/*
+ * Chunk metadata by plain enumeration. Chunk k of sequence s covers tokens
+ * [cu[s] + k*cs, min(cu[s] + (k+1)*cs, cu[s+1])); chunks never span sequences.
+ * Entries past the last chunk hold total_tokens (offsets) and -1 (seq index).
+ * seq_order lists sequences by decreasing length, ties by index.
+ * Returns 0, -1 on malformed cu_seqlens, -2 when max_chunks is too small.
+ */
+int oracle_varlen_metadata(int32_t nseqs, const int32_t *cu_seqlens, int32_t chunk_size,
+                           int32_t max_chunks, int32_t *chunk_offsets, int32_t *chunk_seq_idx,
+                           int32_t *seq_chunk_start, int32_t *nchunks, int32_t *seq_order)
+{
+    if (cu_seqlens[0] != 0)
+        return -1;
+    for (int32_t s = 0; s < nseqs; ++s)
+        if (cu_seqlens[s + 1] < cu_seqlens[s])
+            return -1;
+    const int32_t T = cu_seqlens[nseqs];
+    int32_t c = 0;
+    for (int32_t s = 0; s < nseqs; ++s) {
+        seq_chunk_start[s] = c;
+        for (int32_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; t += chunk_size) {
+            if (c >= max_chunks)
+                return -2;
+            chunk_offsets[c] = t;
+            chunk_seq_idx[c] = s;
+            ++c;
+        }
+    }
+    seq_chunk_start[nseqs] = c;
+    *nchunks = c;
+    for (int32_t k = c; k <= max_chunks; ++k)
+        chunk_offsets[k] = T;
+    for (int32_t k = c; k < max_chunks; ++k)
+        chunk_seq_idx[k] = -1;
+    /* insertion sort by (length desc, index asc) */
+    for (int32_t s = 0; s < nseqs; ++s)
+        seq_order[s] = s;
+    for (int32_t i = 1; i < nseqs; ++i) {
+        int32_t v = seq_order[i], j = i - 1;
+        int32_t lv = cu_seqlens[v + 1] - cu_seqlens[v];
+        while (j >= 0) {
+            int32_t u = seq_order[j];
+            int32_t lu = cu_seqlens[u + 1] - cu_seqlens[u];
+            if (lu > lv || (lu == lv && u < v))
+                break;
+            seq_order[j + 1] = u;
+            --j;
+        }
+        seq_order[j + 1] = v;
+    }
+    return 0;
+}
+
+/*
+ * Block-checkpoint plan, following the scatter loop of the prefix-caching page:
+ * sequence s was computed up to absolute position ncomp (num_computed_tokens,
+ * NULL = 0) and schedules L tokens, i.e. absolute positions [ncomp, ncomp+L).
+ * Blocks first = ncomp / bs .. last = (ncomp + L - 1) / bs are touched.
+ *  - interior blocks k in [first, last): only when ncomp % cs == 0; their
+ *    state is the one after the chunk that ends at the block end, i.e. chunk
+ *    first_chunk[s] + ((k+1)*bs - ncomp)/cs - 1, clamped into the sequence's
+ *    own chunk range;
+ *  - block `last`: the sequence's final state (= its last chunk's state).
+ * ckpt_src[s*max_blocks + k] = that chunk index or -1. chunk_state_dst[c] is
+ * the cache slot block_table[s*max_blocks + k] the chunk's state goes to, or
+ * -1 (no block, or a negative slot).
+ * Returns 0, or -3 when a touched block lies beyond max_blocks.
+ */
+int oracle_checkpoint_plan(int32_t nseqs, const int32_t *cu_seqlens, const int32_t *seq_chunk_start,
+                           int32_t max_chunks, const int32_t *num_computed_tokens,
+                           const int32_t *block_table, int32_t max_blocks, int32_t block_size,
+                           int32_t chunk_size, int32_t *ckpt_src, int32_t *chunk_state_dst)
+{
+    for (int64_t i = 0; i < (int64_t)nseqs * max_blocks; ++i)
+        ckpt_src[i] = -1;
+    for (int32_t c = 0; c < max_chunks; ++c)
+        chunk_state_dst[c] = -1;
+    for (int32_t s = 0; s < nseqs; ++s) {
+        const int64_t L = (int64_t)cu_seqlens[s + 1] - cu_seqlens[s];
+        if (L <= 0)
+            continue;
+        const int64_t ncomp = num_computed_tokens ? num_computed_tokens[s] : 0;
+        const int64_t first = ncomp / block_size, last = (ncomp + L - 1) / block_size;
+        if (last >= max_blocks)
+            return -3;
+        const int64_t lo = seq_chunk_start[s], hi = seq_chunk_start[s + 1] - 1;
+        if (ncomp % chunk_size == 0) {
+            for (int64_t k = first; k < last; ++k) {
+                int64_t src = lo + ((k + 1) * block_size - ncomp) / chunk_size - 1;
+                if (src < lo)
+                    src = lo;
+                if (src > hi)
+                    src = hi;
+                ckpt_src[s * max_blocks + k] = (int32_t)src;
+            }
+        }
+        ckpt_src[s * max_blocks + last] = (int32_t)hi;
+        for (int64_t k = first; k <= last; ++k) {
+            const int32_t src = ckpt_src[s * max_blocks + k];
+            const int32_t slot = block_table[s * max_blocks + k];
+            if (src >= 0 && slot >= 0)
+                chunk_state_dst[src] = slot;
+        }
+    }
+    return 0;
+}

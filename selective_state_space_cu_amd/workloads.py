@@ -1,0 +1,161 @@
+"""Seeded synthetic inputs for the varlen SSD scan.
+
+This module only draws random numbers and casts them to storage dtypes; it holds
+none of the scan's arithmetic. It is the one module that both the CPU oracle
+(through the tests and the bench's CPU baseline) and the HIP library's callers
+use, so both sides always see bit-identical inputs.
+
+Distributions (per the workload statements of the Mamba2 SSD varlen problem):
+  x ~ N(0,1) (T,H,P); raw dt ~ N(0,1) (T,H); dt_bias ~ U(-4,-2) per head;
+  A = -exp(U(log 1, log 16)) per head; B, C ~ N(0,1)/sqrt(N) (T,G,N);
+  D ~ N(0,1) per head; initial states ~ N(0, 0.5^2) (S,H,P,N).
+Draw order from numpy.default_rng(seed): lengths (only for the drawn-length
+workloads) -> x -> dt -> dt_bias -> A -> B -> C -> D -> init -> block table.
+Everything is drawn in float64, then rounded to float32 (RNE) and, for the bf16
+workloads, x/B/C are further rounded float32 -> bfloat16 (RNE).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+# Sequence lengths of the drawn-length workloads. They are what
+# default_rng(seed).integers(lo, hi+1, n), redrawn until |sum - 16384| <= 1024,
+# yields for the stated seeds; the constants win if numpy's stream ever changes.
+_LEN_MAMBA2_PREFILL = [3514, 1449, 903, 1582, 1995, 3430, 2129, 841]
+_LEN_CONT_BATCH = [312, 339, 267, 477, 476, 107, 312, 323, 127, 153, 250, 380, 150, 370, 335, 112,
+                   199, 425, 432, 337, 3, 350, 116, 420, 468, 220, 490, 389, 167, 450, 197, 53,
+                   304, 436, 337, 202, 462, 246, 198, 75, 109, 358, 410, 150, 322, 447, 76, 141,
+                   269, 288, 204, 205, 67, 314, 477, 101, 409, 93, 23, 383, 93, 386, 170, 291]
+
+# The five workloads. `len_draw` = (n, lo, hi) marks drawn lengths.
+CONFIGS = {
+    0: dict(name="tiny_fp32", lengths=[17, 64, 47], nheads=4, headdim=16, dstate=16, ngroups=1,
+            chunk_size=16, dtype="f32", init_seqs=[0, 2]),
+    1: dict(name="single_prompt_768_fp32", lengths=[768], nheads=8, headdim=64, dstate=64, ngroups=1,
+            chunk_size=128, dtype="f32", init_seqs=[0], alt_chunk_sizes=[32, 256]),
+    2: dict(name="mamba2_2p7b_prefill_layer", lengths=_LEN_MAMBA2_PREFILL, len_draw=(8, 512, 4096),
+            nheads=80, headdim=64, dstate=128, ngroups=1, chunk_size=256, dtype="bf16",
+            init_seqs=[0, 2, 4, 6]),
+    3: dict(name="continuous_batching_mix", lengths=_LEN_CONT_BATCH, len_draw=(64, 1, 512),
+            nheads=128, headdim=64, dstate=128, ngroups=8, chunk_size=256, dtype="bf16",
+            init_seqs=list(range(64))),
+    4: dict(name="prefix_cache_checkpoint_4x8894", lengths=[8894] * 4, nheads=32, headdim=128,
+            dstate=128, ngroups=4, chunk_size=64, dtype="bf16", init_seqs=[],
+            block_size=256, num_slots=140, resume_token=6912),
+}
+
+
+@dataclasses.dataclass
+class Workload:
+    """One batch of packed varlen inputs (torch CPU tensors in storage dtypes)."""
+    lengths: list
+    cu_seqlens: torch.Tensor      # int32 [S+1]
+    x: torch.Tensor               # (T,H,P) float32 or bfloat16
+    dt: torch.Tensor              # (T,H) float32
+    dt_bias: torch.Tensor         # (H,) float32
+    A: torch.Tensor               # (H,) float32
+    B: torch.Tensor               # (T,G,N) like x
+    C: torch.Tensor               # (T,G,N) like x
+    D: torch.Tensor               # (H,) float32
+    initial_states: torch.Tensor  # (S,H,P,N) float32
+    has_initial_state: torch.Tensor  # int32 [S]
+    chunk_size: int
+    dtype: str
+    block_table: Optional[torch.Tensor] = None   # int32 [S, max_blocks]
+    block_size: Optional[int] = None
+    num_slots: Optional[int] = None
+    name: str = ""
+
+    @property
+    def nseqs(self):
+        return len(self.lengths)
+
+    @property
+    def total_tokens(self):
+        return int(sum(self.lengths))
+
+    @property
+    def nheads(self):
+        return self.x.shape[1]
+
+    @property
+    def headdim(self):
+        return self.x.shape[2]
+
+    @property
+    def ngroups(self):
+        return self.B.shape[1]
+
+    @property
+    def dstate(self):
+        return self.B.shape[2]
+
+
+def draw_lengths(seed: int, n: int, lo: int, hi: int, target: int = 16384, slack: int = 1024):
+    """The length rule of the drawn-length workloads (kept for documentation and a test)."""
+    rng = np.random.default_rng(seed)
+    while True:
+        L = rng.integers(lo, hi + 1, size=n)
+        if abs(int(L.sum()) - target) <= slack:
+            return [int(v) for v in L], rng
+
+
+def _cast(a64: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a64.astype(np.float32)))
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def make_inputs(lengths, nheads, headdim, dstate, ngroups, chunk_size, dtype="f32", init_seqs=(),
+                seed=0, rng=None, dt_bias_range=(-4.0, -2.0), a_log_range=(0.0, float(np.log(16.0))),
+                x_scale=1.0, block_size=None, num_slots=None, name=""):
+    """Draw one workload. `rng` continues a stream (used after a length draw)."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    lengths = [int(v) for v in lengths]
+    S, T, H, P, N, G = len(lengths), int(sum(lengths)), nheads, headdim, dstate, ngroups
+    cu = np.zeros(S + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    x = rng.standard_normal((T, H, P)) * x_scale
+    dt = rng.standard_normal((T, H))
+    dt_bias = rng.uniform(dt_bias_range[0], dt_bias_range[1], size=H)
+    A = -np.exp(rng.uniform(a_log_range[0], a_log_range[1], size=H))
+    B = rng.standard_normal((T, G, N)) / np.sqrt(N)
+    C = rng.standard_normal((T, G, N)) / np.sqrt(N)
+    D = rng.standard_normal(H)
+    init = rng.standard_normal((S, H, P, N)) * 0.5
+    has = np.zeros(S, dtype=np.int32)
+    has[list(init_seqs)] = 1
+    block_table = None
+    if block_size is not None:
+        nblk = -(-max(lengths) // block_size) if lengths else 0
+        slots = num_slots if num_slots is not None else S * nblk
+        block_table = torch.from_numpy(
+            rng.permutation(slots)[: S * nblk].reshape(S, nblk).astype(np.int32))
+    return Workload(
+        lengths=lengths,
+        cu_seqlens=torch.from_numpy(cu.astype(np.int32)),
+        x=_cast(x, dtype), dt=_cast(dt, "f32"), dt_bias=_cast(dt_bias, "f32"), A=_cast(A, "f32"),
+        B=_cast(B, dtype), C=_cast(C, dtype), D=_cast(D, "f32"),
+        initial_states=_cast(init, "f32"), has_initial_state=torch.from_numpy(has),
+        chunk_size=int(chunk_size), dtype=dtype, block_table=block_table, block_size=block_size,
+        num_slots=num_slots, name=name)
+
+
+def make_config(index: int, chunk_size: Optional[int] = None) -> Workload:
+    """The seeded workload of configuration `index` (seed = index)."""
+    cfg = CONFIGS[index]
+    rng = np.random.default_rng(index)
+    lengths = cfg["lengths"]
+    if "len_draw" in cfg:
+        n, lo, hi = cfg["len_draw"]
+        drawn, rng = draw_lengths(index, n, lo, hi)
+        if drawn != lengths:   # numpy stream changed: keep the constants, restart the stream
+            rng = np.random.default_rng(index)
+    return make_inputs(lengths, cfg["nheads"], cfg["headdim"], cfg["dstate"], cfg["ngroups"],
+                       chunk_size or cfg["chunk_size"], dtype=cfg["dtype"],
+                       init_seqs=cfg["init_seqs"], rng=rng, block_size=cfg.get("block_size"),
+                       num_slots=cfg.get("num_slots"), name=cfg["name"])

@@ -1,0 +1,350 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each pin takes an oracle library handle, so the same checks run against the
+real oracle (tests/test_oracle_pins.py) and against deliberately broken copies
+of it (tests/test_oracle_mutations.py), which must each fail at least one pin.
+"""
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+from ssd_brute import chunked, semiseparable
+from selective_state_space_cu_amd.workloads import make_config, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _run(lib, w, chunk_size=0, init=True):
+    return oracle.ssd_varlen(w.x, w.dt, w.dt_bias, w.A, w.B, w.C, w.D, w.cu_seqlens,
+                             w.initial_states if init else None,
+                             w.has_initial_state if init else None, chunk_size=chunk_size, lib=lib)
+
+
+def _close(a, b, tol, what):
+    a, b = np.asarray(a), np.asarray(b)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    scale = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    assert err <= tol * scale, f"{what}: max abs err {err:.3e} > {tol:.1e}*{scale:.2f}"
+
+
+def _tiny_cases():
+    # (lengths, H, P, N, G, init_seqs, seed): varlen, zero-length, groups, P != N
+    return [([5, 0, 11, 3], 4, 3, 2, 2, [0, 2], 11),
+            ([17, 9], 2, 2, 4, 1, [1], 12),
+            ([1, 30, 2], 6, 4, 3, 3, [0, 1, 2], 13),
+            ([40], 1, 1, 1, 1, [0], 14)]
+
+
+def pin_brute_force_semiseparable(lib):
+    """Oracle == materialised semiseparable matrix on tiny inputs (1e-12)."""
+    for L, H, P, N, G, ini, seed in _tiny_cases():
+        w = make_inputs(L, H, P, N, G, 4, dtype="f32", init_seqs=ini, seed=seed)
+        y, fin, _ = _run(lib, w)
+        yb, fb = semiseparable(w.x, w.dt, w.dt_bias, w.A, w.B, w.C, w.D, w.cu_seqlens,
+                               w.initial_states, w.has_initial_state)
+        _close(y, yb, 1e-12, f"y vs semiseparable {L}")
+        _close(fin, fb, 1e-12, f"final vs semiseparable {L}")
+
+
+def pin_scalar_closed_form(lib):
+    """P=N=1, B=C=x=1, constant delta: h_t = a^(t+1) h0 + delta (1-a^(t+1))/(1-a), y = h + D."""
+    delta, Ah, h0, D, T = 0.5, -0.7, 0.3, 0.25, 37
+    u = math.log(math.expm1(delta))          # the argument whose softplus is exactly `delta`
+    ones = np.ones((T, 1, 1))
+    y, fin, _ = oracle.ssd_varlen(ones, np.full((T, 1), u), np.zeros(1), np.array([Ah]), ones,
+                                  ones, np.array([D]), np.array([0, T], np.int32),
+                                  np.full((1, 1, 1, 1), h0), np.array([1], np.int32), lib=lib)
+    a = math.exp(delta * Ah)
+    t = np.arange(T)
+    h = a ** (t + 1) * h0 + delta * (1 - a ** (t + 1)) / (1 - a)
+    _close(y[:, 0, 0], h + D, 1e-12, "scalar closed form y")
+    _close(fin[0, 0, 0, 0], h[-1], 1e-12, "scalar closed form final")
+
+
+def pin_linear_attention(lib):
+    """A = 0: h_t = h0 + sum_{k<=t} delta_k x_k B_k^T (prefix sums), y_t = C_t h_t + D x_t."""
+    w = make_inputs([9, 14, 1], 4, 3, 5, 2, 4, init_seqs=[1], seed=21)
+    A0 = np.zeros(4)
+    y, fin, _ = oracle.ssd_varlen(w.x, w.dt, w.dt_bias, A0, w.B, w.C, w.D, w.cu_seqlens,
+                                  w.initial_states, w.has_initial_state, lib=lib)
+    x, B, C = (v.double().numpy() for v in (w.x, w.B, w.C))
+    delta = np.logaddexp(0.0, w.dt.double().numpy() + w.dt_bias.double().numpy()[None])
+    D = w.D.double().numpy()
+    cu = w.cu_seqlens.numpy()
+    for s in range(3):
+        t0, t1 = cu[s], cu[s + 1]
+        for h in range(4):
+            g = h // 2
+            h0 = w.initial_states[s, h].double().numpy() if w.has_initial_state[s] else 0.0
+            upd = np.einsum("t,tp,tn->tpn", delta[t0:t1, h], x[t0:t1, h], B[t0:t1, g])
+            hs = h0 + np.cumsum(upd, axis=0)
+            yr = np.einsum("tpn,tn->tp", hs, C[t0:t1, g]) + D[h] * x[t0:t1, h]
+            _close(y[t0:t1, h], yr, 1e-12, "A=0 y")
+            _close(fin[s, h], hs[-1], 1e-12, "A=0 final")
+
+
+def pin_diagonal_limit(lib):
+    """A = -1e4 with delta ~ 1.3: only the current token survives:
+    y_t = delta_t (C_t.B_t) x_t + D x_t, final = delta_last x_last B_last^T."""
+    w = make_inputs([6, 3], 2, 3, 4, 1, 4, init_seqs=[0, 1], seed=31)
+    delta = 1.25
+    u = math.log(math.expm1(delta))
+    T = w.total_tokens
+    y, fin, _ = oracle.ssd_varlen(w.x, np.full((T, 2), u), np.zeros(2), np.full(2, -1e4), w.B,
+                                  w.C, w.D, w.cu_seqlens, w.initial_states, w.has_initial_state,
+                                  lib=lib)
+    x, B, C, D = (v.double().numpy() for v in (w.x, w.B, w.C, w.D))
+    cb = np.einsum("tn,tn->t", C[:, 0], B[:, 0])
+    yr = delta * cb[:, None, None] * x + D[None, :, None] * x
+    _close(y, yr, 1e-12, "diagonal limit y")
+    cu = w.cu_seqlens.numpy()
+    for s in range(2):
+        t = cu[s + 1] - 1
+        _close(fin[s], delta * np.einsum("hp,n->hpn", x[t], B[t, 0]), 1e-12, "diagonal final")
+
+
+def pin_zero_dt(lib):
+    """dt_bias = -1e4 makes softplus exactly 0: state unchanged, y = C.h0 + D x."""
+    w = make_inputs([7, 12], 2, 3, 4, 2, 4, init_seqs=[0, 1], seed=41)
+    y, fin, _ = oracle.ssd_varlen(w.x, w.dt, np.full(2, -1e4), w.A, w.B, w.C, w.D, w.cu_seqlens,
+                                  w.initial_states, w.has_initial_state, lib=lib)
+    h0 = w.initial_states.double().numpy()
+    _close(fin, h0, 0.0, "dt=0 final == init")
+    x, C, D = (v.double().numpy() for v in (w.x, w.C, w.D))
+    cu = w.cu_seqlens.numpy()
+    for s in range(2):
+        for h in range(2):
+            t0, t1 = cu[s], cu[s + 1]
+            yr = C[t0:t1, h] @ h0[s, h].T + D[h] * x[t0:t1, h]
+            _close(y[t0:t1, h], yr, 1e-12, "dt=0 y")
+
+
+def pin_superposition(lib):
+    """Linear in (x, h0): y(x,h0) = y(x,0) + y(0,h0); y(2x,0) = 2 y(x,0)."""
+    w = make_inputs([13, 20], 2, 4, 3, 1, 4, init_seqs=[0, 1], seed=51)
+    args = (w.dt, w.dt_bias, w.A, w.B, w.C)
+    xz = np.zeros(w.x.shape)
+    y_full, f_full, _ = oracle.ssd_varlen(w.x, *args, w.D, w.cu_seqlens, w.initial_states,
+                                          w.has_initial_state, lib=lib)
+    y_x, f_x, _ = oracle.ssd_varlen(w.x, *args, w.D, w.cu_seqlens, lib=lib)
+    y_h, f_h, _ = oracle.ssd_varlen(xz, *args, w.D, w.cu_seqlens, w.initial_states,
+                                    w.has_initial_state, lib=lib)
+    _close(y_full, y_x + y_h, 1e-12, "superposition y")
+    _close(f_full, f_x + f_h, 1e-12, "superposition final")
+    y2, _, _ = oracle.ssd_varlen(2 * w.x.double().numpy(), *args, w.D, w.cu_seqlens, lib=lib)
+    _close(y2, 2 * y_x, 1e-12, "homogeneity")
+
+
+def pin_no_leakage(lib):
+    """A packed batch equals each sequence run alone, bit for bit."""
+    w = make_inputs([11, 4, 0, 23], 2, 3, 4, 2, 4, init_seqs=[0, 3], seed=61)
+    y, fin, _ = _run(lib, w)
+    cu = w.cu_seqlens.numpy()
+    for s in range(4):
+        t0, t1 = cu[s], cu[s + 1]
+        ys, fs, _ = oracle.ssd_varlen(w.x[t0:t1], w.dt[t0:t1], w.dt_bias, w.A, w.B[t0:t1],
+                                      w.C[t0:t1], w.D, np.array([0, t1 - t0], np.int32),
+                                      w.initial_states[s:s + 1], w.has_initial_state[s:s + 1],
+                                      lib=lib)
+        assert np.array_equal(ys, y[t0:t1]) and np.array_equal(fs[0], fin[s]), f"leak seq {s}"
+
+
+def pin_chunked_decomposition(lib):
+    """The chunked decomposition equals the recurrence at every chunk size
+    (y, final states, and the state after each chunk)."""
+    w = make_inputs([37, 1, 64, 50], 4, 3, 5, 2, 16, init_seqs=[0, 2], seed=71)
+    for cs in (1, 4, 16, 32, 64):
+        y, fin, cst = _run(lib, w, chunk_size=cs)
+        yc, fc, sc = chunked(w.x, w.dt, w.dt_bias, w.A, w.B, w.C, w.D, w.cu_seqlens, cs,
+                             w.initial_states, w.has_initial_state)
+        _close(y, yc, 1e-10, f"chunked y cs={cs}")
+        _close(fin, fc, 1e-10, f"chunked final cs={cs}")
+        assert cst.shape == sc.shape, f"chunk count cs={cs}"
+        _close(cst, sc, 1e-10, f"chunk states cs={cs}")
+
+
+def pin_initial_state_decay(lib):
+    """x = 0: y_t = exp(sum_{k<=t} a_k) C_t.h0 -- the entering state carries the decay of
+    every token up to and including t (the quantity the initial-state bug under-decayed)."""
+    w = make_inputs([10, 25], 2, 2, 3, 1, 4, init_seqs=[0, 1], seed=81)
+    xz = np.zeros(w.x.shape)
+    y, _, _ = oracle.ssd_varlen(xz, w.dt, w.dt_bias, w.A, w.B, w.C, None, w.cu_seqlens,
+                                w.initial_states, w.has_initial_state, lib=lib)
+    delta = np.logaddexp(0.0, w.dt.double().numpy() + w.dt_bias.double().numpy()[None])
+    A = w.A.double().numpy()
+    C = w.C.double().numpy()
+    h0 = w.initial_states.double().numpy()
+    cu = w.cu_seqlens.numpy()
+    for s in range(2):
+        t0, t1 = cu[s], cu[s + 1]
+        for h in range(2):
+            decay = np.exp(np.cumsum(delta[t0:t1, h] * A[h]))
+            yr = decay[:, None] * (C[t0:t1, 0] @ h0[s, h].T)
+            _close(y[t0:t1, h], yr, 1e-12, "init decay")
+
+
+def pin_768_token_chunk128(lib):
+    """The bug-fix page's larger case: 768 tokens, chunk_size 128 (8 heads, P=N=64, fp32,
+    random initial state): the oracle equals the chunked decomposition at chunk sizes
+    32/128/256, and the semiseparable form on two heads."""
+    w = make_config(1)
+    y, fin, _ = _run(lib, w)
+    for cs in (32, 128, 256):
+        yc, fc, _ = chunked(w.x, w.dt, w.dt_bias, w.A, w.B, w.C, w.D, w.cu_seqlens, cs,
+                            w.initial_states, w.has_initial_state)
+        _close(y, yc, 1e-10, f"768 y cs={cs}")
+        _close(fin, fc, 1e-10, f"768 final cs={cs}")
+    sl = slice(0, 2)
+    yb, fb = semiseparable(w.x[:, sl], w.dt[:, sl], w.dt_bias[sl], w.A[sl], w.B, w.C, w.D[sl],
+                           w.cu_seqlens, w.initial_states[:, sl], w.has_initial_state)
+    _close(y[:, sl], yb, 1e-10, "768 y semiseparable")
+    _close(fin[:, sl], fb, 1e-10, "768 final semiseparable")
+
+
+# ----- integer outputs: chunk metadata and checkpoint plan -----
+
+def brute_metadata(lengths, cs, max_chunks):
+    """Enumerate the chunk grid the slow way (token by token)."""
+    T = int(sum(lengths))
+    offsets, seq_idx, start = [], [], []
+    t = 0
+    for s, L in enumerate(lengths):
+        start.append(len(offsets))
+        for i in range(L):
+            if i % cs == 0:
+                offsets.append(t + i)
+                seq_idx.append(s)
+        t += L
+    n = len(offsets)
+    start.append(n)
+    offsets += [T] * (max_chunks + 1 - n)
+    seq_idx += [-1] * (max_chunks - n)
+    order = sorted(range(len(lengths)), key=lambda s: (-lengths[s], s))
+    return dict(chunk_offsets=offsets, chunk_seq_idx=seq_idx, seq_chunk_start=start, nchunks=n,
+                seq_order=order)
+
+
+def _check_meta(got, ref, what):
+    for k in ("chunk_offsets", "chunk_seq_idx", "seq_chunk_start", "seq_order"):
+        assert list(np.asarray(got[k])) == list(ref[k]), f"{what}: {k}"
+    assert got["nchunks"] == ref["nchunks"], f"{what}: nchunks"
+
+
+def pin_metadata_enumeration(lib):
+    """Oracle metadata == token-by-token enumeration; nchunks == sum ceil(L/cs)."""
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        S = int(rng.integers(1, 12))
+        lengths = [int(v) for v in rng.integers(0, 300, size=S)]
+        if trial % 5 == 0:
+            lengths[0] = lengths[-1] = 64     # ties
+        cs = int(2 ** rng.integers(4, 9))
+        mc = sum(lengths) // cs + S + 2
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        got = oracle.varlen_metadata(cu, cs, mc, lib=lib)
+        _check_meta(got, brute_metadata(lengths, cs, mc), f"trial {trial}")
+        assert got["nchunks"] == sum(-(-L // cs) for L in lengths)
+
+
+def pin_metadata_golden_tiny(lib):
+    """The tiny workload's chunk grid, worked out by hand (tests/golden/tiny_metadata.json)."""
+    with open(os.path.join(GOLDEN, "tiny_metadata.json")) as f:
+        g = json.load(f)
+    got = oracle.varlen_metadata(np.array(g["cu_seqlens"], np.int32), g["chunk_size"],
+                                 g["max_chunks"], lib=lib)
+    _check_meta(got, g["expected"], "tiny golden")
+
+
+def pin_plan_prefix_cache_closed_form(lib):
+    """4 x 8894 tokens, chunk 64, block 256: 139 chunks per sequence; interior blocks
+    k = 0..33 take chunk 139 s + 4 k + 3; block 34 (190 tokens) takes the final state,
+    chunk 139 s + 138. The resume block for token 6912 is k = 26 -> chunk 139 s + 107."""
+    cu = np.array([0, 8894, 17788, 26682, 35576], np.int32)
+    mc = 35576 // 64 + 4
+    meta = oracle.varlen_metadata(cu, 64, mc, lib=lib)
+    assert meta["nchunks"] == 556 and list(meta["seq_chunk_start"]) == [0, 139, 278, 417, 556]
+    bt = np.arange(140, dtype=np.int32)[::-1].reshape(4, 35).copy()
+    src, dst = oracle.checkpoint_plan(cu, meta["seq_chunk_start"], mc, bt, 256, 64, lib=lib)
+    for s in range(4):
+        for k in range(34):
+            assert src[s, k] == 139 * s + 4 * k + 3, (s, k, src[s, k])
+            assert dst[139 * s + 4 * k + 3] == bt[s, k]
+        assert src[s, 34] == 139 * s + 138 and dst[139 * s + 138] == bt[s, 34]
+        assert src[s, 26] == 139 * s + 107
+    assert (dst >= 0).sum() == 140
+
+
+def pin_plan_misaligned_and_resume(lib):
+    """A computed prefix that is not chunk-aligned gets no interior checkpoints (only the
+    final-state block); an aligned one (6912 = 27 blocks) maps blocks to exact chunk ends."""
+    L = 1982
+    cu = np.array([0, L, 2 * L], np.int32)
+    mc = 2 * L // 64 + 2
+    meta = oracle.varlen_metadata(cu, 64, mc, lib=lib)
+    bt = np.arange(70, dtype=np.int32).reshape(2, 35)
+    ncomp = np.array([6912, 6912 + 32], np.int32)
+    src, dst = oracle.checkpoint_plan(cu, meta["seq_chunk_start"], mc, bt, 256, 64,
+                                      num_computed_tokens=ncomp, lib=lib)
+    c0, c1 = meta["seq_chunk_start"][0], meta["seq_chunk_start"][1]
+    # sequence 0: blocks 27..33 interior (ends at 7168 + 256 i), block 34 gets the final state
+    for k in range(27, 34):
+        assert src[0, k] == c0 + ((k + 1) * 256 - 6912) // 64 - 1
+    assert src[0, 34] == c1 - 1
+    assert all(src[0, k] == -1 for k in range(27))
+    # sequence 1: misaligned -> only its last block (6944+1981)//256 = 34 is written
+    last = (6944 + L - 1) // 256
+    assert [k for k in range(35) if src[1, k] >= 0] == [last]
+    assert src[1, last] == meta["nchunks"] - 1
+
+
+def gather_plan(cu, seq_chunk_start, max_chunks, block_table, bs, cs, ncomp=None):
+    """Per-chunk formulation of the plan (each chunk asks which block ends with it)."""
+    S, maxb = block_table.shape
+    dst = np.full(max_chunks, -1, np.int64)
+    for s in range(S):
+        L = int(cu[s + 1] - cu[s])
+        if L <= 0:
+            continue
+        nc = 0 if ncomp is None else int(ncomp[s])
+        last = (nc + L - 1) // bs
+        for c in range(int(seq_chunk_start[s]), int(seq_chunk_start[s + 1])):
+            lc = c - int(seq_chunk_start[s])
+            end = nc + min((lc + 1) * cs, L)
+            if c == int(seq_chunk_start[s + 1]) - 1:
+                dst[c] = block_table[s, last]
+            elif nc % cs == 0 and end % bs == 0:
+                dst[c] = block_table[s, end // bs - 1]
+    return np.where(dst < 0, -1, dst)
+
+
+def pin_plan_scatter_equals_gather(lib):
+    """The oracle's block-loop plan equals the per-chunk formulation on random batches."""
+    rng = np.random.default_rng(9)
+    for trial in range(30):
+        S = int(rng.integers(1, 7))
+        cs = int(2 ** rng.integers(4, 7))
+        bs = cs * int(rng.integers(1, 5))
+        lengths = [int(v) for v in rng.integers(0, 700, size=S)]
+        ncomp = (rng.integers(0, 6, size=S) * (cs if trial % 3 else 7)).astype(np.int32)
+        maxb = max(((n + max(L, 1) - 1) // bs) + 1 for n, L in zip(ncomp, lengths))
+        bt = rng.permutation(S * maxb).reshape(S, maxb).astype(np.int32)
+        bt[rng.random(bt.shape) < 0.1] = -1
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        mc = sum(lengths) // cs + S
+        meta = oracle.varlen_metadata(cu, cs, mc, lib=lib)
+        _, dst = oracle.checkpoint_plan(cu, meta["seq_chunk_start"], mc, bt, bs, cs,
+                                        num_computed_tokens=ncomp, lib=lib)
+        ref = gather_plan(cu, meta["seq_chunk_start"], mc, bt, bs, cs, ncomp)
+        assert list(dst) == list(ref), f"trial {trial}"
+
+
+ALL_PINS = [pin_brute_force_semiseparable, pin_scalar_closed_form, pin_linear_attention,
+            pin_diagonal_limit, pin_zero_dt, pin_superposition, pin_no_leakage,
+            pin_chunked_decomposition, pin_initial_state_decay, pin_768_token_chunk128,
+            pin_metadata_enumeration, pin_metadata_golden_tiny,
+            pin_plan_prefix_cache_closed_form, pin_plan_misaligned_and_resume,
+            pin_plan_scatter_equals_gather]

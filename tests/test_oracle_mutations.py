@@ -1,0 +1,56 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and checks that
+every one of them fails at least one pin, i.e. the pins can tell."""
+import os
+
+import pytest
+
+import oracle
+from oracle.build import SRC, build_oracle
+from oracle_pins import ALL_PINS
+
+# (name, [(original text, replacement)]) -- each substitution must match exactly once
+MUTATIONS = [
+    ("drop_decay", [("S[p * N + n] = decay * S[p * N + n] +", "S[p * N + n] = S[p * N + n] +")]),
+    ("first_token_not_decayed", [("const double decay = exp(delta * A[h]);",
+                                  "const double decay = (t == t0) ? 1.0 : exp(delta * A[h]);")]),
+    ("decay_sign", [("exp(delta * A[h])", "exp(-0.01 * delta * A[h])")]),
+    ("drop_D", [("yt[p] = acc + (D ? D[h] : 0.0) * xt[p];", "yt[p] = acc;")]),
+    ("wrong_group", [("const int64_t g = h / heads_per_group;", "const int64_t g = h % G;")]),
+    ("swap_B_C", [("const double *Bt = B + (t * G + g) * N;", "const double *Bt = C + (t * G + g) * N;"),
+                  ("const double *Ct = C + (t * G + g) * N;", "const double *Ct = B + (t * G + g) * N;")]),
+    ("softplus_as_exp", [("return log1p(exp(u));", "return exp(u);")]),
+    ("drop_dt_bias", [("dt[t * H + h] + (dt_bias ? dt_bias[h] : 0.0)", "dt[t * H + h]")]),
+    ("input_without_delta", [("+ delta * xt[p] * Bt[n]", "+ xt[p] * Bt[n]")]),
+    ("transposed_input", [("+ delta * xt[p] * Bt[n]", "+ delta * xt[n % P] * Bt[p % N]")]),
+    ("output_uses_previous_C", [("const double *Ct = C + (t * G + g) * N;",
+                                 "const double *Ct = C + ((t > t0 ? t - 1 : t) * G + g) * N;")]),
+    ("chunk_state_off_by_one", [("(local + 1) % chunk_size == 0", "local % chunk_size == 0")]),
+    ("ignore_has_init", [("(has_init == NULL || has_init[s] != 0)", "(has_init == NULL)")]),
+    ("global_chunk_grid", [("t < cu_seqlens[s + 1]; t += chunk_size)",
+                            "t < cu_seqlens[s + 1]; t = (t / chunk_size + 1) * chunk_size)")]),
+    ("plan_missing_minus_one", [("ncomp) / chunk_size - 1;", "ncomp) / chunk_size;")]),
+    ("plan_no_alignment_skip", [("if (ncomp % chunk_size == 0) {", "if (1) {")]),
+    ("plan_no_final_block", [("ckpt_src[s * max_blocks + last] = (int32_t)hi;", "")]),
+    ("order_tie_break", [("(lu == lv && u < v)", "(lu == lv && u > v)")]),
+]
+
+
+@pytest.mark.parametrize("name,subs", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(name, subs, tmp_path):
+    with open(SRC) as f:
+        text = f.read()
+    for old, new in subs:
+        assert text.count(old) == 1, f"mutation {name}: pattern not unique: {old!r}"
+        text = text.replace(old, new)
+    src = os.path.join(tmp_path, f"oracle_{name}.c")
+    with open(src, "w") as f:
+        f.write(text)
+    lib = oracle.load(build_oracle(out=os.path.join(tmp_path, f"liboracle_{name}.so"), src=src,
+                                   werror=False))
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"mutation {name} passed every pin"
