@@ -1,0 +1,57 @@
+// Internal interface between the C-ABI host code (ssd_api.hip) and the kernel
+// translation units of libssd.so. Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ssd.h"
+
+namespace ssd {
+
+// Arguments of the fused chunk-walk scan kernel (one workgroup per
+// (sequence, head, headdim tile), walking the sequence's chunks in order).
+struct ScanArgs {
+    const void *x;
+    const float *dt;
+    const float *dt_bias;   // nullable
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;         // nullable
+    const float *init;      // nullable
+    const int32_t *has_init;  // nullable
+    void *y;
+    float *final_states;
+    float *chunk_states;      // nullable
+    const int32_t *chunk_state_dst;  // nullable
+    const int32_t *cu_seqlens;
+    const int32_t *seq_chunk_start;
+    const int32_t *seq_order;
+    int32_t *error_flag;
+    int32_t T, S, H, P, G, cs, max_chunks, capacity, nptiles;
+};
+
+// Launches the scan for one (dtype, waves-per-workgroup, dstate) instance.
+hipError_t launch_scan_bf16(const ScanArgs &a, int waves, int dstate, hipStream_t stream);
+hipError_t launch_scan_f32(const ScanArgs &a, int waves, int dstate, hipStream_t stream);
+
+struct MetaArgs {
+    const int32_t *cu_seqlens;
+    int32_t *chunk_offsets, *chunk_seq_idx, *seq_chunk_start, *nchunks, *seq_order, *error_flag;
+    int32_t S, T, cs, max_chunks;
+};
+hipError_t launch_metadata(const MetaArgs &a, hipStream_t stream);
+
+struct PlanArgs {
+    const int32_t *cu_seqlens, *seq_chunk_start, *chunk_seq_idx, *nchunks;
+    const int32_t *num_computed_tokens;  // nullable
+    const int32_t *block_table;
+    int32_t *ckpt_src, *chunk_state_dst, *error_flag;
+    const float *chunk_states;  // nullable: scatter now
+    float *state_cache;
+    int32_t S, cs, max_chunks, max_blocks, block_size, state_elems, num_slots;
+};
+hipError_t launch_plan(const PlanArgs &a, hipStream_t stream);
+
+}  // namespace ssd

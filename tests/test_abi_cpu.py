@@ -1,0 +1,108 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad arguments synchronously (no GPU needed: nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_cu_amd import ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ssd.LIB_PATH), reason="libssd.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssd_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ssd.load_library()
+    names = declared_functions()
+    assert set(names) == set(ssd.EXPORTS), names
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings():
+    assert ssd.status_string(0) == "ok"
+    for code in range(1, 9):
+        assert ssd.status_string(code) not in ("ok", "unknown status")
+    assert ssd.status_string(99) == "unknown status"
+
+
+FAKE = 0x1000  # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def _meta(S=2, T=100, cs=64, max_chunks=None, null_field=None):
+    mc = T // cs + S if max_chunks is None else max_chunks
+    m = ssd._Meta(S, T, cs, mc, *([FAKE] * 7))
+    if null_field:
+        setattr(m, null_field, None)
+    return m
+
+
+def _scan(m, **kw):
+    args = dict(x=FAKE, dt=FAKE, dt_bias=None, A=FAKE, B=FAKE, C=FAKE, D=None, dtype=1, H=4, P=64,
+                N=128, G=2, init=None, has=None, y=FAKE, final=FAKE, cst=None, dst=None, cap=0)
+    args.update(kw)
+    lib = ssd.load_library()
+    return lib.ssd_chunk_scan_varlen(args["x"], args["dt"], args["dt_bias"], args["A"], args["B"],
+                                     args["C"], args["D"], args["dtype"], ctypes.byref(m), args["H"],
+                                     args["P"], args["N"], args["G"], args["init"], args["has"],
+                                     args["y"], args["final"], args["cst"], args["dst"], args["cap"],
+                                     None)
+
+
+@pytest.mark.parametrize("cs", [0, 8, 17, 48, 100, 512, -64])
+def test_metadata_rejects_bad_chunk_size(cs):
+    lib = ssd.load_library()
+    m = _meta(cs=cs, max_chunks=1000)
+    assert lib.ssd_varlen_metadata(ctypes.byref(m), None) == 2
+
+
+def test_metadata_rejects_small_capacity_and_nulls():
+    lib = ssd.load_library()
+    assert lib.ssd_varlen_metadata(ctypes.byref(_meta(S=3, T=128, cs=16, max_chunks=10)), None) == 5
+    assert lib.ssd_varlen_metadata(None, None) == 1
+    for f in ("cu_seqlens", "chunk_offsets", "chunk_seq_idx", "seq_chunk_start", "nchunks",
+              "seq_order", "error_flag"):
+        assert lib.ssd_varlen_metadata(ctypes.byref(_meta(null_field=f)), None) == 1
+    assert lib.ssd_varlen_metadata(ctypes.byref(_meta(S=-1)), None) == 3
+
+
+def test_scan_argument_errors():
+    m = _meta()
+    assert _scan(m, H=6, G=4) == 3                 # nheads % ngroups
+    assert _scan(m, H=0) == 3
+    assert _scan(m, P=40) == 8                     # headdim % 16
+    assert _scan(m, N=48) == 8                     # dstate
+    assert _scan(m, N=256, dtype=0) == 8           # f32 dstate 256
+    assert _scan(m, dtype=5) == 6
+    assert _scan(m, x=None) == 1
+    assert _scan(m, A=None) == 1
+    assert _scan(m, final=None) == 1
+    assert _scan(m, y=FAKE + 4) == 3               # misaligned
+    assert _scan(m, cst=FAKE, cap=0) == 5
+    assert _scan(m, cst=FAKE, cap=2) == 5          # dense export needs max_chunks slots
+    assert _scan(_meta(cs=24, max_chunks=100)) == 2
+
+
+def test_export_argument_errors():
+    lib = ssd.load_library()
+    m = _meta()
+
+    def call(bs=128, bt=FAKE, maxb=4, src=FAKE, dst=FAKE, cst=None, elems=0, cache=None, slots=8):
+        return lib.ssd_export_chunk_states(ctypes.byref(m), None, bt, maxb, bs, src, dst, cst, elems,
+                                           cache, slots, None)
+    assert call(bs=96) == 4          # not a multiple of chunk_size
+    assert call(bs=0) == 4
+    assert call(bt=None) == 1
+    assert call(dst=None) == 1
+    assert call(cst=FAKE, cache=None) == 1
+    assert call(cst=FAKE, cache=FAKE, elems=6) == 3
+    assert call(maxb=-1) == 3

@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU float64 oracle.
+
+Integers (chunk metadata, checkpoint plan) must match bit for bit; y, final
+states and exported chunk states must satisfy |gpu - ref| <= tol + tol*|ref|
+with tol = 5e-3 for float32 inputs and 2e-2 for bf16 inputs (float32 state).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, check_close, gpu_run, log, oracle_pair, oracle_run, to_dev
+from selective_state_space_cu_amd import ssd
+from selective_state_space_cu_amd.workloads import CONFIGS, make_config, make_inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+_CFG = {}
+
+
+def cfg(i):
+    if i not in _CFG:
+        _CFG[i] = make_config(i)
+    return _CFG[i]
+
+
+def _meta_host(meta):
+    n = int(meta.nchunks.item())
+    return dict(chunk_offsets=meta.chunk_offsets.cpu().numpy(),
+                chunk_seq_idx=meta.chunk_seq_idx.cpu().numpy()[: meta.max_chunks],
+                seq_chunk_start=meta.seq_chunk_start.cpu().numpy(), nchunks=n,
+                seq_order=meta.seq_order.cpu().numpy()[: meta.nseqs],
+                error=int(meta.error_flag.item()))
+
+
+def _check_meta(meta, cu, cs):
+    got = _meta_host(meta)
+    ref = oracle.varlen_metadata(cu, cs, meta.max_chunks)
+    assert got["error"] == 0
+    for k in ("chunk_offsets", "chunk_seq_idx", "seq_chunk_start", "seq_order"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert got["nchunks"] == ref["nchunks"]
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_metadata_configs_bit_exact(idx):
+    w = cfg(idx)
+    log(f"metadata config {idx}")
+    meta = ssd.varlen_metadata(w.cu_seqlens.cuda(), w.chunk_size, total_tokens=w.total_tokens)
+    _check_meta(meta, w.cu_seqlens.numpy(), w.chunk_size)
+
+
+def test_metadata_random_bit_exact():
+    rng = np.random.default_rng(123)
+    for trial in range(25):
+        S = int(rng.integers(1, 300)) if trial % 4 else int(rng.integers(1, 5))
+        L = rng.integers(0, 700, size=S)
+        L[rng.random(S) < 0.15] = 0
+        cs = int(2 ** rng.integers(4, 9))
+        cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+        T = int(cu[-1])
+        extra = int(rng.integers(0, 5))
+        meta = ssd.varlen_metadata(torch.from_numpy(cu).cuda(), cs, total_tokens=T,
+                                   max_chunks=T // cs + S + extra)
+        _check_meta(meta, cu, cs)
+
+
+def _full_compare(w, cs=None, dense=True, what=""):
+    cs = cs or w.chunk_size
+    log(f"scan {what} T={w.total_tokens} H={w.nheads} P={w.headdim} N={w.dstate} G={w.ngroups} "
+        f"cs={cs} {w.dtype}")
+    meta, y, fin, cst = gpu_run(w, chunk_size=cs, export="dense" if dense else None)
+    yr, fr, cr = oracle_run(w, chunk_size=cs)
+    tol = TOL[w.dtype]
+    check_close(y, yr, tol, f"{what} y")
+    check_close(fin, fr, tol, f"{what} final")
+    if dense:
+        n = int(meta.nchunks.item())
+        check_close(cst[:n], cr, tol, f"{what} chunk states")
+    assert int(meta.error_flag.item()) == 0
+
+
+def test_tiny_config_full():
+    _full_compare(cfg(0), what="tiny")
+
+
+@pytest.mark.parametrize("cs", [128, 32, 256])
+def test_768_token_config_chunk_sizes(cs):
+    """The bug-fix page's 768-token / chunk 128 case, and chunk-size invariance."""
+    _full_compare(cfg(1), cs=cs, what="768-token")
+
+
+SHAPES = [
+    # dtype, lengths, H, P, N, G, cs
+    ("bf16", [300, 77, 1, 0, 513], 4, 64, 128, 2, 256),
+    ("bf16", [200, 64, 65, 129], 4, 128, 128, 4, 64),
+    ("bf16", [130, 5, 260], 2, 32, 64, 1, 128),
+    ("bf16", [40, 3, 17], 2, 16, 16, 1, 16),
+    ("bf16", [100, 33], 2, 48, 256, 2, 32),
+    ("bf16", [1], 2, 64, 32, 2, 64),
+    ("f32", [300, 9], 2, 64, 128, 1, 256),
+    ("f32", [70, 0, 10], 3, 16, 32, 3, 64),
+    ("f32", [50, 64, 16], 2, 32, 64, 1, 16),
+    ("f32", [129], 2, 80, 16, 2, 128),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}-P{s[3]}-N{s[4]}-cs{s[6]}")
+def test_scan_shapes(shape):
+    dtype, L, H, P, N, G, cs = shape
+    w = make_inputs(L, H, P, N, G, cs, dtype=dtype, init_seqs=list(range(0, len(L), 2)),
+                    seed=sum(L) + H + P + N)
+    _full_compare(w, what=f"shape {shape}")
+
+
+SAMPLES = {2: ([0, 1, 7], [0, 41, 79]), 3: ([0, 20, 31, 63], [0, 17, 127]), 4: ([0, 3], [0, 13, 31])}
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_full_size_configs_sampled(idx):
+    """Full-size workloads in the benchmark's launch configuration; the oracle
+    recomputes sampled (sequence, head) pairs one by one."""
+    w = cfg(idx)
+    log(f"full config {idx}: T={w.total_tokens}")
+    meta, y, fin, cst = gpu_run(w, export="dense")
+    assert int(meta.error_flag.item()) == 0
+    tol = TOL[w.dtype]
+    seqs, heads = SAMPLES[idx]
+    cu = w.cu_seqlens.numpy()
+    start = meta.seq_chunk_start.cpu().numpy()
+    worst = 0.0
+    for s in seqs:
+        for h in heads:
+            yr, fr, cr = oracle_pair(w, s, h, chunk_size=w.chunk_size)
+            t0, t1 = cu[s], cu[s + 1]
+            worst = max(worst, check_close(y[t0:t1, h:h + 1], yr, tol, f"cfg{idx} y s={s} h={h}"))
+            worst = max(worst, check_close(fin[s:s + 1, h:h + 1], fr, tol, f"cfg{idx} final s={s} h={h}"))
+            cs_gpu = cst[start[s]:start[s + 1], h:h + 1]
+            worst = max(worst, check_close(cs_gpu, cr, tol, f"cfg{idx} chunk states s={s} h={h}"))
+    log(f"cfg{idx} worst err/bound {worst:.3f}")
+
+
+def _dev(a):
+    return torch.as_tensor(np.asarray(a)).cuda()
+
+
+def test_prefix_cache_checkpoint_and_resume():
+    """4 x 8894 tokens, chunk 64, block 256: the plan is bit-exact; the checkpoints
+    written at the source match the oracle's chunk states; resuming from the
+    checkpoint at token 6912 reproduces the tail outputs and the final state
+    (bit-identical to the full run, and within tolerance of the oracle)."""
+    w = cfg(4)
+    d = to_dev(w)
+    meta = ssd.varlen_metadata(d["cu_seqlens"], w.chunk_size, total_tokens=w.total_tokens)
+    bt = w.block_table
+    ckpt_src, dst = ssd.export_chunk_states(meta, bt, w.block_size, num_slots=w.num_slots)
+    ref_src, ref_dst = oracle.checkpoint_plan(w.cu_seqlens.numpy(), meta.seq_chunk_start.cpu().numpy(),
+                                              meta.max_chunks, bt.numpy(), w.block_size, w.chunk_size)
+    assert np.array_equal(ckpt_src.cpu().numpy(), ref_src)
+    assert np.array_equal(dst.cpu().numpy(), ref_dst)
+    cache = torch.full((w.num_slots, w.nheads, w.headdim, w.dstate), float("nan"), device="cuda")
+    _, y, fin, _ = gpu_run(w, export="cache", state_cache=cache, chunk_state_dst=dst, d=d)
+    assert int(meta.error_flag.item()) == 0
+    assert torch.isfinite(cache).all()    # every one of the 140 slots was written
+    tol = TOL[w.dtype]
+    cu = w.cu_seqlens.numpy()
+    for s in (0, 3):
+        for h in (0, 13, 31):
+            yr, fr, cr = oracle_pair(w, s, h, chunk_size=w.chunk_size)
+            for k in range(35):
+                src = ref_src[s, k] - meta.seq_chunk_start[s].item()
+                check_close(cache[bt[s, k]][h:h + 1][None], cr[src:src + 1], tol, f"slot s={s} k={k} h={h}")
+    # resume at token 6912 = block 27 start: init from the slot of block 26
+    R = CONFIGS[4]["resume_token"]
+    tail = []
+    for s in range(4):
+        t0 = int(cu[s])
+        tail.append(torch.arange(t0 + R, int(cu[s + 1])))
+    idx = torch.cat(tail)
+    Lt = int(cu[1]) - R
+    cu_t = torch.arange(5, dtype=torch.int32) * Lt
+    init = cache[bt[:, 26].long().cuda()].contiguous()
+    meta_t = ssd.varlen_metadata(cu_t.cuda(), w.chunk_size, total_tokens=4 * Lt)
+    y_t, fin_t = ssd.chunk_scan_varlen(d["x"][idx.cuda()].contiguous(), d["dt"][idx.cuda()].contiguous(),
+                                       d["A"], d["B"][idx.cuda()].contiguous(),
+                                       d["C"][idx.cuda()].contiguous(), meta_t, dt_bias=d["dt_bias"],
+                                       D=d["D"], initial_states=init,
+                                       has_initial_state=torch.ones(4, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(y_t.view(torch.int16), y[idx.cuda()].view(torch.int16)), "resumed y differs"
+    assert torch.equal(fin_t, fin), "resumed final state differs"
+
+
+def test_dense_export_scatter_equals_at_source():
+    w = make_inputs([700, 130, 0, 257], 4, 64, 64, 2, 64, dtype="bf16", init_seqs=[1, 3], seed=7,
+                    block_size=128, num_slots=40)
+    d = to_dev(w)
+    meta, y, fin, cst = gpu_run(w, export="dense", d=d)
+    cache_a = torch.zeros((40, 4, 64, 64), device="cuda")
+    ssd.export_chunk_states(meta, w.block_table, 128, chunk_states=cst, state_cache=cache_a)
+    _, dst = ssd.export_chunk_states(meta, w.block_table, 128, num_slots=40)
+    cache_b = torch.zeros_like(cache_a)
+    gpu_run(w, export="cache", state_cache=cache_b, chunk_state_dst=dst, d=d)
+    torch.cuda.synchronize()
+    assert torch.equal(cache_a, cache_b)
+    src, ref_dst = oracle.checkpoint_plan(w.cu_seqlens.numpy(), meta.seq_chunk_start.cpu().numpy(),
+                                          meta.max_chunks, w.block_table.numpy(), 128, 64)
+    assert np.array_equal(dst.cpu().numpy(), ref_dst)
+    used = sorted(int(v) for v in ref_dst if v >= 0)
+    unused = [i for i in range(40) if i not in used]
+    assert torch.count_nonzero(cache_a[unused]) == 0
+
+
+def test_plan_with_computed_prefix_bit_exact():
+    rng = np.random.default_rng(77)
+    for trial in range(12):
+        S = int(rng.integers(1, 9))
+        cs = int(2 ** rng.integers(4, 8))
+        bs = cs * int(rng.integers(1, 5))
+        L = rng.integers(0, 900, size=S)
+        ncomp = (rng.integers(0, 6, size=S) * (cs if trial % 3 else 5)).astype(np.int32)
+        maxb = int(max((n + max(l, 1) - 1) // bs for n, l in zip(ncomp, L))) + 1
+        bt = rng.permutation(S * maxb).reshape(S, maxb).astype(np.int32)
+        cu = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+        meta = ssd.varlen_metadata(_dev(cu), cs, total_tokens=int(cu[-1]))
+        src, dst = ssd.export_chunk_states(meta, torch.from_numpy(bt), bs,
+                                           num_computed_tokens=torch.from_numpy(ncomp), num_slots=S * maxb)
+        rs, rd = oracle.checkpoint_plan(cu, meta.seq_chunk_start.cpu().numpy(), meta.max_chunks, bt, bs, cs,
+                                        num_computed_tokens=ncomp)
+        assert np.array_equal(src.cpu().numpy(), rs), trial
+        assert np.array_equal(dst.cpu().numpy(), rd), trial
+        assert int(meta.error_flag.item()) == 0
