@@ -1,0 +1,192 @@
+"""Benchmark of the varlen SSD scan hot path on one MI355X.
+
+One step = the whole hot path over one batch already resident in HBM:
+  ssd_varlen_metadata  (chunk grid)
+  ssd_export_chunk_states  (block-checkpoint plan)
+  ssd_chunk_scan_varlen  (scan, writing the block checkpoints at the source)
+on the prefix-cache checkpoint workload (4 sequences x 8894 tokens, 32 heads,
+headdim 128, dstate 128, 4 groups, chunk 64, 256-token blocks, bf16 inputs,
+float32 state). Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config I] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
+COUNTERS = os.path.join(ROOT, "profiles", "scan_prefix_cache_4x8894_counters.json")
+KERNEL_SOURCES = ["ssd_scan.hpp", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_internal.h"]
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "selective_state_space_cu_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(w, n_ckpt):
+    """Bytes the method must move and flops it must do for one pass."""
+    T, H, P, N, G = w.total_tokens, w.nheads, w.headdim, w.dstate, w.ngroups
+    sx = 2 if w.dtype == "bf16" else 4
+    n_init = int(w.has_initial_state.sum())
+    state = H * P * N * 4
+    bytes_ = T * (2 * H * P * sx + 4 * H + 2 * G * N * sx) + (n_init + w.nseqs) * state + n_ckpt * state
+    flops = 0
+    for L in w.lengths:
+        for c0 in range(0, L, w.chunk_size):
+            Lc = min(w.chunk_size, L - c0)
+            flops += 2 * (Lc * (Lc + 1) // 2 * (N * G + P * H) + 2 * Lc * P * N * H)
+    return bytes_, flops
+
+
+def cpu_baseline(w, heads):
+    """The float64 oracle on the host cores over a bounded sample: every sequence,
+    the first `heads` heads, per-chunk state recording on."""
+    import oracle
+    per = w.nheads // w.ngroups          # heads per group
+    t = time.perf_counter()
+    for h0 in range(0, heads, per):      # one call per group, so the oracle sees one group
+        h1, g = min(h0 + per, heads), h0 // per
+        hs, gs = slice(h0, h1), slice(g, g + 1)
+        oracle.ssd_varlen(w.x[:, hs], w.dt[:, hs], w.dt_bias[hs], w.A[hs], w.B[:, gs], w.C[:, gs],
+                          w.D[hs], w.cu_seqlens, w.initial_states[:, hs], w.has_initial_state,
+                          chunk_size=w.chunk_size)
+    dt_s = time.perf_counter() - t
+    frac = heads / w.nheads
+    return dict(value=w.total_tokens * frac / dt_s, unit="tokens/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"all {w.nseqs} sequences ({w.total_tokens} tokens), heads 0-{heads - 1} of "
+                       f"{w.nheads} ({frac:.3f} of the work), float64, chunk-state recording on; "
+                       f"{dt_s:.2f} s wall; value scaled to whole-workload tokens/s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md for how the scan would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_cu_amd import ssd
+    from selective_state_space_cu_amd.workloads import CONFIGS, make_config
+
+    cfgd = CONFIGS[args.config]
+    w = make_config(args.config)
+    dev = torch.device("cuda:0")
+    d = {k: getattr(w, k).to(dev).contiguous() for k in
+         ("x", "dt", "dt_bias", "A", "B", "C", "D", "initial_states", "has_initial_state", "cu_seqlens")}
+    S, T, H, P, N = w.nseqs, w.total_tokens, w.nheads, w.headdim, w.dstate
+    has_blocks = w.block_table is not None
+    bt = w.block_table.to(dev) if has_blocks else None
+    y = torch.empty_like(d["x"])
+    fin = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+    cache = (torch.zeros((w.num_slots, H, P, N), dtype=torch.float32, device=dev)
+             if has_blocks else None)
+    init = d["initial_states"] if int(w.has_initial_state.sum()) else None
+    has = d["has_initial_state"] if init is not None else None
+
+    ev = []
+
+    def step(timed):
+        meta = ssd.varlen_metadata(d["cu_seqlens"], w.chunk_size, total_tokens=T)
+        dst = None
+        if has_blocks:
+            _, dst = ssd.export_chunk_states(meta, bt, w.block_size, num_slots=w.num_slots)
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        ssd.chunk_scan_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], meta, dt_bias=d["dt_bias"],
+                              D=d["D"], initial_states=init, has_initial_state=has, y=y,
+                              final_states=fin, chunk_states=cache, chunk_state_dst=dst)
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+        return meta
+
+    for _ in range(args.warmup):
+        meta = step(False)
+    torch.cuda.synchronize()
+    if int(meta.error_flag.item()) != 0:
+        raise RuntimeError("device error flag set")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dstb = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dstb.copy_(src)
+        torch.cuda.synchronize()
+
+    n_ckpt = 0
+    if has_blocks:
+        _, dst = ssd.export_chunk_states(meta, bt, w.block_size, num_slots=w.num_slots)
+        n_ckpt = int((dst >= 0).sum().item())
+    alg_bytes, alg_flops = algorithmic_work(w, n_ckpt)
+    achieved = alg_bytes / (scan_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            c = json.load(f)
+        if c.get("kernel_hash") == kernel_hash() and c.get("config") == args.config:
+            traffic = c["hbm_bytes_per_launch"]
+    ms_per_step = wall * 1e3 / args.steps
+    out = {
+        "metric": "SSD varlen prefill tokens/s on 1 MI355X; % of HBM/MFMA roofline",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {"workload": cfgd["name"], "nseqs": S, "total_tokens": T, "nheads": H,
+                   "headdim": P, "dstate": N, "ngroups": w.ngroups, "chunk_size": w.chunk_size,
+                   "block_size": w.block_size, "checkpoints_per_step": n_ckpt,
+                   "step": "metadata + checkpoint plan + scan with at-source checkpoint export"},
+        "roofline": {"bound": "hbm", "kernel": "ssd_scan_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes": alg_bytes,
+                     "kernel_ms": scan_ms,
+                     "mfma_tflops": alg_flops / (scan_ms * 1e-3) / 1e12,
+                     "mfma_frac": alg_flops / (scan_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, H))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
