@@ -150,6 +150,12 @@ template <> struct Ops<uint16_t> {
     __device__ static uint32_t tr_addr(const unsigned char *t, int pitch, int kb, int col0, int q) {
         return lds_addr(t + (kb + (q >> 2)) * pitch + (col0 + 4 * (q & 3)) * 2);
     }
+    // Same, but the fragment's 16 columns are the paired-state rows
+    // {8m + j : m, j = 0..3} (+ the tile's immediate offset): source lane q
+    // supplies the 4 columns at 8 (q%4), so result lane q gets column 8 (q/4) + q%4.
+    __device__ static uint32_t tr_addr_pairs(const unsigned char *t, int pitch, int kb, int q) {
+        return lds_addr(t + (kb + (q >> 2)) * pitch + 8 * (q & 3) * 2);
+    }
     template <int F0, int F1, int R4>   // R4 = 4 * pitch (second read of a fragment)
     __device__ static void tr2(uint32_t addr, Frag &a, Frag &b) {
         u32x2 r0, r1, r2, r3;
@@ -237,6 +243,9 @@ template <> struct Ops<float> {
     __device__ static uint32_t tr_addr(const unsigned char *t, int pitch, int kb, int col0, int q) {
         return lds_addr(t + kb * pitch + (col0 + q) * 4);
     }
+    __device__ static uint32_t tr_addr_pairs(const unsigned char *t, int pitch, int kb, int q) {
+        return lds_addr(t + kb * pitch + (8 * (q >> 2) + (q & 3)) * 4);
+    }
     __device__ static Frag tr_one(uint32_t addr, int pitch) {
         const unsigned char *p = lds_ptr(addr);
         Frag f;
@@ -290,7 +299,9 @@ struct ScanShape {
     static constexpr int kThreads = 64 * NW;
     static constexpr int kCols = 16 * NW;            // headdim columns per workgroup
     static constexpr int kES = sizeof(T);
-    static constexpr int kRB = N * kES;              // data bytes per B/C tile row
+    static constexpr int kNE = N < 32 ? 32 : N;      // state width in LDS / registers (zero-padded)
+    static constexpr int kRG = N * kES;              // bytes per B/C row in global memory
+    static constexpr int kRB = kNE * kES;            // data bytes per B/C tile row in LDS
     static constexpr int kRX = kCols * kES;          // data bytes per x tile row
     static constexpr int kPB = kRB + 16;             // padded LDS row pitch (B/C)
     static constexpr int kPX = kRX + 16;             // padded LDS row pitch (x)
@@ -300,9 +311,9 @@ struct ScanShape {
     static constexpr int kIX = (kTileX / 1024 + NW - 1) / NW;   // (x)
     static constexpr int kID = (4 + NW - 1) / NW;               // (dt: 4 x 64 floats)
     static constexpr int kLoads = 2 * kIB + kIX + kID;          // vector memory loads per wave per step
-    static constexpr int kNT = N / 16;                          // 16-row state tiles
+    static constexpr int kNT = kNE / 16;                        // 16-row state tiles (even)
     static constexpr int kYStores = 4;                          // y stores per wave per step
-    static constexpr int kNK = (N + 31) / 32;                   // 32-deep steps over dstate
+    static constexpr int kNK = kNE / 32;                        // 32-deep steps over dstate
     static constexpr int kMP = kTile + Ops<T>::kPad;            // decay matrix pitch (elements)
     // LDS: NST stages of [B | C | x | dt(256 f32)] + decay matrix + 2 scan tables + 1 KB sink
     static constexpr int kStage = 2 * kTileB + kTileX + 1024;
@@ -380,20 +391,19 @@ __device__ __forceinline__ void chunk_scan(float *tab, int Lc, float bias, float
     }
 }
 
-// Transposed reads of NT consecutive 16-column fragments (state tiles t = T0..)
-// that share one base address; fragment t sits 16*t elements to the right.
+// Transposed reads of the NT state-tile fragments of B^T (rows n of the paired
+// state layout) sharing one base address (tr_addr_pairs): tile t = 2c + u
+// starts at column 32 c + 4 u.
 template <typename O, int NT, int ES, int R4, int T0 = 0>
 __device__ __forceinline__ void tr_tiles(uint32_t addr, typename O::Frag (&f)[NT]) {
+    constexpr auto off = [](int t) { return (32 * (t >> 1) + 4 * (t & 1)) * ES; };
     if constexpr (T0 + 4 <= NT) {
-        O::template tr4<16 * T0 * ES, 16 * (T0 + 1) * ES, 16 * (T0 + 2) * ES, 16 * (T0 + 3) * ES, R4>(
-            addr, f[T0], f[T0 + 1], f[T0 + 2], f[T0 + 3]);
+        O::template tr4<off(T0), off(T0 + 1), off(T0 + 2), off(T0 + 3), R4>(addr, f[T0], f[T0 + 1], f[T0 + 2],
+                                                                            f[T0 + 3]);
         tr_tiles<O, NT, ES, R4, T0 + 4>(addr, f);
     } else if constexpr (T0 + 2 <= NT) {
-        O::template tr2<16 * T0 * ES, 16 * (T0 + 1) * ES, R4>(addr, f[T0], f[T0 + 1]);
+        O::template tr2<off(T0), off(T0 + 1), R4>(addr, f[T0], f[T0 + 1]);
         tr_tiles<O, NT, ES, R4, T0 + 2>(addr, f);
-    } else if constexpr (T0 < NT) {
-        typename O::Frag unused;
-        O::template tr2<16 * T0 * ES, 16 * T0 * ES, R4>(addr, f[T0], unused);
     }
 }
 
@@ -411,7 +421,7 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     using O = Ops<T>;
     using Frag = typename O::Frag;
     using SH = ScanShape<T, NW, N>;
-    constexpr int NST = SH::kNST, RB = SH::kRB, RX = SH::kRX, PB = SH::kPB, PX = SH::kPX;
+    constexpr int NST = SH::kNST, RG = SH::kRG, RX = SH::kRX, PB = SH::kPB, PX = SH::kPX;
     constexpr int MP = SH::kMP, ES = SH::kES, NT = SH::kNT, NK = SH::kNK;
     constexpr int JS = (4 + NW - 1) / NW;   // decay-matrix column blocks per wave
 
@@ -459,14 +469,19 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         if (++kt > m) { kt = 0; if (++m >= ntiles(k)) { m = 0; ++k; } }
     };
 
-    // carried state: st[t][r] = h[p = pw + q][n = 16 t + 4 g + r]
+    // Carried state, in pairs of 16-row tiles: st[2c+u][r] = h[p = pw + q][n = 32 c + 8 g + 4 u + r],
+    // i.e. lane group g holds the 8 consecutive n that the 32-deep operand slots of
+    // group g cover, so the state feeds C . h^T with the same C fragments as C . B^T.
+    // Rows n >= N (dstate < 32 only) stay zero.
     f32x4 st[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) st[t] = f32x4{0, 0, 0, 0};
+    auto state_n = [&](int t) { return 32 * (t >> 1) + 8 * g + 4 * (t & 1); };
     if (a.init != nullptr && (a.has_init == nullptr || a.has_init[s] != 0)) {
         const float *src = a.init + ((int64_t)(s * H + h) * P + pw + q) * N;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) st[t] = *reinterpret_cast<const f32x4 *>(src + 16 * t + 4 * g);
+        for (int t = 0; t < NT; ++t)
+            if (state_n(t) < N) st[t] = *reinterpret_cast<const f32x4 *>(src + state_n(t));
     }
 
     // scan tables of chunk 0, from global dt
@@ -483,7 +498,7 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #pragma unroll
     for (int i = 0; i < SH::kIB; ++i) {
         const int j = wave + NW * i, o = 1024 * j + 16 * lane, r = o / PB, pos = o % PB;
-        go.b[i] = (j < SH::kTileB / 1024 && pos < RB) ? r * brow + pos : kOob;
+        go.b[i] = (j < SH::kTileB / 1024 && pos < RG) ? r * brow + pos : kOob;
     }
 #pragma unroll
     for (int i = 0; i < SH::kIX; ++i) {
@@ -497,8 +512,9 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     }
 
     // Fetch the tiles of step (k, m, kt) into stage buffer `slot` (out-of-range,
-    // zero-filling loads when k >= nch). Always SH::kLoads instructions per wave.
-    auto fetch = [&](int slot, int k, int m, int kt) {
+    // zero-filling loads when k >= nch), in two parts issued at different points
+    // of a step. Always 2*kIB + kIX + kID instructions per wave.
+    auto fetch_bc = [&](int slot, int k, int m, int kt) {
         unsigned char *stg = smem + slot * SH::kStage;
         const bool live = k < nch;
         const int Lc = live ? chunk_len(k) : 0;
@@ -509,13 +525,6 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             (void *)(Bg + ((t0 + kTile * kt) * G + grp) * N), 0, vk * brow, kBufFlags);
         const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(Cg + ((t0 + kTile * m) * G + grp) * N), 0, vm * brow, kBufFlags);
-        const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(xg + ((t0 + kTile * kt) * H + h) * P + p0), 0, vk * xrow, kBufFlags);
-        // dt of chunk k+1 rides with the first step of chunk k
-        const bool dnext = live && m == 0 && kt == 0 && k + 1 < nch;
-        const int64_t t1 = tb + (int64_t)(k + 1) * cs;
-        const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.dt + (dnext ? t1 : 0) * H + h), 0, dnext ? chunk_len(k + 1) * H * 4 : 0, kBufFlags);
 #pragma unroll
         for (int i = 0; i < SH::kIB; ++i) {
             const int j = wave + NW * i;   // 1 KB block of the tile
@@ -524,6 +533,20 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rC, (lds_void *)(ok ? stg + SH::kTileB + 1024 * j : sink), 16,
                                                      go.b[i], 0, 0, 0);
         }
+    };
+    auto fetch_xd = [&](int slot, int k, int m, int kt) {
+        unsigned char *stg = smem + slot * SH::kStage;
+        const bool live = k < nch;
+        const int Lc = live ? chunk_len(k) : 0;
+        const int64_t t0 = tb + (int64_t)k * cs;
+        const int vk = live ? min(kTile, Lc - kTile * kt) : 0;
+        const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(xg + ((t0 + kTile * kt) * H + h) * P + p0), 0, vk * xrow, kBufFlags);
+        // dt of chunk k+1 rides with the first step of chunk k
+        const bool dnext = live && m == 0 && kt == 0 && k + 1 < nch;
+        const int64_t t1 = tb + (int64_t)(k + 1) * cs;
+        const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.dt + (dnext ? t1 : 0) * H + h), 0, dnext ? chunk_len(k + 1) * H * 4 : 0, kBufFlags);
 #pragma unroll
         for (int i = 0; i < SH::kIX; ++i) {
             const int j = wave + NW * i;
@@ -562,7 +585,8 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     if constexpr (NST > 1) {
 #pragma unroll
         for (int p = 0; p < NST - 1; ++p) {
-            fetch(p, fk, fm, fkt);
+            fetch_bc(p, fk, fm, fkt);
+            fetch_xd(p, fk, fm, fkt);
             if (fk < nch) advance(fk, fm, fkt);
             dummy_y_stores();
         }
@@ -584,16 +608,13 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         const bool last_m = (m == ntile - 1);
 
         if constexpr (NST == 1) {
-            fetch(0, k, m, kt);
+            fetch_bc(0, k, m, kt);
+            fetch_xd(0, k, m, kt);
             __builtin_amdgcn_s_waitcnt(WaitVm<0>::imm);
         } else {
             wait_stage(NST == 3 ? ex1 + ex2 : ex1);
         }
         lds_barrier();   // stage `slot` and this chunk's scan tables are visible
-        if constexpr (NST > 1) {
-            fetch((step + NST - 1) % NST, fk, fm, fkt);
-            if (fk < nch) advance(fk, fm, fkt);
-        }
         // checkpoint slot of this chunk (scalar load, consumed at the chunk's end)
         int dst = -1;
         if (a.chunk_states != nullptr && last_m && kt == m) {
@@ -607,28 +628,41 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         }
         const float sL = sS[Lc - 1];   // chunk total decay, at its last valid token
 
+        // C fragments of M-tile m (rows i; 32-deep slots n = 32 c + 8 g + s), shared by
+        // the inter-chunk product and C . B^T, and B fragments of this wave's
+        // column blocks jsub = wave + NW*jj
+        Frag cfm[4][NK], bf[JS][NK];
+        float ei[4], si[4], sj[JS][4], dj[JS][4];
+#pragma unroll
+        for (int isub = 0; isub < 4; ++isub) {
+#pragma unroll
+            for (int c = 0; c < NK; ++c) cfm[isub][c] = O::rowk(sC, PB, 16 * isub + q, 32 * c + 8 * g);
+            si[isub] = sS[kTile * m + 16 * isub + q];
+            ei[isub] = sE[kTile * m + 16 * isub + q];
+        }
+#pragma unroll
+        for (int jj = 0; jj < JS; ++jj) {
+            const int jsub = (wave + NW * jj) & 3;
+#pragma unroll
+            for (int c = 0; c < NK; ++c) bf[jj][c] = O::rowk(sB, PB, 16 * jsub + q, 32 * c + 8 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int jc = kTile * kt + 16 * jsub + 4 * g + r;
+                sj[jj][r] = sS[jc];
+                dj[jj][r] = sD[jc];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
         if (kt == 0) {
             // (6) inter-chunk term Y^T = h_in . C^T, then scale column i by 2^(s_i)
-            Frag cf[NK][4];
-#pragma unroll
-            for (int c = 0; c < NK; ++c)
-#pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    cf[c][it] = O::rowk_perm(sC, PB, 16 * it + q, 32 * c, g);
-                    if (N < 32) cf[c][it] = O::low_half(cf[c][it]);   // dstate 16: slots n >= 16 are zero
-                }
-            float ei[4];
-#pragma unroll
-            for (int it = 0; it < 4; ++it) ei[it] = sE[kTile * m + 16 * it + q];
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int it = 0; it < 4; ++it) acc[it] = f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int c = 0; c < NK; ++c) {
-                const f32x4 zero = {0, 0, 0, 0};
-                const Frag hf = O::from_f32(st[2 * c], (2 * c + 1 < NT) ? st[2 * c + 1] : zero);
+                const Frag hf = O::from_f32(st[2 * c], st[2 * c + 1]);
 #pragma unroll
-                for (int it = 0; it < 4; ++it) acc[it] = O::mma(acc[it], hf, cf[c][it]);
+                for (int it = 0; it < 4; ++it) acc[it] = O::mma(acc[it], hf, cfm[it][c]);
             }
 #pragma unroll
             for (int it = 0; it < 4; ++it) acc[it] *= ei[it];
@@ -639,54 +673,29 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 for (int t = 0; t < NT; ++t) st[t] *= e;
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NST > 1) fetch_bc((step + NST - 1) % NST, fk, fm, fkt);   // overlaps the matrix ops
 
-        // (5) CB^T sub-tiles of (M-tile m, K-tile kt) -> masked decay matrix in LDS.
-        // This wave owns column blocks jsub = wave + NW*jj for all four row blocks;
-        // sub-tiles above the diagonal come out as zeros through the mask.
-        {
-            Frag bf[JS][NK], cfm[4][NK];
-            float sj[JS][4], dj[JS][4], si[4];
+        // (5) CB^T sub-tiles of (M-tile m, K-tile kt) -> masked decay matrix in LDS;
+        // sub-tiles above the diagonal come out as zeros through the mask
 #pragma unroll
-            for (int jj = 0; jj < JS; ++jj) {
-                const int jsub = (wave + NW * jj) & 3;
+        for (int jj = 0; jj < JS; ++jj) {
+            const int jsub = (wave + NW * jj) & 3;
+            if (wave + NW * jj < 4) {
 #pragma unroll
-                for (int c = 0; c < NK; ++c) bf[jj][c] = O::rowk(sB, PB, 16 * jsub + q, (32 * c + 8 * g) % N);
+                for (int isub = 0; isub < 4; ++isub) {
+                    f32x4 cb = {0, 0, 0, 0};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int jc = kTile * kt + 16 * jsub + 4 * g + r;
-                    sj[jj][r] = sS[jc];
-                    dj[jj][r] = sD[jc];
-                }
-            }
+                    for (int c = 0; c < NK; ++c) cb = O::mma(cb, bf[jj][c], cfm[isub][c]);
+                    const int il = 16 * isub + q, ic = kTile * m + il;
+                    float v[4];
 #pragma unroll
-            for (int isub = 0; isub < 4; ++isub) {
-#pragma unroll
-                for (int c = 0; c < NK; ++c) {
-                    cfm[isub][c] = O::rowk(sC, PB, 16 * isub + q, 32 * c + 8 * g);
-                    if (N < 32 && 8 * g >= N) cfm[isub][c] = Frag{};   // dstate < 32: slots past N are zero
-                }
-                si[isub] = sS[kTile * m + 16 * isub + q];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int jj = 0; jj < JS; ++jj) {
-                const int jsub = (wave + NW * jj) & 3;
-                if (wave + NW * jj < 4) {
-#pragma unroll
-                    for (int isub = 0; isub < 4; ++isub) {
-                        f32x4 cb = {0, 0, 0, 0};
-#pragma unroll
-                        for (int c = 0; c < NK; ++c) cb = O::mma(cb, bf[jj][c], cfm[isub][c]);
-                        const int il = 16 * isub + q, ic = kTile * m + il;
-                        float v[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int jc = kTile * kt + 16 * jsub + 4 * g + r;
-                            const float dec = fast_exp2(si[isub] - sj[jj][r]) * dj[jj][r];
-                            v[r] = (jc <= ic && ic < Lc) ? cb[r] * dec : 0.0f;
-                        }
-                        O::mstore4(sM, MP, il, 16 * jsub + 4 * g, v);
+                    for (int r = 0; r < 4; ++r) {
+                        const int jc = kTile * kt + 16 * jsub + 4 * g + r;
+                        const float dec = fast_exp2(si[isub] - sj[jj][r]) * dj[jj][r];
+                        v[r] = (jc <= ic && ic < Lc) ? cb[r] * dec : 0.0f;
                     }
+                    O::mstore4(sM, MP, il, 16 * jsub + 4 * g, v);
                 }
             }
         }
@@ -714,12 +723,17 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) acc[it] = O::mma(acc[it], xf[ks], mf[it][ks]);
 
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NST > 1) {
+            fetch_xd((step + NST - 1) % NST, fk, fm, fkt);
+            if (fk < nch) advance(fk, fm, fkt);
+        }
         if (last_m) {
             // (3) chunk state h += B^T . (w o x)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 Frag bt[NT];
-                tr_tiles<O, NT, ES, 4 * PB>(O::tr_addr(sB, PB, 32 * ks + 8 * g, 0, q), bt);
+                tr_tiles<O, NT, ES, 4 * PB>(O::tr_addr_pairs(sB, PB, 32 * ks + 8 * g, q), bt);
                 const Frag xw = O::scale(xf[ks], w[ks]);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) st[t] = O::mma(st[t], bt[t], xw);
@@ -749,10 +763,11 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 float *cbase = a.chunk_states + ((int64_t)dst * H + h) * P * N + (int64_t)p0 * N;
                 const __amdgpu_buffer_rsrc_t re =
                     __builtin_amdgcn_make_buffer_rsrc((void *)cbase, 0, SH::kCols * N * 4, kBufFlags);
-                const int eoff = ((16 * wave + q) * N + 4 * g) * 4;
+                const int eoff = (16 * wave + q) * N * 4;
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st[t]), re, eoff + 64 * t, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st[t]), re,
+                                                           state_n(t) < N ? eoff + 4 * state_n(t) : kOob, 0, 0);
             }
         }
         if constexpr (NST == 1) lds_barrier();   // the single stage is refilled next step
@@ -761,7 +776,8 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
     float *fd = a.final_states + ((int64_t)(s * H + h) * P + pw + q) * N;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4 *>(fd + 16 * t + 4 * g) = st[t];
+    for (int t = 0; t < NT; ++t)
+        if (state_n(t) < N) *reinterpret_cast<f32x4 *>(fd + state_n(t)) = st[t];
 }
 #endif
 
