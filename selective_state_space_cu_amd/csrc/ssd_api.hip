@@ -89,9 +89,11 @@ ssd_status ssd_chunk_scan_varlen(const void *x, const float *dt, const float *dt
     a.T = meta->total_tokens; a.S = meta->nseqs; a.H = nheads; a.P = headdim; a.G = ngroups;
     a.cs = meta->chunk_size; a.max_chunks = meta->max_chunks;
     a.capacity = chunk_states ? chunk_states_capacity : 0;
-    // headdim tile per workgroup: 64 columns (4 waves) when it divides headdim
+    // headdim tile per workgroup: 64 columns when it divides headdim (8 waves,
+    // two per 16-column block, for bf16 up to dstate 128; else 4 waves),
+    // else 32 (2 waves) or 16 (1 wave)
     const int waves = headdim % 64 == 0 ? 4 : (headdim % 32 == 0 ? 2 : 1);
-    a.nptiles = headdim / (16 * waves);
+    a.nptiles = headdim / (16 * (waves < 4 ? waves : 4));
     if (meta->nseqs == 0) return SSD_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = in_dtype == SSD_BF16 ? ssd::launch_scan_bf16(a, waves, dstate, s)

@@ -1,42 +1,61 @@
-// Fused chunk-walk kernel of the Mamba2 SSD varlen scan for gfx950.
+// Fused tile-walk kernel of the Mamba2 SSD varlen scan for gfx950.
 //
 // One workgroup owns one (sequence, head, headdim tile of 16*NW columns) and
-// walks that sequence's chunks in order; each of its NW waves owns 16 headdim
-// columns and carries their (16 x N) float32 state in registers from chunk to
-// chunk, so chunk states never round-trip through HBM (only exported
+// walks that sequence's tokens in tiles, in order; each of its NW waves owns
+// 16 headdim columns and carries their (16 x N) float32 state in registers
+// from tile to tile, so states never round-trip through HBM (only exported
 // checkpoints and final states are written).
 //
-// Per chunk (the chunked decomposition of the SSD layer; the numbers follow the
+// Tiles hold min(chunk_size, 64) tokens. A chunk longer than 64 tokens is
+// walked as consecutive 64-token tiles with the state passed between them:
+// the chunked form is an exact re-association of the recurrence, so this is
+// the same linear map as the quadratic form over the whole chunk, with less
+// work. chunk_size still fixes the chunk grid and which states are exported
+// (the state after the last token of each chunk).
+//
+// Per tile (the chunked decomposition of the SSD layer; the numbers follow the
 // kernel list of the problem statement):
 //   (2) delta_j = softplus(dt_j + dt_bias), cumulative log-decay s_j =
-//       sum_{k<=j} delta_k*A (inclusive, chunk-local, log2 units), plus the
-//       per-token factors 2^(s_i) and w_j = delta_j 2^(s_last - s_j), one wave,
-//       one chunk ahead of its use;
+//       sum_{k<=j} delta_k*A (inclusive, tile-local, log2 units) and per-token
+//       factors, computed one tile ahead of their use;
 //   (5) CB^T = B . C^T per 16x16 sub-tile on the matrix cores, masked by the
-//       segment-sum decay: M[i][j] = CB[i][j] * 2^(s_i - s_j) * delta_j, j <= i;
+//       segment-sum decay: M[i][j] = CB[i][j] * 2^(s_i - s_j) * delta_j for
+//       j <= i, plus D on the diagonal (the skip term D x rides with (6));
 //   (6) Y^T = h_in . C^T scaled per token by 2^(s_i)   (inter-chunk term)
-//           + x^T . M^T                                (intra-chunk term)
-//           + D x;
-//   (3,4) h_out = 2^(s_last) h_in + B^T . (w o x).
-// The decay that reaches the entering state at token i is 2^(s_i) with s_i
-// the INCLUSIVE cumsum at i, and the chunk's total decay is read at the chunk's
-// last valid token -- never at a tile start or past the sequence end (the
-// init-state decay rule of the varlen bug-fix page).
+//           + x^T . M^T                                (intra-chunk and D terms);
+//   (3,4) h_out = 2^(s_last) h_in + B^T . (w o x),  w_j = delta_j 2^(s_last - s_j).
+// The decay that reaches the entering state at token i is 2^(s_i) with s_i the
+// INCLUSIVE cumsum at i, and the total decay is read at the tile's last valid
+// token (s is constant past it, since delta is 0 there) -- never past the
+// sequence end (the init-state decay rule of the varlen bug-fix page).
 //
-// Chunks longer than 64 tokens run as 64-row M-tiles; M-tile m streams the
-// chunk's K-tiles 0..m (quadratic intra-chunk form over the whole chunk), and
-// the last M-tile also accumulates the chunk state. A "step" is one
-// (chunk, M-tile, K-tile) triple.
+// Decay matrix: on a diagonal 16x16 sub-tile the factor is 2^(s_i - s_j)
+// itself, masked for j > i. Below the diagonal (row block I > column block J)
+// it is split at the ends of blocks J and I-1:
+//   2^(s_i - s_j) delta_j = V_i * P(I, J) * B_j,  V_i = 2^(s_i - s_end(I-1)),
+//   P(I, J) = 2^(s_end(I-1) - s_end(J)),  B_j = delta_j 2^(s_end(J) - s_j),
+// each factor at most 1 for a decaying state (A <= 0), so nothing overflows,
+// and each element costs two multiplies instead of an exp2. Sub-tiles above
+// the diagonal get P = 0.
 //
-// Memory pipeline: the B, C and x tiles (and the next chunk's dt) of step
-// i + NST - 1 are fetched with direct-to-LDS buffer loads while step i
-// computes (NST stage buffers). Every step issues the same number of vector
-// memory instructions (out-of-range buffer lanes are zero-filled on load and
-// dropped on store), so an exact s_waitcnt vmcnt(n) waits for one stage only;
-// barriers are bare s_barrier after an LDS-count wait. Tile rows in LDS are
-// padded by 16 bytes, which keeps the row-strided and transposed fragment reads
-// below free of bank conflicts and their addresses affine (a per-lane base plus
-// compile-time offsets); the direct loads skip the pad slots.
+// Memory pipeline: the B, C and x tiles of step i + NST - 1 (and the dt of the
+// tile after it) are fetched with direct-to-LDS buffer loads during step i
+// (NST stage buffers). Every step issues the same number of vector memory
+// instructions (out-of-range buffer lanes are zero-filled on load and dropped
+// on store), so an exact s_waitcnt vmcnt(n) waits for one stage only. The
+// direct loads are issued through inline assembly: the compiler does not see
+// them, so none of its LDS reads waits for them (it would otherwise wait for
+// all of them before every transposed read); the stage hand-off is ordered by
+// those exact waits and the barrier after them. The step loop is unrolled over
+// the NST stages, so LDS addresses are per-lane bases plus immediates.
+//
+// LDS layouts (conflict-free for the reads that dominate):
+//   C tile: rows padded by 16 bytes, so the 16 rows of a row-fragment read
+//           start on 16 distinct 16-byte bank groups;
+//   B tile: rows padded by 32 bytes plus 128 bytes after every 8 rows, so the
+//           eight rows {0..3, 8..11} (or {4..7, 12..15}) that one transposed
+//           read touches start on eight distinct 32-byte bank groups;
+//   x tile: rows padded by 16 bytes.
 //
 // Operand layouts on the matrix cores (v_mfma_f32_16x16x32_bf16; the f32 path
 // issues eight v_mfma_f32_16x16x4f32 per 32-deep step with the same
@@ -45,13 +64,21 @@
 // operands use the same one, which lets
 //   - token-major tiles in LDS feed operands that contract over tokens through
 //     the gfx950 LDS transpose read (ds_read_b64_tr_b16), and
-//   - the carried state, held in the accumulator layout of B^T.(w o x), feed the
-//     inter-chunk product directly from registers (C is read with the matching
-//     permuted k order).
+//   - the carried state, held in the accumulator layout of B^T.(w o x), feed
+//     the inter-chunk product directly from registers: its k slots take n in
+//     the order the accumulator tiles hold it (4 rows of one tile, then 4 of
+//     the next), and C is read in that order; C . B^T reads B the same way and
+//     shares the C fragments.
+// Row blocks are visited in the order ib[d] = (wave + d) mod 4, so for the
+// decay-matrix column block J = wave the offset d from the diagonal is a
+// compile-time index: d = 0 is the diagonal (mask and D term) and every wave
+// runs the same code.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "ssd_internal.h"
 
@@ -64,18 +91,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kTile = 64;       // tokens per M-/K-tile
-constexpr int kMaxChunk = 256;  // largest supported chunk_size
+constexpr int kTile = 64;       // tokens per tile
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kBufFlags = 0x00020000;  // raw buffer resource word 3 on gfx9-family parts
 constexpr int kOob = 0x40000000;       // buffer offset beyond every tile's range (zero fill / dropped)
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
-
-__device__ __forceinline__ float softplus(float u) { return u > 20.0f ? u : log1pf(expf(u)); }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     bf16x2 v = {(__bf16)lo, (__bf16)hi};
@@ -105,108 +128,80 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)(p);
 }
-__device__ __forceinline__ const unsigned char *lds_ptr(uint32_t a) {
-    return (const unsigned char *)(const __attribute__((address_space(3))) unsigned char *)(uintptr_t)a;
+
+// Direct-to-LDS buffer loads: lane l's 16 (or 4) bytes land at LDS byte
+// address lds + 16 l (or + 4 l). Issued through inline assembly (see the
+// memory pipeline note above), with a raw buffer resource made of wave-uniform
+// words: base address, num_records bytes (loads past it read zero), stride 0.
+__device__ __forceinline__ u32x4 dma_rsrc(const void *base, int num_records) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(num_records), (uint32_t)kBufFlags};
 }
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const u32x4 &r, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const u32x4 &r, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // ---------------------------------------------------------------------------
-// Element traits: fragment type, LDS tile reads, matrix op. A tile row holds
-// `pitch` bytes (data + 16 bytes of padding); element e of row r is at
-// r*pitch + e*sizeof(T).
+// Element traits: fragment type, LDS fragment reads, matrix op.
 // ---------------------------------------------------------------------------
 template <typename T> struct Ops;
-
-template <typename T>
-__device__ __forceinline__ int lds_off(int row, int e, int pitch) { return row * pitch + e * (int)sizeof(T); }
 
 // bfloat16 (stored as uint16_t)
 template <> struct Ops<uint16_t> {
     struct Frag { u32x4 w; };
-    static constexpr int kPad = 8;  // decay matrix row padding (elements)
+    static constexpr int kPad = 16;      // decay matrix row padding (elements): 160-byte rows
+    static constexpr int kHiOff = 32;    // bytes from the low to the high half of a permuted row fragment
 
     __device__ static f32x4 mma(f32x4 acc, const Frag &a, const Frag &b) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.w),
                                                        __builtin_bit_cast(bf16x8, b.w), acc, 0, 0, 0);
     }
-    // slots s <- tile[row][k + s] (k a multiple of 8)
-    __device__ static Frag rowk(const unsigned char *t, int pitch, int row, int k) {
-        return Frag{*reinterpret_cast<const u32x4 *>(t + lds_off<uint16_t>(row, k, pitch))};
-    }
-    // slots 0..3 <- tile[row][k0 + 4g + s]; slots 4..7 <- tile[row][k0 + 16 + 4g + s - 4]
-    __device__ static Frag rowk_perm(const unsigned char *t, int pitch, int row, int k0, int g) {
-        u32x2 lo = *reinterpret_cast<const u32x2 *>(t + lds_off<uint16_t>(row, k0 + 4 * g, pitch));
-        u32x2 hi = *reinterpret_cast<const u32x2 *>(t + lds_off<uint16_t>(row, k0 + 16 + 4 * g, pitch));
+    // Row fragment in the permuted 32-deep k order of lane group g: slots 0..3
+    // <- row[k0 + 4g ..], slots 4..7 <- row[k0 + 16 + 4g ..]; p points at
+    // row[k0 + 4g]. The two halves are read as separate 8-byte loads (volatile,
+    // so they are not merged into one two-address read: on this layout two
+    // single reads cost a quarter of the merged one's bank cycles).
+    __device__ static Frag rowk_perm(const unsigned char *p) {
+        typedef const volatile __attribute__((address_space(3))) u32x2 lds_u32x2;
+        const uint32_t la = lds_addr(p);
+        const u32x2 lo = *(lds_u32x2 *)(uintptr_t)la;
+        const u32x2 hi = *(lds_u32x2 *)(uintptr_t)(la + kHiOff);
         return Frag{u32x4{lo.x, lo.y, hi.x, hi.y}};
     }
-    // Transposed fragment reads of a token-major tile: slots s <- tile[kb + s][col0 + q].
-    // Within each 16-lane group, lane q supplies the 4 elements at row kb + q/4,
-    // columns col0 + 4(q%4)..+3, and receives column col0 + q of rows kb..kb+3
-    // (ds_read_b64_tr_b16; a fragment is two reads, rows kb.. and kb+4..).
-    // `addr` is this lane's LDS byte address for the first fragment; fragment f
-    // is at byte offset F_f (a compile-time immediate). The reads are issued as
-    // one inline-asm statement that also waits for them, so in-flight
-    // direct-to-LDS loads are not drained and no register holds a pending value
-    // outside the statement.
-    __device__ static uint32_t tr_addr(const unsigned char *t, int pitch, int kb, int col0, int q) {
-        return lds_addr(t + (kb + (q >> 2)) * pitch + (col0 + 4 * (q & 3)) * 2);
+    // Transposed fragment of a token-major tile (gfx950 ds_read_b64_tr_b16):
+    // slots s <- tile[kb + s][column of the lane]. Within each 16-lane group,
+    // lane q supplies the 4 elements at row kb + q/4, columns 4(q%4)..+3 of the
+    // group's 16 columns, and receives column q of rows kb..kb+3; a fragment is
+    // two such reads (rows kb.. and kb+4.., `four_rows` bytes apart). The
+    // lane's first address is row kb + tr_row(q), column col0 + tr_col(q).
+    __device__ static int tr_row(int q) { return q >> 2; }
+    __device__ static int tr_col(int q) { return 4 * (q & 3); }
+    __device__ static Frag tr(const unsigned char *p, int four_rows) {
+        const uint32_t la = lds_addr(p);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)la);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)(la + four_rows));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+        return Frag{u32x4{a.x, a.y, b.x, b.y}};
     }
-    // Same, but the fragment's 16 columns are the paired-state rows
-    // {8m + j : m, j = 0..3} (+ the tile's immediate offset): source lane q
-    // supplies the 4 columns at 8 (q%4), so result lane q gets column 8 (q/4) + q%4.
-    __device__ static uint32_t tr_addr_pairs(const unsigned char *t, int pitch, int kb, int q) {
-        return lds_addr(t + (kb + (q >> 2)) * pitch + 8 * (q & 3) * 2);
-    }
-    template <int F0, int F1, int R4>   // R4 = 4 * pitch (second read of a fragment)
-    __device__ static void tr2(uint32_t addr, Frag &a, Frag &b) {
-        u32x2 r0, r1, r2, r3;
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"
-            "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
-            "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
-            "ds_read_b64_tr_b16 %3, %4 offset:%8\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-            : "v"(addr), "i"(F0), "i"(F0 + R4), "i"(F1), "i"(F1 + R4));
-        a = Frag{u32x4{r0.x, r0.y, r1.x, r1.y}};
-        b = Frag{u32x4{r2.x, r2.y, r3.x, r3.y}};
-    }
-    template <int F0, int F1, int F2, int F3, int R4>
-    __device__ static void tr4(uint32_t addr, Frag &a, Frag &b, Frag &c, Frag &d) {
-        u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
-            "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
-            "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
-            "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
-            "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
-            "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
-            "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
-            "ds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-            : "v"(addr), "i"(F0), "i"(F0 + R4), "i"(F1), "i"(F1 + R4), "i"(F2), "i"(F2 + R4), "i"(F3),
-              "i"(F3 + R4));
-        a = Frag{u32x4{r0.x, r0.y, r1.x, r1.y}};
-        b = Frag{u32x4{r2.x, r2.y, r3.x, r3.y}};
-        c = Frag{u32x4{r4.x, r4.y, r5.x, r5.y}};
-        d = Frag{u32x4{r6.x, r6.y, r7.x, r7.y}};
-    }
-    __device__ static void load4(const unsigned char *t, int pitch, int row, int e, float (&v)[4]) {
-        u32x2 w = *reinterpret_cast<const u32x2 *>(t + lds_off<uint16_t>(row, e, pitch));
-        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-    }
-    // decay matrix (padded row-major, not swizzled)
-    __device__ static Frag mrow(const uint16_t *m, int pitch, int row, int k) {
-        return Frag{*reinterpret_cast<const u32x4 *>(m + row * pitch + k)};
-    }
-    __device__ static void mstore4(uint16_t *m, int pitch, int row, int col, const float (&v)[4]) {
-        *reinterpret_cast<u32x2 *>(m + row * pitch + col) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+    // decay-matrix row fragment: slots s <- m[k + s] (p points at it)
+    __device__ static Frag mrow(const unsigned char *p) { return Frag{*reinterpret_cast<const u32x4 *>(p)}; }
+    __device__ static void mstore4(unsigned char *p, const float (&v)[4]) {
+        *reinterpret_cast<u32x2 *>(p) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     }
     __device__ static Frag from_f32(const f32x4 &lo, const f32x4 &hi) {
         return Frag{u32x4{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
                           pack_bf16(hi[2], hi[3])}};
     }
-    __device__ static Frag low_half(const Frag &f) { return Frag{u32x4{f.w[0], f.w[1], 0u, 0u}}; }
     __device__ static Frag scale(const Frag &f, const float (&w)[8]) {
         Frag r;
 #pragma unroll
@@ -215,7 +210,7 @@ template <> struct Ops<uint16_t> {
         return r;
     }
     // 4 output values (consecutive headdim columns) -> y
-    __device__ static void store_y(__amdgpu_buffer_rsrc_t r, int off, const float (&v)[4]) {
+    __device__ static void store_y(__amdgpu_buffer_rsrc_t r, int off, const f32x4 &v) {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, r, off, 0, 0);
     }
 };
@@ -223,77 +218,50 @@ template <> struct Ops<uint16_t> {
 // float32
 template <> struct Ops<float> {
     struct Frag { float v[8]; };
-    static constexpr int kPad = 4;
+    static constexpr int kPad = 8;       // 288-byte rows
+    static constexpr int kHiOff = 64;
 
     __device__ static f32x4 mma(f32x4 acc, const Frag &a, const Frag &b) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
         return acc;
     }
-    __device__ static Frag rowk(const unsigned char *t, int pitch, int row, int k) {
-        f32x4 a = *reinterpret_cast<const f32x4 *>(t + lds_off<float>(row, k, pitch));
-        f32x4 b = *reinterpret_cast<const f32x4 *>(t + lds_off<float>(row, k + 4, pitch));
+    __device__ static Frag rowk_perm(const unsigned char *p) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(p + kHiOff);
         return Frag{{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}};
     }
-    __device__ static Frag rowk_perm(const unsigned char *t, int pitch, int row, int k0, int g) {
-        f32x4 a = *reinterpret_cast<const f32x4 *>(t + lds_off<float>(row, k0 + 4 * g, pitch));
-        f32x4 b = *reinterpret_cast<const f32x4 *>(t + lds_off<float>(row, k0 + 16 + 4 * g, pitch));
-        return Frag{{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}};
-    }
-    __device__ static uint32_t tr_addr(const unsigned char *t, int pitch, int kb, int col0, int q) {
-        return lds_addr(t + kb * pitch + (col0 + q) * 4);
-    }
-    __device__ static uint32_t tr_addr_pairs(const unsigned char *t, int pitch, int kb, int q) {
-        return lds_addr(t + kb * pitch + (8 * (q >> 2) + (q & 3)) * 4);
-    }
-    __device__ static Frag tr_one(uint32_t addr, int pitch) {
-        const unsigned char *p = lds_ptr(addr);
+    // column reads: slot s <- tile[kb + s][col0 + q] (rows four_rows / 4 bytes apart)
+    __device__ static int tr_row(int) { return 0; }
+    __device__ static int tr_col(int q) { return q; }
+    __device__ static Frag tr(const unsigned char *p, int four_rows) {
         Frag f;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) f.v[s] = *reinterpret_cast<const float *>(p + s * pitch);
+        for (int s = 0; s < 8; ++s) f.v[s] = *reinterpret_cast<const float *>(p + s * (four_rows / 4));
         return f;
     }
-    template <int F0, int F1, int R4>
-    __device__ static void tr2(uint32_t addr, Frag &a, Frag &b) {
-        a = tr_one(addr + F0, R4 / 4);
-        b = tr_one(addr + F1, R4 / 4);
-    }
-    template <int F0, int F1, int F2, int F3, int R4>
-    __device__ static void tr4(uint32_t addr, Frag &a, Frag &b, Frag &c, Frag &d) {
-        a = tr_one(addr + F0, R4 / 4);
-        b = tr_one(addr + F1, R4 / 4);
-        c = tr_one(addr + F2, R4 / 4);
-        d = tr_one(addr + F3, R4 / 4);
-    }
-    __device__ static void load4(const unsigned char *t, int pitch, int row, int e, float (&v)[4]) {
-        f32x4 w = *reinterpret_cast<const f32x4 *>(t + lds_off<float>(row, e, pitch));
-        v[0] = w[0]; v[1] = w[1]; v[2] = w[2]; v[3] = w[3];
-    }
-    __device__ static Frag mrow(const float *m, int pitch, int row, int k) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(m + row * pitch + k);
-        f32x4 a = p[0], b = p[1];
+    __device__ static Frag mrow(const unsigned char *p) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 16);
         return Frag{{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}};
     }
-    __device__ static void mstore4(float *m, int pitch, int row, int col, const float (&v)[4]) {
-        *reinterpret_cast<f32x4 *>(m + row * pitch + col) = f32x4{v[0], v[1], v[2], v[3]};
+    __device__ static void mstore4(unsigned char *p, const float (&v)[4]) {
+        *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
     }
     __device__ static Frag from_f32(const f32x4 &lo, const f32x4 &hi) {
         return Frag{{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}};
     }
-    __device__ static Frag low_half(const Frag &f) { return Frag{{f.v[0], f.v[1], f.v[2], f.v[3], 0, 0, 0, 0}}; }
     __device__ static Frag scale(const Frag &f, const float (&w)[8]) {
         Frag r;
 #pragma unroll
         for (int s = 0; s < 8; ++s) r.v[s] = f.v[s] * w[s];
         return r;
     }
-    __device__ static void store_y(__amdgpu_buffer_rsrc_t r, int off, const float (&v)[4]) {
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                                     __float_as_uint(v[2]), __float_as_uint(v[3])},
-                                               r, off, 0, 0);
+    __device__ static void store_y(__amdgpu_buffer_rsrc_t r, int off, const f32x4 &v) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
     }
 };
 
+// Tile shapes and the LDS plan of one (dtype, waves, dstate) instance.
 template <typename T, int NW, int N>
 struct ScanShape {
     static constexpr int kThreads = 64 * NW;
@@ -303,22 +271,28 @@ struct ScanShape {
     static constexpr int kRG = N * kES;              // bytes per B/C row in global memory
     static constexpr int kRB = kNE * kES;            // data bytes per B/C tile row in LDS
     static constexpr int kRX = kCols * kES;          // data bytes per x tile row
-    static constexpr int kPB = kRB + 16;             // padded LDS row pitch (B/C)
-    static constexpr int kPX = kRX + 16;             // padded LDS row pitch (x)
-    static constexpr int kTileB = kTile * kPB;       // a multiple of 1 KB
+    static constexpr int kPC = kRB + 16;             // C row pitch
+    static constexpr int kPB = kRB + 32;             // B row pitch within a group of 8 rows
+    static constexpr int kGB = 8 * kPB + 128;        // B bytes per group of 8 rows
+    static constexpr int kPX = kRX + 16;             // x row pitch
+    static constexpr int kTileC = kTile * kPC;       // all multiples of 1 KB
+    static constexpr int kTileB = 8 * kGB;
     static constexpr int kTileX = kTile * kPX;
-    static constexpr int kIB = (kTileB / 1024 + NW - 1) / NW;   // 1 KB load instructions per wave (B, and C)
+    static constexpr int kIC = (kTileC / 1024 + NW - 1) / NW;   // 1 KB direct loads per wave (C)
+    static constexpr int kIB = (kTileB / 1024 + NW - 1) / NW;   // (B)
     static constexpr int kIX = (kTileX / 1024 + NW - 1) / NW;   // (x)
-    static constexpr int kID = (4 + NW - 1) / NW;               // (dt: 4 x 64 floats)
-    static constexpr int kLoads = 2 * kIB + kIX + kID;          // vector memory loads per wave per step
+    static constexpr int kLoads = kIC + kIB + kIX + 1;          // + one dt load: vector memory loads per wave per step
     static constexpr int kNT = kNE / 16;                        // 16-row state tiles (even)
     static constexpr int kYStores = 4;                          // y stores per wave per step
     static constexpr int kNK = kNE / 32;                        // 32-deep steps over dstate
     static constexpr int kMP = kTile + Ops<T>::kPad;            // decay matrix pitch (elements)
-    // LDS: NST stages of [B | C | x | dt(256 f32)] + decay matrix + 2 scan tables + 1 KB sink
-    static constexpr int kStage = 2 * kTileB + kTileX + 1024;
-    static constexpr int kFixed = kTile * kMP * kES + 2 * 4 * kMaxChunk * 4 + 1024;
-    static constexpr int fit(int n) { return n * kStage + kFixed <= kLdsLimit; }
+    static constexpr int kMPB = kMP * kES;
+    // scan tables of one tile: S, E, Dl, W, V, Bf (64 floats each) and P (16)
+    static constexpr int kTab = 6 * 64 + 16;
+    static constexpr int kStage = kTileC + kTileB + kTileX + 256;
+    static constexpr int kSink = 2048 + 1024;
+    static constexpr int bytes(int n) { return n * (kStage + kTab * 4) + kTile * kMPB + kSink; }
+    static constexpr bool fit(int n) { return bytes(n) <= kLdsLimit; }
     // vector memory instructions a wave issued after the loads of the stage it
     // waits for: the later stages' loads, and the stores of the steps since
     // (4 y stores each, plus kNT state stores per step that exported a checkpoint)
@@ -329,8 +303,9 @@ struct ScanShape {
         return (fit(3) && vm_wait(3, 2) <= 63) ? 3 : ((fit(2) && vm_wait(2, 1) <= 63) ? 2 : 1);
     }
     static constexpr int kNST = pick();
-    static constexpr int kLdsBytes = kNST * kStage + kFixed;
     static_assert(fit(1), "tile does not fit in LDS");
+    // byte offset of row r in a B tile
+    __device__ static int brow(int r) { return (r >> 3) * kGB + (r & 7) * kPB; }
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then row
@@ -348,6 +323,9 @@ __device__ __forceinline__ float wave_scan(float v) {
     v += dpp_mov<0x143, 0xc>(v);   // row_bcast:31 -> rows 2, 3
     return v;
 }
+__device__ __forceinline__ float readlane(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 
 // softplus(u) = max(u, 0) + ln(1 + e^-|u|), on the hardware exp2/log2
 __device__ __forceinline__ float softplus_hw(float u) {
@@ -355,56 +333,35 @@ __device__ __forceinline__ float softplus_hw(float u) {
     return fmaxf(u, 0.0f) + __builtin_amdgcn_logf(1.0f + z) * 0.6931471805599453f;
 }
 
-// Per-chunk scan tables (log2-unit cumsum, delta, 2^s_i, w_j), one wave.
-// raw(j) returns dt of token j (j < Lc).
-template <typename RawDt>
-__device__ __forceinline__ void chunk_scan(float *tab, int Lc, float bias, float a2, int lane, RawDt raw) {
-    float *sS = tab, *sD = tab + kMaxChunk, *sE = tab + 2 * kMaxChunk, *sW = tab + 3 * kMaxChunk;
-    float v_keep[kMaxChunk / 64], d_keep[kMaxChunk / 64];
-    float carry = 0.0f;
-#pragma unroll
-    for (int piece = 0; piece < kMaxChunk / 64; ++piece) {
-        const int j = piece * 64 + lane;
-        float d = 0.0f, v = 0.0f;
-        if (piece * 64 < Lc) {
-            if (j < Lc) {
-                d = softplus_hw(raw(j) + bias);
-                v = d * a2;
-            }
-            v = wave_scan(v) + carry;
-            carry = __shfl(v, 63, 64);
-        }
-        v_keep[piece] = v;
-        d_keep[piece] = d;
-    }
-    const float sL = carry;   // cumsum at the chunk's last valid token (invalid tokens add 0)
-#pragma unroll
-    for (int piece = 0; piece < kMaxChunk / 64; ++piece) {
-        if (piece * 64 < Lc) {
-            const int j = piece * 64 + lane;
-            const float v = v_keep[piece], d = d_keep[piece];
-            sS[j] = v;
-            sD[j] = d;
-            sE[j] = fast_exp2(v);
-            sW[j] = j < Lc ? d * fast_exp2(sL - v) : 0.0f;
-        }
-    }
-}
-
-// Transposed reads of the NT state-tile fragments of B^T (rows n of the paired
-// state layout) sharing one base address (tr_addr_pairs): tile t = 2c + u
-// starts at column 32 c + 4 u.
-template <typename O, int NT, int ES, int R4, int T0 = 0>
-__device__ __forceinline__ void tr_tiles(uint32_t addr, typename O::Frag (&f)[NT]) {
-    constexpr auto off = [](int t) { return (32 * (t >> 1) + 4 * (t & 1)) * ES; };
-    if constexpr (T0 + 4 <= NT) {
-        O::template tr4<off(T0), off(T0 + 1), off(T0 + 2), off(T0 + 3), R4>(addr, f[T0], f[T0 + 1], f[T0 + 2],
-                                                                            f[T0 + 3]);
-        tr_tiles<O, NT, ES, R4, T0 + 4>(addr, f);
-    } else if constexpr (T0 + 2 <= NT) {
-        O::template tr2<off(T0), off(T0 + 1), R4>(addr, f[T0], f[T0 + 1]);
-        tr_tiles<O, NT, ES, R4, T0 + 2>(addr, f);
-    }
+// Scan tables of one tile from delta (lane j = token j; delta = 0 past the tile
+// end): S = s_j, E = 2^(s_j), Dl = delta_j, W = delta_j 2^(s_last - s_j),
+// V = 2^(s_j - s_end(block(j) - 1)), Bf = delta_j 2^(s_end(block(j)) - s_j)
+// (64 floats each, block = 16 tokens, s_end(-1) = 0), and
+// P[4 J + d] = 2^(s_end(J + d - 1) - s_end(J)) for 1 <= d and J + d < 4, 0 for
+// J + d >= 4 (16 floats). Every wave computes the scan (a short latency
+// chain); wave w stores the entries of its share of the lanes and the other
+// lanes store into `sink` (2 KB of scratch LDS).
+template <int NW>
+__device__ __forceinline__ void tile_tables(float *tab, float *sink, float d, float a2, int lane, int wave) {
+    const float v = wave_scan(d * a2);
+    const float e0 = readlane(v, 15), e1 = readlane(v, 31), e2 = readlane(v, 47), e3 = readlane(v, 63);
+    const int blk = lane >> 4;
+    const float s_prev = blk == 0 ? 0.0f : (blk == 1 ? e0 : (blk == 2 ? e1 : e2));
+    const float s_end = blk == 0 ? e0 : (blk == 1 ? e1 : (blk == 2 ? e2 : e3));
+    const bool owner = ((lane * NW) >> 6) == wave;
+    float *p = owner ? tab + lane : sink + lane;
+    p[0] = v;
+    p[64] = fast_exp2(v);
+    p[128] = d;
+    p[192] = d * fast_exp2(e3 - v);
+    p[256] = fast_exp2(v - s_prev);
+    p[320] = d * fast_exp2(s_end - v);
+    // P, by lanes 4 J + d < 16 of wave 0
+    const int J = (lane >> 2) & 3, dd = lane & 3, I = J + dd;
+    const float ea = I == 1 ? e0 : (I == 2 ? e1 : e2), eb = J == 0 ? e0 : (J == 1 ? e1 : e2);
+    const float pv = dd == 0 ? 1.0f : (I >= 4 ? 0.0f : fast_exp2(ea - eb));
+    float *pp = (wave == 0 && lane < 16) ? tab + 384 + lane : sink + 384 + lane;
+    *pp = pv;
 }
 
 // One workgroup per CU (the stage buffers take most of the LDS), i.e. one wave
@@ -421,14 +378,21 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     using O = Ops<T>;
     using Frag = typename O::Frag;
     using SH = ScanShape<T, NW, N>;
-    constexpr int NST = SH::kNST, RG = SH::kRG, RX = SH::kRX, PB = SH::kPB, PX = SH::kPX;
-    constexpr int MP = SH::kMP, ES = SH::kES, NT = SH::kNT, NK = SH::kNK;
-    constexpr int JS = (4 + NW - 1) / NW;   // decay-matrix column blocks per wave
+    constexpr int NST = SH::kNST, RG = SH::kRG, RX = SH::kRX, PC = SH::kPC, PB = SH::kPB, PX = SH::kPX;
+    constexpr int ES = SH::kES, NT = SH::kNT, NK = SH::kNK, MPB = SH::kMPB, TAB = SH::kTab;
+    constexpr int JS = 4 / NW;   // decay-matrix column blocks per wave
+    static_assert(NW == 1 || NW == 2 || NW == 4, "1, 2 or 4 waves per workgroup");
 
-    extern __shared__ __align__(16) unsigned char smem[];
-    T *sM = reinterpret_cast<T *>(smem + NST * SH::kStage);                              // [kTile][MP]
-    float *tabs = reinterpret_cast<float *>(smem + NST * SH::kStage + kTile * MP * ES);  // 2 x [4][kMaxChunk]
-    unsigned char *sink = smem + NST * SH::kStage + kTile * MP * ES + 2 * 4 * kMaxChunk * 4;
+    // Separate LDS objects, so the compiler knows that decay-matrix and table
+    // stores never alias tile reads and may reorder them freely.
+    __shared__ __align__(16) unsigned char sC[NST * SH::kTileC];
+    __shared__ __align__(16) unsigned char sB[NST * SH::kTileB];
+    __shared__ __align__(16) unsigned char sX[NST * SH::kTileX];
+    __shared__ __align__(16) float sDt[NST * 64];
+    __shared__ __align__(16) unsigned char sM[kTile * MPB];
+    __shared__ __align__(16) float tabs[NST * TAB + 512];   // + 2 KB of discarded table stores
+    __shared__ __align__(16) float sink_dma[256];          // discarded direct loads (1 KB)
+    float *const sink = tabs + NST * TAB;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (kept in an SGPR)
@@ -447,7 +411,8 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     tb = tb < 0 ? 0 : (tb > a.T ? a.T : tb);
     te = te < tb ? tb : (te > a.T ? a.T : te);
     const int L = (int)(te - tb);
-    const int nch = (L + cs - 1) / cs;
+    const int TT = cs < kTile ? cs : kTile;   // tokens per tile
+    const int nt = (L + TT - 1) / TT;         // tiles of this sequence
     const int c0 = a.seq_chunk_start[s];
     const int p0 = pt * SH::kCols;       // first headdim column of the workgroup
     const int pw = p0 + 16 * wave;       // first headdim column of this wave
@@ -458,116 +423,110 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     const T *Bg = reinterpret_cast<const T *>(a.B);
     const T *Cg = reinterpret_cast<const T *>(a.C);
     T *yg = reinterpret_cast<T *>(a.y);
-    const int scan_wave = NW - 1;
     const int xrow = H * P * ES;    // bytes between tokens of x / y
-    const int brow = G * N * ES;    // bytes between tokens of B / C
+    const int browg = G * N * ES;   // bytes between tokens of B / C
 
-    auto chunk_len = [&](int k) { return min(cs, L - k * cs); };
-    auto ntiles = [&](int k) { return (chunk_len(k) + kTile - 1) / kTile; };
-    // step order: chunk k, M-tile m, K-tile kt = 0..m
-    auto advance = [&](int &k, int &m, int &kt) {
-        if (++kt > m) { kt = 0; if (++m >= ntiles(k)) { m = 0; ++k; } }
+    auto tile_len = [&](int t) { return min(TT, L - t * TT); };
+    // the state after tile t is exported when the tile ends a chunk: its slot, else -1
+    auto slot_of = [&](int t) -> int {
+        if (a.chunk_states == nullptr || t >= nt) return -1;
+        if (((t + 1) * TT) % cs != 0 && t != nt - 1) return -1;
+        const int gc = c0 + (t * TT) / cs;
+        return (gc >= 0 && gc < a.max_chunks) ? (dstmap ? dstmap[gc] : gc) : -1;
     };
 
-    // Carried state, in pairs of 16-row tiles: st[2c+u][r] = h[p = pw + q][n = 32 c + 8 g + 4 u + r],
-    // i.e. lane group g holds the 8 consecutive n that the 32-deep operand slots of
-    // group g cover, so the state feeds C . h^T with the same C fragments as C . B^T.
+    // Carried state, in the accumulator layout of B^T . (w o x): st[t][r] = h[p = pw + q][n = 16 t + 4 g + r].
+    // The pair st[2c], st[2c+1] is the 32-deep operand of step c of C . h^T in the
+    // permuted k order (slots 0..3: n = 32 c + 4 g + r, slots 4..7: n = 32 c + 16 + 4 g + r),
+    // so C is read in that order, and C . B^T shares those C fragments.
     // Rows n >= N (dstate < 32 only) stay zero.
     f32x4 st[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) st[t] = f32x4{0, 0, 0, 0};
-    auto state_n = [&](int t) { return 32 * (t >> 1) + 8 * g + 4 * (t & 1); };
+    for (int u = 0; u < NT; ++u) st[u] = f32x4{0, 0, 0, 0};
+    auto state_n = [&](int u) { return 16 * u + 4 * g; };
     if (a.init != nullptr && (a.has_init == nullptr || a.has_init[s] != 0)) {
         const float *src = a.init + ((int64_t)(s * H + h) * P + pw + q) * N;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            if (state_n(t) < N) st[t] = *reinterpret_cast<const f32x4 *>(src + state_n(t));
+        for (int u = 0; u < NT; ++u)
+            if (state_n(u) < N) st[u] = *reinterpret_cast<const f32x4 *>(src + state_n(u));
     }
 
-    // scan tables of chunk 0, from global dt
-    if (nch > 0 && wave == scan_wave) {
-        const float *dt0 = a.dt + tb * H + h;
-        chunk_scan(tabs, chunk_len(0), bias, a2, lane, [&](int j) { return dt0[(int64_t)j * H]; });
+    // scan tables of tile 0, from global dt
+    if (nt > 0) {
+        float d = 0.0f;
+        if (lane < tile_len(0)) d = softplus_hw(a.dt[(tb + lane) * H + h] + bias);
+        tile_tables<NW>(tabs, sink, d, a2, lane, wave);
     }
     __builtin_amdgcn_s_waitcnt(WaitVm<0>::imm);   // nothing outstanding before the tile pipeline starts
 
     // Per-lane parts of the direct-to-LDS loads (loop invariant). Lane l of load
-    // block j fills LDS bytes [1024 j + 16 l, +16) of a tile: row r = that / pitch;
-    // bytes of the row padding get an out-of-range offset (zero fill).
-    struct GlobalOffsets { int b[SH::kIB], x[SH::kIX], d[SH::kID]; } go;
+    // block j fills LDS bytes [1024 j + 16 l, +16) of a tile; bytes of row
+    // padding (and past dstate in global memory) get an out-of-range offset.
+    struct GlobalOffsets { int c[SH::kIC], b[SH::kIB], x[SH::kIX]; int d; } go;
+#pragma unroll
+    for (int i = 0; i < SH::kIC; ++i) {
+        const int j = wave + NW * i, o = 1024 * j + 16 * lane, r = o / PC, pos = o % PC;
+        go.c[i] = (j < SH::kTileC / 1024 && pos < RG) ? r * browg + pos : kOob;
+    }
 #pragma unroll
     for (int i = 0; i < SH::kIB; ++i) {
-        const int j = wave + NW * i, o = 1024 * j + 16 * lane, r = o / PB, pos = o % PB;
-        go.b[i] = (j < SH::kTileB / 1024 && pos < RG) ? r * brow + pos : kOob;
+        const int j = wave + NW * i, o = 1024 * j + 16 * lane;
+        const int gr = o / SH::kGB, rm = o % SH::kGB, rin = rm / PB, pos = rm % PB;
+        go.b[i] = (j < SH::kTileB / 1024 && rin < 8 && pos < RG) ? (8 * gr + rin) * browg + pos : kOob;
     }
 #pragma unroll
     for (int i = 0; i < SH::kIX; ++i) {
         const int j = wave + NW * i, o = 1024 * j + 16 * lane, r = o / PX, pos = o % PX;
         go.x[i] = (j < SH::kTileX / 1024 && pos < RX) ? r * xrow + pos : kOob;
     }
-#pragma unroll
-    for (int i = 0; i < SH::kID; ++i) {
-        const int j = wave + NW * i;
-        go.d[i] = j < 4 ? (64 * j + lane) * H * 4 : kOob;
-    }
+    go.d = wave == 0 ? lane * H * 4 : kOob;
+    // LDS byte addresses (integers: no generic pointers in the address arithmetic)
+    const uint32_t lds_sink = lds_addr(sink_dma), lds_c = lds_addr(sC), lds_b = lds_addr(sB),
+                   lds_x = lds_addr(sX), lds_dt = lds_addr(sDt);
+    auto lds_u = [&](uint32_t a) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)a); };
 
-    // Fetch the tiles of step (k, m, kt) into stage buffer `slot` (out-of-range,
-    // zero-filling loads when k >= nch), in two parts issued at different points
-    // of a step. Always 2*kIB + kIX + kID instructions per wave.
-    auto fetch_bc = [&](int slot, int k, int m, int kt) {
-        unsigned char *stg = smem + slot * SH::kStage;
-        const bool live = k < nch;
-        const int Lc = live ? chunk_len(k) : 0;
-        const int64_t t0 = tb + (int64_t)k * cs;
-        const int vk = live ? min(kTile, Lc - kTile * kt) : 0;
-        const int vm = live ? min(kTile, Lc - kTile * m) : 0;
-        const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Bg + ((t0 + kTile * kt) * G + grp) * N), 0, vk * brow, kBufFlags);
-        const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Cg + ((t0 + kTile * m) * G + grp) * N), 0, vm * brow, kBufFlags);
+    // Fetch the tiles of tile u into stage buffer SLOT (out-of-range,
+    // zero-filling loads when u >= nt): part 0 loads C and B, part 1 x and the
+    // dt of tile u + 1; always kLoads instructions per wave in all. The parts
+    // are issued at different points of a step, so that the waves of a
+    // workgroup do not all queue their loads at the same moment.
+    auto fetch = [&](auto part, auto slot_c, int u) {
+        constexpr int PART = decltype(part)::value, SLOT = decltype(slot_c)::value;
+        const bool live = u < nt;
+        const int Lt = live ? tile_len(u) : 0;
+        const int64_t t0 = tb + (int64_t)u * TT;
+        if constexpr (PART == 0) {
+            const u32x4 rC = dma_rsrc(Cg + (t0 * G + grp) * N, Lt * browg);
+            const u32x4 rB = dma_rsrc(Bg + (t0 * G + grp) * N, Lt * browg);
 #pragma unroll
-        for (int i = 0; i < SH::kIB; ++i) {
-            const int j = wave + NW * i;   // 1 KB block of the tile
-            const bool ok = j < SH::kTileB / 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(ok ? stg + 1024 * j : sink), 16, go.b[i], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rC, (lds_void *)(ok ? stg + SH::kTileB + 1024 * j : sink), 16,
-                                                     go.b[i], 0, 0, 0);
+            for (int i = 0; i < SH::kIC; ++i) {
+                const int j = wave + NW * i;   // 1 KB block of the tile
+                dma16(rC, lds_u(j < SH::kTileC / 1024 ? lds_c + SLOT * SH::kTileC + 1024 * j : lds_sink), go.c[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < SH::kIB; ++i) {
+                const int j = wave + NW * i;
+                dma16(rB, lds_u(j < SH::kTileB / 1024 ? lds_b + SLOT * SH::kTileB + 1024 * j : lds_sink), go.b[i]);
+            }
+        } else {
+            const u32x4 rX = dma_rsrc(xg + (t0 * H + h) * P + p0, Lt * xrow);
+            const bool dnext = live && u + 1 < nt;
+            const u32x4 rD = dma_rsrc(a.dt + (dnext ? t0 + TT : 0) * H + h, dnext ? tile_len(u + 1) * H * 4 : 0);
+#pragma unroll
+            for (int i = 0; i < SH::kIX; ++i) {
+                const int j = wave + NW * i;
+                dma16(rX, lds_u(j < SH::kTileX / 1024 ? lds_x + SLOT * SH::kTileX + 1024 * j : lds_sink), go.x[i]);
+            }
+            dma4(rD, lds_u(wave == 0 ? lds_dt + SLOT * 256 : lds_sink), go.d);
         }
     };
-    auto fetch_xd = [&](int slot, int k, int m, int kt) {
-        unsigned char *stg = smem + slot * SH::kStage;
-        const bool live = k < nch;
-        const int Lc = live ? chunk_len(k) : 0;
-        const int64_t t0 = tb + (int64_t)k * cs;
-        const int vk = live ? min(kTile, Lc - kTile * kt) : 0;
-        const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(xg + ((t0 + kTile * kt) * H + h) * P + p0), 0, vk * xrow, kBufFlags);
-        // dt of chunk k+1 rides with the first step of chunk k
-        const bool dnext = live && m == 0 && kt == 0 && k + 1 < nch;
-        const int64_t t1 = tb + (int64_t)(k + 1) * cs;
-        const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.dt + (dnext ? t1 : 0) * H + h), 0, dnext ? chunk_len(k + 1) * H * 4 : 0, kBufFlags);
-#pragma unroll
-        for (int i = 0; i < SH::kIX; ++i) {
-            const int j = wave + NW * i;
-            const bool ok = j < SH::kTileX / 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (lds_void *)(ok ? stg + 2 * SH::kTileB + 1024 * j : sink), 16,
-                                                     go.x[i], 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < SH::kID; ++i) {
-            const int j = wave + NW * i;   // 64-token block of dt
-            const bool ok = j < 4;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rD, (lds_void *)(ok ? stg + 2 * SH::kTileB + SH::kTileX + 256 * j : sink), 4, go.d[i], 0, 0, 0);
-        }
-    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
     // y stores of a step that writes no y (keeps the per-step count fixed)
     const __amdgpu_buffer_rsrc_t r_none = __builtin_amdgcn_make_buffer_rsrc((void *)yg, 0, 0, kBufFlags);
     auto dummy_y_stores = [&]() {
-        const float z[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < SH::kYStores; ++i) O::store_y(r_none, 0, z);
+        for (int i = 0; i < SH::kYStores; ++i) O::store_y(r_none, 0, f32x4{0, 0, 0, 0});
     };
     auto wait_stage = [&](int exports) {   // exports among the last NST-1 steps
         if constexpr (NST == 3) {
@@ -580,218 +539,238 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         }
     };
 
-    // prologue: stages of steps 0 .. NST-2
-    int fk = 0, fm = 0, fkt = 0;   // fetch cursor
+    // prologue: stages of tiles 0 .. NST-2
     if constexpr (NST > 1) {
-#pragma unroll
-        for (int p = 0; p < NST - 1; ++p) {
-            fetch_bc(p, fk, fm, fkt);
-            fetch_xd(p, fk, fm, fkt);
-            if (fk < nch) advance(fk, fm, fkt);
-            dummy_y_stores();
-        }
+        fetch(P0{}, std::integral_constant<int, 0>{}, 0);
+        fetch(P1{}, std::integral_constant<int, 0>{}, 0);
+        dummy_y_stores();
+    }
+    if constexpr (NST > 2) {
+        fetch(P0{}, std::integral_constant<int, 1>{}, 1);
+        fetch(P1{}, std::integral_constant<int, 1>{}, 1);
+        dummy_y_stores();
     }
 
-    f32x4 acc[4];  // Y^T tile: acc[it][r] = y[i = 16 it + q][p = pw + 4 g + r]
-    int k = 0, m = 0, kt = 0;
+    // Row blocks of the Y^T tiles in visiting order: acc[d] covers tile rows
+    // 16 ib[d] + q. The decay-matrix sub-tile of column block jb = wave + NW jj at
+    // offset dd below the diagonal has row block (jb + dd) mod 4 = ib[(NW jj + dd) mod 4].
+    int ib[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) ib[d] = (wave + d) & 3;
+    // diagonal sub-tiles: the causal mask as an exponent bias, and D on the diagonal
+    float cm[4], dadd[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        cm[r] = 4 * g + r <= q ? 0.0f : -INFINITY;
+        dadd[r] = 4 * g + r == q ? Dh : 0.0f;
+    }
+
+    f32x4 acc[4];   // Y^T tiles: acc[d][r] = y[token 16 ib[d] + q][p = pw + 4 g + r]
     int ex1 = 0, ex2 = 0;   // did the previous / second previous step export a state
-    for (int step = 0; k < nch; ++step) {
-        const int slot = step % NST;
-        const unsigned char *stg = smem + slot * SH::kStage;
-        const unsigned char *sB = stg, *sC = stg + SH::kTileB, *sX = stg + 2 * SH::kTileB;
-        const float *sDt = reinterpret_cast<const float *>(stg + 2 * SH::kTileB + SH::kTileX);
-        const float *tab = tabs + (k & 1) * 4 * kMaxChunk;
-        const float *sS = tab, *sD = tab + kMaxChunk, *sE = tab + 2 * kMaxChunk, *sW = tab + 3 * kMaxChunk;
-        const int64_t t0 = tb + (int64_t)k * cs;
-        const int Lc = chunk_len(k);
-        const int ntile = (Lc + kTile - 1) / kTile;
-        const bool last_m = (m == ntile - 1);
+    int dst = slot_of(0);   // checkpoint slot of the state after the current tile, or -1
+    int t = 0;              // current tile
+
+    // One step: tile t in stage SLOT (= t mod NST).
+    auto step = [&](auto slot_c) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        constexpr int NEXT = (SLOT + 1) % NST, FETCH = (SLOT + NST - 1) % NST;
+        const unsigned char *tC = sC + SLOT * SH::kTileC;
+        const unsigned char *tB = sB + SLOT * SH::kTileB;
+        const unsigned char *tX = sX + SLOT * SH::kTileX;
+        const float *tab = tabs + SLOT * TAB;
+        const float *tS = tab, *tE = tab + 64, *tD = tab + 128, *tW = tab + 192, *tV = tab + 256, *tBf = tab + 320,
+                    *tP = tab + 384;
+        const int Lt = tile_len(t);
+        const int64_t t0 = tb + (int64_t)t * TT;
 
         if constexpr (NST == 1) {
-            fetch_bc(0, k, m, kt);
-            fetch_xd(0, k, m, kt);
+            fetch(P0{}, slot_c, t);
+            fetch(P1{}, slot_c, t);
             __builtin_amdgcn_s_waitcnt(WaitVm<0>::imm);
         } else {
             wait_stage(NST == 3 ? ex1 + ex2 : ex1);
         }
-        lds_barrier();   // stage `slot` and this chunk's scan tables are visible
-        // checkpoint slot of this chunk (scalar load, consumed at the chunk's end)
-        int dst = -1;
-        if (a.chunk_states != nullptr && last_m && kt == m) {
-            const int gc = c0 + k;
-            if (gc >= 0 && gc < a.max_chunks) dst = dstmap ? dstmap[gc] : gc;
-        }
-        if (m == 0 && kt == 0 && k + 1 < nch && wave == scan_wave) {
-            // scan tables of the next chunk, from the dt that rode with this stage
-            chunk_scan(tabs + ((k + 1) & 1) * 4 * kMaxChunk, chunk_len(k + 1), bias, a2, lane,
-                       [&](int j) { return sDt[j]; });
-        }
-        const float sL = sS[Lc - 1];   // chunk total decay, at its last valid token
+        lds_barrier();   // (A) stage SLOT and this tile's scan tables are visible
 
-        // C fragments of M-tile m (rows i; 32-deep slots n = 32 c + 8 g + s), shared by
-        // the inter-chunk product and C . B^T, and B fragments of this wave's
-        // column blocks jsub = wave + NW*jj
-        Frag cfm[4][NK], bf[JS][NK];
-        float ei[4], si[4], sj[JS][4], dj[JS][4];
+        // ---- phase A: the LDS operands of the step, then the matrix work
+        const float sL = tS[63];   // total log-decay of the tile (s is constant past its end)
+        // C fragments of the row blocks (32-deep k steps over n in the permuted
+        // order of the state), shared by the inter-chunk product and C . B^T
+        Frag cfm[4][NK];
+        float ei[4], vi[4];
 #pragma unroll
-        for (int isub = 0; isub < 4; ++isub) {
+        for (int d = 0; d < 4; ++d) {
+            const int il = 16 * ib[d] + q;
+            const unsigned char *pc = tC + il * PC + 4 * g * ES;
 #pragma unroll
-            for (int c = 0; c < NK; ++c) cfm[isub][c] = O::rowk(sC, PB, 16 * isub + q, 32 * c + 8 * g);
-            si[isub] = sS[kTile * m + 16 * isub + q];
-            ei[isub] = sE[kTile * m + 16 * isub + q];
+            for (int c = 0; c < NK; ++c) cfm[d][c] = O::rowk_perm(pc + 32 * c * ES);
+            ei[d] = tE[il];
+            vi[d] = tV[il];
         }
+        // B fragments and column factors of this wave's column blocks
+        Frag bf[JS][NK];
+        float si0[JS], sj[JS][4], dj[JS][4], bj[JS][4], pf[JS][4];
 #pragma unroll
         for (int jj = 0; jj < JS; ++jj) {
-            const int jsub = (wave + NW * jj) & 3;
+            const int jb = wave + NW * jj;
+            const unsigned char *pb = tB + SH::brow(16 * jb + q) + 4 * g * ES;
 #pragma unroll
-            for (int c = 0; c < NK; ++c) bf[jj][c] = O::rowk(sB, PB, 16 * jsub + q, 32 * c + 8 * g);
+            for (int c = 0; c < NK; ++c) bf[jj][c] = O::rowk_perm(pb + 32 * c * ES);
+            si0[jj] = tS[16 * jb + q];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int jc = kTile * kt + 16 * jsub + 4 * g + r;
-                sj[jj][r] = sS[jc];
-                dj[jj][r] = sD[jc];
+                const int jc = 16 * jb + 4 * g + r;
+                sj[jj][r] = tS[jc];
+                dj[jj][r] = tD[jc];
+                bj[jj][r] = tBf[jc];
+                pf[jj][r] = tP[4 * jb + r];
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-
-        if (kt == 0) {
-            // (6) inter-chunk term Y^T = h_in . C^T, then scale column i by 2^(s_i)
+        // x^T fragments (tokens 32 ks + 8 g + slot) of this wave's 16 columns, shared by
+        // the state update and the intra term, and B^T fragments (tile u: state rows n = 16 u ..)
+        Frag xf[2], bt[2][NT];
+        float w[2][8];
 #pragma unroll
-            for (int it = 0; it < 4; ++it) acc[it] = f32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < 2; ++ks) {
+            xf[ks] = O::tr(tX + (32 * ks + 8 * g + O::tr_row(q)) * PX + (16 * wave + O::tr_col(q)) * ES, 4 * PX);
+            const unsigned char *pb = tB + SH::brow(32 * ks + 8 * g) + O::tr_row(q) * PB + O::tr_col(q) * ES;
 #pragma unroll
-            for (int c = 0; c < NK; ++c) {
-                const Frag hf = O::from_f32(st[2 * c], st[2 * c + 1]);
+            for (int u = 0; u < NT; ++u) bt[ks][u] = O::tr(pb + 16 * u * ES, 4 * PB);
 #pragma unroll
-                for (int it = 0; it < 4; ++it) acc[it] = O::mma(acc[it], hf, cfm[it][c]);
-            }
-#pragma unroll
-            for (int it = 0; it < 4; ++it) acc[it] *= ei[it];
-            if (last_m) {
-                // (4) the entering state decays over the whole chunk
-                const float e = fast_exp2(sL);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) st[t] *= e;
-            }
+            for (int sl = 0; sl < 8; ++sl) w[ks][sl] = tW[32 * ks + 8 * g + sl];
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (NST > 1) fetch_bc((step + NST - 1) % NST, fk, fm, fkt);   // overlaps the matrix ops
 
-        // (5) CB^T sub-tiles of (M-tile m, K-tile kt) -> masked decay matrix in LDS;
-        // sub-tiles above the diagonal come out as zeros through the mask
+        // B and C of tile t + NST - 1, into the stage the previous step used
+        // (issued after this phase's LDS reads)
+        if constexpr (NST > 1) fetch(P0{}, std::integral_constant<int, FETCH>{}, t + NST - 1);
+
+        // (6) inter-chunk term Y^T = h_in . C^T, then scale column i by 2^(s_i)
 #pragma unroll
-        for (int jj = 0; jj < JS; ++jj) {
-            const int jsub = (wave + NW * jj) & 3;
-            if (wave + NW * jj < 4) {
+        for (int d = 0; d < 4; ++d) acc[d] = f32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int isub = 0; isub < 4; ++isub) {
-                    f32x4 cb = {0, 0, 0, 0};
+        for (int c = 0; c < NK; ++c) {
+            const Frag hf = O::from_f32(st[2 * c], st[2 * c + 1]);
 #pragma unroll
-                    for (int c = 0; c < NK; ++c) cb = O::mma(cb, bf[jj][c], cfm[isub][c]);
-                    const int il = 16 * isub + q, ic = kTile * m + il;
-                    float v[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int jc = kTile * kt + 16 * jsub + 4 * g + r;
-                        const float dec = fast_exp2(si[isub] - sj[jj][r]) * dj[jj][r];
-                        v[r] = (jc <= ic && ic < Lc) ? cb[r] * dec : 0.0f;
-                    }
-                    O::mstore4(sM, MP, il, 16 * jsub + 4 * g, v);
-                }
-            }
+            for (int d = 0; d < 4; ++d) acc[d] = O::mma(acc[d], hf, cfm[d][c]);
         }
-        lds_barrier();   // decay matrix complete
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc[d] *= ei[d];
 
-        // x^T fragments (tokens 32 ks + 8 g + slot) of this wave's 16 columns,
-        // decay-matrix fragments, x for the D term, and w_j
-        Frag xf[2], mf[4][2];
-        float xv[4][4], w[2][8];
-        O::template tr2<0, 32 * PX, 4 * PX>(O::tr_addr(sX, PX, 8 * g, 16 * wave, q), xf[0], xf[1]);
+        // (3, 4) state: h = 2^(s_last) h + B^T . (w o x)
+        {
+            const float e = fast_exp2(sL);
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) mf[it][ks] = O::mrow(sM, MP, 16 * it + q, 32 * ks + 8 * g);
-#pragma unroll
-        for (int it = 0; it < 4; ++it) O::load4(sX, PX, 16 * it + q, 16 * wave + 4 * g, xv[it]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int sl = 0; sl < 8; ++sl) w[ks][sl] = sW[kTile * kt + 32 * ks + 8 * g + sl];
-
-        // (6) intra-chunk term Y^T += x^T . M^T (zeros above the diagonal)
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) acc[it] = O::mma(acc[it], xf[ks], mf[it][ks]);
-
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (NST > 1) {
-            fetch_xd((step + NST - 1) % NST, fk, fm, fkt);
-            if (fk < nch) advance(fk, fm, fkt);
-        }
-        if (last_m) {
-            // (3) chunk state h += B^T . (w o x)
+            for (int u = 0; u < NT; ++u) st[u] *= e;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                Frag bt[NT];
-                tr_tiles<O, NT, ES, 4 * PB>(O::tr_addr_pairs(sB, PB, 32 * ks + 8 * g, q), bt);
                 const Frag xw = O::scale(xf[ks], w[ks]);
 #pragma unroll
-                for (int t = 0; t < NT; ++t) st[t] = O::mma(st[t], bt[t], xw);
+                for (int u = 0; u < NT; ++u) st[u] = O::mma(st[u], bt[ks][u], xw);
             }
         }
 
-        // stores: y of M-tile m (written on diagonal steps; 4 instructions every
-        // step), then the state after the chunk's last token into its slot
-        {
-            const bool ystore = (kt == m);
-            const int vm = min(kTile, Lc - kTile * m);
-            const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(yg + ((t0 + kTile * m) * H + h) * P + p0), 0, ystore ? vm * xrow : 0, kBufFlags);
+        // (5) decay-matrix sub-tiles (row block ib[dr], column block jb) -> LDS
 #pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                float yv[4];
+        for (int jj = 0; jj < JS; ++jj) {
+            const int jb = wave + NW * jj;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) yv[r] = acc[it][r] + Dh * xv[it][r];
-                O::store_y(ry, (16 * it + q) * xrow + (16 * wave + 4 * g) * ES, yv);
+            for (int dd = 0; dd < 4; ++dd) {
+                const int dr = (NW * jj + dd) & 3;   // visiting index of row block (jb + dd) mod 4
+                f32x4 cb = {0, 0, 0, 0};
+#pragma unroll
+                for (int c = 0; c < NK; ++c) cb = O::mma(cb, bf[jj][c], cfm[dr][c]);
+                float v[4];
+                if (dd == 0) {   // diagonal: exact factor, masked, plus D
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = fmaf(cb[r], fast_exp2(cm[r] + (si0[jj] - sj[jj][r])) * dj[jj][r], dadd[r]);
+                } else {         // below the diagonal (P = 0 for blocks above it)
+                    const float rowf = vi[dr] * pf[jj][dd];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = cb[r] * (rowf * bj[jj][r]);
+                }
+                O::mstore4(sM + (16 * ib[dr] + q) * MPB + (16 * jb + 4 * g) * ES, v);
             }
+        }
+
+        // scan tables of the next tile, from the dt that rode with this stage
+        {
+            const bool nxt = t + 1 < nt;
+            const int Ln = nxt ? tile_len(t + 1) : 0;
+            const float dn = softplus_hw(sDt[SLOT * 64 + lane] + bias + (lane < Ln ? 0.0f : -INFINITY));
+            tile_tables<NW>(nxt ? tabs + NEXT * TAB : sink, sink, dn, a2, lane, wave);
+        }
+        lds_barrier();   // (B) decay matrix and next tables complete
+
+        // ---- phase B: (6) intra-chunk and D terms Y^T += x^T . M^T
+        Frag mf[4][2];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) mf[d][ks] = O::mrow(sM + (16 * ib[d] + q) * MPB + (32 * ks + 8 * g) * ES);
+        if constexpr (NST > 1)   // x and dt of tile t + NST - 1
+            fetch(P1{}, std::integral_constant<int, FETCH>{}, t + NST - 1);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc[d] = O::mma(acc[d], xf[ks], mf[d][ks]);
+
+        // stores: y of the tile (4 instructions), then the state after the tile
+        // into its checkpoint slot if the tile ends a chunk
+        {
+            const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(yg + (t0 * H + h) * P + p0), 0, Lt * xrow, kBufFlags);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) O::store_y(ry, (16 * ib[d] + q) * xrow + (16 * wave + 4 * g) * ES, acc[d]);
             const bool bad_slot = dst >= a.capacity;
             if (bad_slot && tid == 0) atomicOr(a.error_flag, SSD_DATA_BAD_SLOT);
-            dst = __builtin_amdgcn_readfirstlane(bad_slot ? -1 : dst);
+            const int dsl = __builtin_amdgcn_readfirstlane(bad_slot ? -1 : dst);
             ex2 = ex1;
-            ex1 = dst >= 0;
-            if (dst >= 0) {
-                float *cbase = a.chunk_states + ((int64_t)dst * H + h) * P * N + (int64_t)p0 * N;
+            ex1 = dsl >= 0;
+            if (dsl >= 0) {
+                float *cbase = a.chunk_states + ((int64_t)dsl * H + h) * P * N + (int64_t)p0 * N;
                 const __amdgpu_buffer_rsrc_t re =
                     __builtin_amdgcn_make_buffer_rsrc((void *)cbase, 0, SH::kCols * N * 4, kBufFlags);
                 const int eoff = (16 * wave + q) * N * 4;
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st[t]), re,
-                                                           state_n(t) < N ? eoff + 4 * state_n(t) : kOob, 0, 0);
+                for (int u = 0; u < NT; ++u)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st[u]), re,
+                                                           state_n(u) < N ? eoff + 4 * state_n(u) : kOob, 0, 0);
             }
         }
         if constexpr (NST == 1) lds_barrier();   // the single stage is refilled next step
-        advance(k, m, kt);
+        ++t;
+        // slot of the next tile's state (loaded now, so that no scalar load is in
+        // flight while the next step reads LDS)
+        dst = slot_of(t);
+    };
+
+    while (t < nt) {
+        step(std::integral_constant<int, 0>{});
+        if constexpr (NST > 1) {
+            if (t >= nt) break;
+            step(std::integral_constant<int, 1>{});
+        }
+        if constexpr (NST > 2) {
+            if (t >= nt) break;
+            step(std::integral_constant<int, 2>{});
+        }
     }
 
     float *fd = a.final_states + ((int64_t)(s * H + h) * P + pw + q) * N;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-        if (state_n(t) < N) *reinterpret_cast<f32x4 *>(fd + state_n(t)) = st[t];
+    for (int u = 0; u < NT; ++u)
+        if (state_n(u) < N) *reinterpret_cast<f32x4 *>(fd + state_n(u)) = st[u];
 }
 #endif
 
 template <typename T, int NW, int N>
 hipError_t launch_scan_instance(const ScanArgs &a, hipStream_t stream) {
     using SH = ScanShape<T, NW, N>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&ssd_scan_kernel<T, NW, N>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, SH::kLdsBytes);
-    if (attr != hipSuccess) return attr;
     const int64_t blocks = (int64_t)a.S * a.H * a.nptiles;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((ssd_scan_kernel<T, NW, N>), dim3((unsigned)blocks), dim3(SH::kThreads),
-                       SH::kLdsBytes, stream, a, a.chunk_state_dst);
+    hipLaunchKernelGGL((ssd_scan_kernel<T, NW, N>), dim3((unsigned)blocks), dim3(SH::kThreads), 0, stream, a,
+                       a.chunk_state_dst);
     return hipGetLastError();
 }
 
