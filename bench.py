@@ -35,6 +35,38 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
+def ingest_counters(fetch_csv, write_csv, config, calib_mib, out=COUNTERS):
+    """Turn two rocprofv3 --pmc runs of `bench.py --copy-calib-mib M` (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch) into the HBM traffic of one scan launch,
+    each counter scaled by what it reads for the calibration kernel (one
+    elementwise pass that reads and writes M MiB)."""
+    import csv
+
+    def per_kernel(path):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    scan_f = [v for k, v in fetch.items() if "ssd_scan_kernel" in k][0]
+    scan_w = [v for k, v in write.items() if "ssd_scan_kernel" in k][0]
+    calib_kib = calib_mib * 1024.0
+    # calibration dispatch: the elementwise kernel with the largest reading (the add)
+    cal_f = max(x for k, v in fetch.items() if "elementwise" in k for x in v)
+    cal_w = max(x for k, v in write.items() if "elementwise" in k for x in v)
+    ff, fw = calib_kib / cal_f, calib_kib / cal_w
+    fk, wk = sum(scan_f) / len(scan_f), sum(scan_w) / len(scan_w)
+    rec = {"kernel": "ssd_scan_kernel", "kernel_hash": kernel_hash(), "config": config,
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": len(scan_f),
+           "calibration_mib": calib_mib, "calibration_fetch_kib": cal_f, "calibration_write_kib": cal_w,
+           "fetch_scale": ff, "write_scale": fw,
+           "hbm_bytes_per_launch": (fk * ff + wk * fw) * 1024.0}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def algorithmic_work(w, n_ckpt):
     """Bytes the method must move and flops it must do for one pass."""
     T, H, P, N, G = w.total_tokens, w.nheads, w.headdim, w.dstate, w.ngroups
@@ -78,10 +110,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic record from two rocprofv3 counter CSVs and exit "
+                         "(with --copy-calib-mib giving the calibration size)")
     args = ap.parse_args()
+    if args.ingest_counters:
+        print(json.dumps(ingest_counters(*args.ingest_counters, config=args.config,
+                                         calib_mib=args.copy_calib_mib or 512)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(see DESIGN.md for how the scan would shard)", file=sys.stderr)
@@ -138,11 +177,13 @@ def main():
     scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
 
     if args.copy_calib_mib:
+        # one plain elementwise kernel that reads and writes copy_calib_mib MiB each
+        # (the scale for the FETCH_SIZE / WRITE_SIZE counters)
         n = args.copy_calib_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dstb = torch.empty_like(src)
         torch.cuda.synchronize()
-        dstb.copy_(src)
+        torch.add(src, 1.0, out=dstb)
         torch.cuda.synchronize()
 
     n_ckpt = 0

@@ -22,8 +22,10 @@
  *     delta_t = softplus(dt[t,h] + dt_bias[h])
  *     h_t     = exp(delta_t * A[h]) * h_{t-1} + delta_t * x_t (outer) B_t[g]
  *     y_t     = h_t . C_t[g] + D[h] * x_t
- * starting from initial_states[s,h] (if flagged) or zero; evaluated chunk by
- * chunk (intra-chunk quadratic form + state passing between chunks).
+ * starting from initial_states[s,h] (if flagged) or zero; evaluated tile by
+ * tile of min(chunk_size, 64) tokens (intra-tile quadratic form + state passing
+ * between tiles, an exact re-association of the recurrence), with chunk_size
+ * fixing the chunk grid and the exported states.
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless marked [host]. Tensors are dense,

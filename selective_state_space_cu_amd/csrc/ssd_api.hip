@@ -94,6 +94,7 @@ ssd_status ssd_chunk_scan_varlen(const void *x, const float *dt, const float *dt
     // else 32 (2 waves) or 16 (1 wave)
     const int waves = headdim % 64 == 0 ? 4 : (headdim % 32 == 0 ? 2 : 1);
     a.nptiles = headdim / (16 * (waves < 4 ? waves : 4));
+    a.xcd_pairs = (meta->nseqs * ngroups) % 8 == 0;
     if (meta->nseqs == 0) return SSD_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = in_dtype == SSD_BF16 ? ssd::launch_scan_bf16(a, waves, dstate, s)

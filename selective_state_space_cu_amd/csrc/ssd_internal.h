@@ -30,6 +30,8 @@ struct ScanArgs {
     const int32_t *seq_order;
     int32_t *error_flag;
     int32_t T, S, H, P, G, cs, max_chunks, capacity, nptiles;
+    // 1: workgroups of one (sequence, group) run on one XCD (needs S*G % 8 == 0)
+    int32_t xcd_pairs;
 };
 
 // Launches the scan for one (dtype, waves-per-workgroup, dstate) instance.

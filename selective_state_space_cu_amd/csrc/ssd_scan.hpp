@@ -399,10 +399,29 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     const int q = lane & 15, g = lane >> 4;
 
     if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
-    const int per_seq = a.H * a.nptiles;
-    const int rank = blockIdx.x / per_seq;
-    const int rem = blockIdx.x - rank * per_seq;
-    const int h = rem / a.nptiles, pt = rem - h * a.nptiles;
+    // Workgroup -> (sequence rank, head, headdim tile). Workgroups are handed to
+    // the 8 XCDs round-robin (block b runs on XCD b mod 8), each with its own L2:
+    // with xcd_pairs, all workgroups of one (sequence, group) pair -- which read
+    // the same B and C tiles -- land on one XCD, pairs p = x, x + 8, ... on XCD x
+    // (longest sequences first on every XCD).
+    int rank, h, pt;
+    {
+        const int b = blockIdx.x, hpg = a.H / a.G;
+        if (a.xcd_pairs) {
+            const int wpp = hpg * a.nptiles;   // workgroups per pair
+            const int x = b & 7, i = b >> 3;
+            const int pair = x + 8 * (i / wpp), loc = i - (i / wpp) * wpp;
+            rank = pair / a.G;
+            h = (pair - rank * a.G) * hpg + loc / a.nptiles;
+            pt = loc - (loc / a.nptiles) * a.nptiles;
+        } else {
+            const int per_seq = a.H * a.nptiles;
+            rank = b / per_seq;
+            const int rem = b - rank * per_seq;
+            h = rem / a.nptiles;
+            pt = rem - h * a.nptiles;
+        }
+    }
     const int s = a.seq_order[rank];
     if (s < 0 || s >= a.S) return;
     const int grp = h / (a.H / a.G);
