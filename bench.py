@@ -24,7 +24,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "scan_prefix_cache_4x8894_counters.json")
-KERNEL_SOURCES = ["ssd_scan.hpp", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_internal.h"]
+KERNEL_SOURCES = ["ssd_scan.hpp", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_internal.h",
+                  "ssd_scan_split.hpp", "ssd_scan_split_bf16.hip"]
 
 
 def kernel_hash():
@@ -49,15 +50,15 @@ def ingest_counters(fetch_csv, write_csv, config, calib_mib, out=COUNTERS):
         return vals
 
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
-    scan_f = [v for k, v in fetch.items() if "ssd_scan_kernel" in k][0]
-    scan_w = [v for k, v in write.items() if "ssd_scan_kernel" in k][0]
+    scan_f = [v for k, v in fetch.items() if "ssd_scan" in k][0]
+    scan_w = [v for k, v in write.items() if "ssd_scan" in k][0]
     calib_kib = calib_mib * 1024.0
     # calibration dispatch: the elementwise kernel with the largest reading (the add)
     cal_f = max(x for k, v in fetch.items() if "elementwise" in k for x in v)
     cal_w = max(x for k, v in write.items() if "elementwise" in k for x in v)
     ff, fw = calib_kib / cal_f, calib_kib / cal_w
     fk, wk = sum(scan_f) / len(scan_f), sum(scan_w) / len(scan_w)
-    rec = {"kernel": "ssd_scan_kernel", "kernel_hash": kernel_hash(), "config": config,
+    rec = {"kernel": scan_kernel_name(config), "kernel_hash": kernel_hash(), "config": config,
            "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": len(scan_f),
            "calibration_mib": calib_mib, "calibration_fetch_kib": cal_f, "calibration_write_kib": cal_w,
            "fetch_scale": ff, "write_scale": fw,
@@ -65,6 +66,14 @@ def ingest_counters(fetch_csv, write_csv, config, calib_mib, out=COUNTERS):
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     return rec
+
+
+def scan_kernel_name(config):
+    """The scan kernel the library launches for a workload (see ssd_api.hip)."""
+    from selective_state_space_cu_amd.workloads import CONFIGS
+    c = CONFIGS[config]
+    split = c["dtype"] == "bf16" and c["dstate"] == 128 and c["headdim"] % 64 == 0
+    return "ssd_scan_split_kernel" if split else "ssd_scan_kernel"
 
 
 def algorithmic_work(w, n_ckpt):
@@ -216,7 +225,7 @@ def main():
                    "headdim": P, "dstate": N, "ngroups": w.ngroups, "chunk_size": w.chunk_size,
                    "block_size": w.block_size, "checkpoints_per_step": n_ckpt,
                    "step": "metadata + checkpoint plan + scan with at-source checkpoint export"},
-        "roofline": {"bound": "hbm", "kernel": "ssd_scan_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": scan_kernel_name(args.config), "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": alg_bytes,
                      "kernel_ms": scan_ms,

@@ -89,16 +89,18 @@ ssd_status ssd_chunk_scan_varlen(const void *x, const float *dt, const float *dt
     a.T = meta->total_tokens; a.S = meta->nseqs; a.H = nheads; a.P = headdim; a.G = ngroups;
     a.cs = meta->chunk_size; a.max_chunks = meta->max_chunks;
     a.capacity = chunk_states ? chunk_states_capacity : 0;
-    // headdim tile per workgroup: 64 columns when it divides headdim (8 waves,
-    // two per 16-column block, for bf16 up to dstate 128; else 4 waves),
+    // headdim tile per workgroup: 64 columns when it divides headdim (4 waves,
+    // or 8 with the state split between wave pairs for bf16 with dstate 128),
     // else 32 (2 waves) or 16 (1 wave)
     const int waves = headdim % 64 == 0 ? 4 : (headdim % 32 == 0 ? 2 : 1);
-    a.nptiles = headdim / (16 * (waves < 4 ? waves : 4));
+    const bool split = in_dtype == SSD_BF16 && dstate == 128 && headdim % 64 == 0;
+    a.nptiles = headdim / (16 * waves);
     a.xcd_pairs = (meta->nseqs * ngroups) % 8 == 0;
     if (meta->nseqs == 0) return SSD_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = in_dtype == SSD_BF16 ? ssd::launch_scan_bf16(a, waves, dstate, s)
-                                              : ssd::launch_scan_f32(a, waves, dstate, s);
+    const hipError_t e = split ? ssd::launch_scan_split_bf16(a, dstate, s)
+                         : in_dtype == SSD_BF16 ? ssd::launch_scan_bf16(a, waves, dstate, s)
+                                                : ssd::launch_scan_f32(a, waves, dstate, s);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

@@ -37,6 +37,8 @@ struct ScanArgs {
 // Launches the scan for one (dtype, waves-per-workgroup, dstate) instance.
 hipError_t launch_scan_bf16(const ScanArgs &a, int waves, int dstate, hipStream_t stream);
 hipError_t launch_scan_f32(const ScanArgs &a, int waves, int dstate, hipStream_t stream);
+// Split-state bf16 scan (eight waves per 64 headdim columns; dstate 128).
+hipError_t launch_scan_split_bf16(const ScanArgs &a, int dstate, hipStream_t stream);
 
 struct MetaArgs {
     const int32_t *cu_seqlens;

@@ -364,6 +364,29 @@ __device__ __forceinline__ void tile_tables(float *tab, float *sink, float d, fl
     *pp = pv;
 }
 
+// Workgroup -> (sequence rank, head, headdim tile). Workgroups are handed to
+// the 8 XCDs round-robin (block b runs on XCD b mod 8), each with its own L2:
+// with xcd_pairs, all workgroups of one (sequence, group) pair -- which read
+// the same B and C tiles -- land on one XCD, pairs p = x, x + 8, ... on XCD x
+// (longest sequences first on every XCD).
+__device__ __forceinline__ void decode_block(const ScanArgs &a, int b, int &rank, int &h, int &pt) {
+    const int hpg = a.H / a.G;
+    if (a.xcd_pairs) {
+        const int wpp = hpg * a.nptiles;   // workgroups per pair
+        const int x = b & 7, i = b >> 3;
+        const int pair = x + 8 * (i / wpp), loc = i - (i / wpp) * wpp;
+        rank = pair / a.G;
+        h = (pair - rank * a.G) * hpg + loc / a.nptiles;
+        pt = loc - (loc / a.nptiles) * a.nptiles;
+    } else {
+        const int per_seq = a.H * a.nptiles;
+        rank = b / per_seq;
+        const int rem = b - rank * per_seq;
+        h = rem / a.nptiles;
+        pt = rem - h * a.nptiles;
+    }
+}
+
 // One workgroup per CU (the stage buffers take most of the LDS), i.e. one wave
 // per SIMD: let the scheduler spend registers on hoisting LDS reads ahead of
 // the matrix ops instead of targeting an occupancy the LDS cannot give.
@@ -399,29 +422,8 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     const int q = lane & 15, g = lane >> 4;
 
     if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
-    // Workgroup -> (sequence rank, head, headdim tile). Workgroups are handed to
-    // the 8 XCDs round-robin (block b runs on XCD b mod 8), each with its own L2:
-    // with xcd_pairs, all workgroups of one (sequence, group) pair -- which read
-    // the same B and C tiles -- land on one XCD, pairs p = x, x + 8, ... on XCD x
-    // (longest sequences first on every XCD).
     int rank, h, pt;
-    {
-        const int b = blockIdx.x, hpg = a.H / a.G;
-        if (a.xcd_pairs) {
-            const int wpp = hpg * a.nptiles;   // workgroups per pair
-            const int x = b & 7, i = b >> 3;
-            const int pair = x + 8 * (i / wpp), loc = i - (i / wpp) * wpp;
-            rank = pair / a.G;
-            h = (pair - rank * a.G) * hpg + loc / a.nptiles;
-            pt = loc - (loc / a.nptiles) * a.nptiles;
-        } else {
-            const int per_seq = a.H * a.nptiles;
-            rank = b / per_seq;
-            const int rem = b - rank * per_seq;
-            h = rem / a.nptiles;
-            pt = rem - h * a.nptiles;
-        }
-    }
+    decode_block(a, blockIdx.x, rank, h, pt);
     const int s = a.seq_order[rank];
     if (s < 0 || s >= a.S) return;
     const int grp = h / (a.H / a.G);

@@ -1,0 +1,608 @@
+// Split-state variant of the fused tile-walk scan, for bf16 inputs with
+// dstate 128 (the Mamba2 layer shape): two waves per SIMD instead of one.
+//
+// One workgroup owns one (sequence, head, 64 headdim columns), like the
+// four-wave kernel in ssd_scan.hpp, but runs eight waves: wave w owns the 16
+// columns of block pb = w mod 4 and HALF nh = w / 4, meaning
+//   - state rows n in [nh N/2, (nh + 1) N/2) of those columns (float32, in
+//     registers, carried from tile to tile), and
+//   - output tokens 32 nh .. 32 nh + 31 of every tile (y rows, decay-matrix rows).
+// Waves w and w + 4 run on the same SIMD, so each SIMD interleaves two
+// instruction streams and hides the latency a single wave would stall on.
+//
+// The inter-chunk term of a wave's 32 tokens needs the whole entering state of
+// its 16 columns, so the two halves are swapped once per tile: after the state
+// update each wave converts its half to the bf16 operand fragments of the next
+// tile's inter-chunk product and stores them into the C-tile blocks of the
+// stage it has just consumed (those bytes are dead until the same reader
+// refills them with its own direct loads, after reading the fragments), and
+// its partner reads them after the next tile's first barrier.
+//
+// Per tile, wave (pb, nh), row blocks I = 2 nh + d (d = 0, 1), column block J = pb:
+//   Y^T[p, i]   = h_in[p, :] . C[i, :]^T                (all n: own + partner halves)
+//   CB[i, j]    = C[i, :] . B[j, :]^T -> decay matrix M[i, j] (sub-tiles (I, J))
+//   h_out[p, n] = 2^(s_last) h_in[p, n] + sum_j B[j, n] w_j x[j, p]  (own n half)
+//   Y^T[p, i]  += sum_j x[j, p] M[i, j]                 (after the second barrier)
+// with the scan tables (s, 2^s, delta, w) of the next tile computed by waves 0-3.
+// The tile pipeline (NST stages of direct-to-LDS loads, exact vmcnt waits) is
+// that of the four-wave kernel.
+//
+// LDS tiles are unpadded (a C or B tile is 16 KB, an x tile 8 KB, so each of
+// the eight waves fills whole 1 KB blocks of every tile) and conflict-free by
+// an XOR swizzle of 16-byte chunks: chunk k of row r is stored at chunk
+// k ^ swz(r). The direct loads apply it on the global side (each lane picks
+// the global chunk that belongs at its LDS position); the readers apply it
+// per lane. B and C rows (256 bytes) use swz(r) = r mod 16, x rows (128 bytes)
+// swz(r) = (b2, b1, b3) of r (bit 0 first).
+//
+// State layout: lane (g, q) holds h[p][n] for p = pw + q and the 16 n values
+// nb + 16 g .. nb + 16 g + 15 (register u, element r: n = nb + 16 g + 4 (u ^ (g & 1)) + r;
+// the u ^ (g & 1) order makes the transposed B reads conflict-free). So the
+// 32-deep k step c of every product over n takes, in lane group g, the 8
+// consecutive n = nb + 16 g + 8 c .. + 7: one 16-byte read per C or B row
+// fragment, and the state needs no data movement to become an operand.
+//
+// Stores leave the workgroup as whole 128-byte lines: each wave puts its y
+// values into an LDS tile of the workgroup's 64 tokens x 64 columns, which is
+// written out row by row after the next barrier (one step later); a
+// checkpoint is transposed through the just-consumed B tile, so that each
+// store covers 4 state rows x 256 bytes.
+#pragma once
+
+#include "ssd_scan.hpp"
+
+namespace ssd {
+
+// Direct-to-LDS loads with the LDS address as an SGPR base plus a compile-time
+// offset (m0 = base + OFF), so that per-stage addresses need no extra registers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int OFF>
+__device__ __forceinline__ void dma16_at(const u32x4 &r, uint32_t lds_base, int voff) {
+    asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF) : "memory", "m0", "scc");
+}
+template <int OFF>
+__device__ __forceinline__ void dma4_at(const u32x4 &r, uint32_t lds_base, int voff) {
+    asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF) : "memory", "m0", "scc");
+}
+#pragma clang diagnostic pop
+
+// Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// Row fragment: 8 consecutive bf16 (one 16-byte read); transposed fragment:
+// two ds_read_b64_tr_b16 from per-lane addresses.
+__device__ __forceinline__ Ops<uint16_t>::Frag rf16(uint32_t addr) {
+    return Ops<uint16_t>::Frag{*(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr};
+}
+__device__ __forceinline__ Ops<uint16_t>::Frag tr2(uint32_t lo_addr, uint32_t hi_addr) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)lo_addr);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)hi_addr);
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+    return Ops<uint16_t>::Frag{u32x4{a.x, a.y, b.x, b.y}};
+}
+// Orders LDS accesses across the lanes of one wave at the compiler level
+// (the hardware executes a wave's LDS instructions in order).
+__device__ __forceinline__ void wave_lds_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ u32x4 buf_rsrc(const void *base, int num_records) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(num_records), (uint32_t)kBufFlags};
+}
+
+template <int N>
+struct SplitShape {
+    static constexpr int kWaves = 8;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kCols = 64;                 // headdim columns per workgroup
+    static constexpr int kES = 2;                    // bf16
+    static constexpr int kRB = N * kES;              // bytes per B/C row (256)
+    static constexpr int kRX = kCols * kES;          // bytes per x / y tile row (128)
+    static constexpr int kTileC = kTile * kRB;       // 16 KB
+    static constexpr int kTileB = kTile * kRB;
+    static constexpr int kTileX = kTile * kRX;       // 8 KB
+    static constexpr int kIC = kTileC / 1024 / kWaves;   // 1 KB direct loads per wave (C)
+    static constexpr int kIB = kTileB / 1024 / kWaves;   // (B)
+    static constexpr int kIX = kTileX / 1024 / kWaves;   // (x)
+    static constexpr int kLoads = kIC + kIB + kIX + 1;   // + one dt load
+    static constexpr int kNKH = N / 64;              // 32-deep steps over one state half
+    static constexpr int kNTH = N / 32;              // state registers (f32x4) per lane
+    static constexpr int kMPB = (kTile + 16) * kES;  // decay matrix row pitch (160 bytes)
+    static constexpr int kTab = 4 * 64;              // S, E, Dl, W
+    static constexpr int kStage = kTileC + kTileB + kTileX + 256;
+    static constexpr int bytes(int n) { return n * (kStage + kTab * 4) + kTile * kMPB + kTileX; }
+    static constexpr bool fit(int n) { return bytes(n) <= kLdsLimit; }
+    // vector memory instructions issued after the last load of the stage
+    // waited for: one y store and the next stage's loads per step since, and
+    // kNTH stores per step that exported a checkpoint
+    static constexpr int vm_wait(int exports) { return 1 + kLoads + exports * kNTH; }
+    static constexpr int kNST = 3;
+    static_assert(fit(kNST), "three stages must fit in LDS");
+    static_assert(vm_wait(2) <= 63, "vmcnt range");
+    // the partner's state fragments use C blocks w + 8 c of a consumed stage
+    static_assert(8 * kNKH <= kTileC / 1024, "state exchange needs 8 C blocks per fragment");
+    // a checkpoint is staged in 2 KB per wave of a consumed B tile
+    static_assert(kWaves * 2048 <= kTileB, "checkpoint staging");
+    static_assert(N == 128, "the swizzles and layouts are laid out for 256-byte B/C rows");
+    __device__ static int swz128(int r) { return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
+};
+
+template <int N>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
+#if !defined(__HIP_DEVICE_COMPILE__)
+{   // the host pass only needs the signature (for the launch stub)
+}
+#else
+{
+    using O = Ops<uint16_t>;
+    using Frag = O::Frag;
+    using SH = SplitShape<N>;
+    constexpr int NST = SH::kNST, RB = SH::kRB, RX = SH::kRX;
+    constexpr int NTH = SH::kNTH, NKH = SH::kNKH, MPB = SH::kMPB, TAB = SH::kTab;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
+    __shared__ __align__(16) unsigned char sC[NST * SH::kTileC];
+    __shared__ __align__(16) unsigned char sB[NST * SH::kTileB];
+    __shared__ __align__(16) unsigned char sX[NST * SH::kTileX];
+    __shared__ __align__(16) float sDt[NST * 64];
+    __shared__ __align__(16) unsigned char sM[kTile * MPB];
+    __shared__ __align__(16) unsigned char sY[SH::kTileX];   // y of the previous tile
+    __shared__ __align__(16) float tabs[NST * TAB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (kept in an SGPR)
+    const int pb = wave & 3, nh = wave >> 2;                      // column block, half
+    const int q = lane & 15, g = lane >> 4;
+    const bool godd = (g & 1) != 0;
+
+    if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
+    int rank, h, pt;
+    decode_block(a, blockIdx.x, rank, h, pt);
+    const int s = a.seq_order[rank];
+    if (s < 0 || s >= a.S) return;
+    const int grp = h / (a.H / a.G);
+    const int H = a.H, P = a.P, G = a.G, cs = a.cs;
+    int64_t tb = a.cu_seqlens[s], te = a.cu_seqlens[s + 1];
+    tb = tb < 0 ? 0 : (tb > a.T ? a.T : tb);
+    te = te < tb ? tb : (te > a.T ? a.T : te);
+    const int L = (int)(te - tb);
+    const int TT = cs < kTile ? cs : kTile;   // tokens per tile
+    const int nt = (L + TT - 1) / TT;         // tiles of this sequence
+    // chunk_size and the tile are powers of two: a chunk is 2^lg_tpc tiles
+    const int lg_tpc = __builtin_ctz((unsigned)cs) - __builtin_ctz((unsigned)TT);
+    const int c0 = a.seq_chunk_start[s];
+    const int p0 = pt * SH::kCols;       // first headdim column of the workgroup
+    const int pw = p0 + 16 * pb;         // first headdim column of this wave
+    const int nb = nh * (N / 2);         // first state row of this wave's half
+    const int r0 = 32 * nh;              // first token row of this wave's half
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float a2 = a.A[h] * kLog2e;
+    const float Dh = a.D ? a.D[h] : 0.0f;
+    const int xrow = H * P * 2;     // bytes between tokens of x / y
+    const int browg = G * N * 2;    // bytes between tokens of B / C
+    const int clampTT = TT;
+    auto clamp_len = [&](int rem) { return rem < 0 ? 0 : (rem > clampTT ? clampTT : rem); };
+
+    // the state after tile t is exported when the tile ends a chunk: its slot, else -1
+    auto slot_of = [&](int t) -> int {
+        if (a.chunk_states == nullptr || t >= nt) return -1;
+        if (((t + 1) & ((1 << lg_tpc) - 1)) != 0 && t != nt - 1) return -1;
+        const int gc = c0 + (t >> lg_tpc);
+        return (gc >= 0 && gc < a.max_chunks) ? (dstmap ? dstmap[gc] : gc) : -1;
+    };
+    // n offset (elements) of register u's 4 values within the lane's 16
+    auto n_of = [&](int u) { return 16 * g + 4 * (u ^ (g & 1)); };
+
+    // This wave's half of the carried state (see the layout note above).
+    f32x4 st[NTH];
+#pragma unroll
+    for (int u = 0; u < NTH; ++u) st[u] = f32x4{0, 0, 0, 0};
+    if (a.init != nullptr && (a.has_init == nullptr || a.has_init[s] != 0)) {
+        const float *src = a.init + ((int64_t)(s * H + h) * P + pw + q) * N + nb;
+#pragma unroll
+        for (int u = 0; u < NTH; ++u) st[u] = *reinterpret_cast<const f32x4 *>(src + n_of(u));
+    }
+
+    // Scan tables of a tile from delta (lane j = token j; delta = 0 past the
+    // tile end), one table per wave of waves 0-3: S = s_j (inclusive cumulative
+    // log2-decay), E = 2^(s_j), Dl = delta_j, W = delta_j 2^(s_last - s_j).
+    auto tables = [&](float *tab, float d) {
+        const float v = wave_scan(d * a2);
+        const float e3 = readlane(v, 63);
+        const float ex = fast_exp2(wave == 1 ? v : e3 - v);
+        const float val = wave == 0 ? v : (wave == 1 ? ex : (wave == 2 ? d : d * ex));
+        tab[64 * wave + lane] = val;
+    };
+    if (nt > 0 && wave < 4) {
+        float d = 0.0f;
+        if (lane < clamp_len(L)) d = softplus_hw(a.dt[(tb + lane) * H + h] + bias);
+        tables(tabs, d);
+    }
+
+    // Exchange of state halves: the fragments this wave gives its partner
+    // (wave ^ 4) go to C blocks (wave ^ 4) + 8 c of a consumed stage, which the
+    // partner reads before it refills them. Fragment c, lane group g: the 8
+    // values n = nb + 16 g + 8 c .. + 7 (registers 2c, 2c+1 in g-dependent order).
+    Frag hown[NKH];
+    auto make_own = [&]() {
+#pragma unroll
+        for (int c = 0; c < NKH; ++c) {
+            const uint32_t a0 = pack_bf16(st[2 * c][0], st[2 * c][1]), a1 = pack_bf16(st[2 * c][2], st[2 * c][3]);
+            const uint32_t b0 = pack_bf16(st[2 * c + 1][0], st[2 * c + 1][1]),
+                           b1 = pack_bf16(st[2 * c + 1][2], st[2 * c + 1][3]);
+            hown[c].w = godd ? u32x4{b0, b1, a0, a1} : u32x4{a0, a1, b0, b1};
+        }
+    };
+    const uint32_t x_put = lds_addr(sC) + 1024 * (wave ^ 4) + 16 * lane;
+    const uint32_t x_get = lds_addr(sC) + 1024 * wave + 16 * lane;
+    auto put_own = [&](auto slot_c) {
+        constexpr int SLOT = decltype(slot_c)::value;
+#pragma unroll
+        for (int c = 0; c < NKH; ++c) *(lds_u32x4 *)(uintptr_t)(x_put + SLOT * SH::kTileC + 8192 * c) = hown[c].w;
+    };
+    make_own();
+    put_own(std::integral_constant<int, NST - 1>{});   // read by step 0 (from stage NST - 1)
+    __builtin_amdgcn_s_waitcnt(WaitVm<0>::imm);        // nothing outstanding before the tile pipeline starts
+
+    // Per-lane parts of the direct-to-LDS loads (loop invariant): lane l of
+    // load block j fills LDS bytes [1024 j + 16 l, +16) of a tile, i.e. chunk
+    // l mod 16 (l mod 8 for x) of row 4 j + l / 16 (8 j + l / 8), with the
+    // global chunk that the swizzle puts there.
+    int go_c[SH::kIC], go_b[SH::kIB], go_x[SH::kIX];
+#pragma unroll
+    for (int i = 0; i < SH::kIC; ++i) {
+        const int r = 4 * (wave + 8 * i) + (lane >> 4);
+        go_c[i] = r * browg + 16 * ((lane & 15) ^ (r & 15));
+    }
+#pragma unroll
+    for (int i = 0; i < SH::kIB; ++i) {
+        const int r = 4 * (wave + 8 * i) + (lane >> 4);
+        go_b[i] = r * browg + 16 * ((lane & 15) ^ (r & 15));
+    }
+#pragma unroll
+    for (int i = 0; i < SH::kIX; ++i) {
+        const int r = 8 * (wave + 8 * i) + (lane >> 3);
+        go_x[i] = r * xrow + 16 * ((lane & 7) ^ SH::swz128(r));
+    }
+    const int go_d = lane * H * 4;   // every wave loads the same dt (identical bytes)
+    // LDS byte addresses of this wave's first 1 KB block in each tile region
+    // (wave-uniform); block i of stage SLOT is at + SLOT * tile + 8 KB i
+    auto rfl = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); };
+    const uint32_t lds_c = rfl(lds_addr(sC) + 1024 * wave), lds_b = rfl(lds_addr(sB) + 1024 * wave),
+                   lds_x = rfl(lds_addr(sX) + 1024 * wave), lds_dt = rfl(lds_addr(sDt));
+
+    // Running global positions of the tile being fetched (tile f) and of the
+    // tile whose y is being stored (tile t - 1).
+    const char *f_c = reinterpret_cast<const char *>(a.C) + ((tb * G + grp) * N) * 2;
+    const char *f_b = reinterpret_cast<const char *>(a.B) + ((tb * G + grp) * N) * 2;
+    const char *f_x = reinterpret_cast<const char *>(a.x) + ((tb * H + h) * P + p0) * 2;
+    const char *f_d = reinterpret_cast<const char *>(a.dt) + ((tb + TT) * H + h) * 4;
+    int f_rem = L;                         // tokens from tile f on
+    const int64_t step_bc = (int64_t)TT * browg, step_x = (int64_t)TT * xrow, step_d = (int64_t)TT * H * 4;
+
+    // Fetch tile f into stage buffer SLOT (zero-filling loads past the
+    // sequence): part 0 loads C and B, part 1 x and the dt of tile f + 1
+    // (then advances f); always kLoads instructions per wave in all.
+    auto fetch = [&](auto part, auto slot_c) {
+        constexpr int PART = decltype(part)::value, SLOT = decltype(slot_c)::value;
+        const int Lt = clamp_len(f_rem);
+        if constexpr (PART == 0) {
+            const u32x4 rC = buf_rsrc(f_c, Lt * browg);
+            const u32x4 rB = buf_rsrc(f_b, Lt * browg);
+            static_for<SH::kIC>([&](auto i_c) {
+                constexpr int I = decltype(i_c)::value;
+                dma16_at<SLOT * SH::kTileC + 8192 * I>(rC, lds_c, go_c[I]);
+            });
+            static_for<SH::kIB>([&](auto i_c) {
+                constexpr int I = decltype(i_c)::value;
+                dma16_at<SLOT * SH::kTileB + 8192 * I>(rB, lds_b, go_b[I]);
+            });
+        } else {
+            const u32x4 rX = buf_rsrc(f_x, Lt * xrow);
+            const u32x4 rD = buf_rsrc(f_d, clamp_len(f_rem - TT) * H * 4);
+            static_for<SH::kIX>([&](auto i_c) {
+                constexpr int I = decltype(i_c)::value;
+                dma16_at<SLOT * SH::kTileX + 8192 * I>(rX, lds_x, go_x[I]);
+            });
+            dma4_at<SLOT * 256>(rD, lds_dt, go_d);
+            if (f_rem > 0) {   // advance to the next tile (past the end: stays, zero-sized)
+                f_c += step_bc; f_b += step_bc; f_x += step_x; f_d += step_d;
+            }
+            f_rem -= TT;
+        }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    auto wait_stage = [&](int exports) {   // checkpoint exports among the last two steps
+        if (exports == 0) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(0)>::imm);
+        else if (exports == 1) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(1)>::imm);
+        else __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(2)>::imm);
+    };
+
+    // y of the previous tile: LDS tile (row rho = token, 128 bytes, chunk k at
+    // k ^ ((rho >> 1) & 7)) -> y, one row per 8 lanes
+    char *y_prev = reinterpret_cast<char *>(a.y) + ((tb * H + h) * P + p0) * 2;   // tile t - 1
+    int y_len = 0;                                     // its tokens (0: nothing to store)
+    const int yrow = 8 * wave + (lane >> 3);
+    const uint32_t y_get = lds_addr(sY) + yrow * RX + 16 * ((lane & 7) ^ ((yrow >> 1) & 7));
+    const uint32_t y_put = lds_addr(sY) + (r0 + q) * RX + 16 * ((2 * pb + (g >> 1)) ^ (((r0 + q) >> 1) & 7)) + 8 * (g & 1);
+    auto store_prev_y = [&](const u32x4 &v) {
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(y_prev, 0, y_len * xrow, kBufFlags);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, yrow * xrow + 16 * (lane & 7), 0, 0);
+    };
+
+    // prologue: stages of tiles 0 .. NST-2 (and the y store slot of step -1)
+    fetch(P0{}, std::integral_constant<int, 0>{});
+    fetch(P1{}, std::integral_constant<int, 0>{});
+    store_prev_y(u32x4{0, 0, 0, 0});   // zero-sized: keeps the per-step count of vector memory ops
+    fetch(P0{}, std::integral_constant<int, 1>{});
+    fetch(P1{}, std::integral_constant<int, 1>{});
+
+    // Diagonal structure of this wave's decay-matrix sub-tiles (rows
+    // i = r0 + 16 d + q, columns j = 16 pb + 4 g + r): exponent bias 0 for
+    // j <= i, -inf above the diagonal; D where j == i.
+    float mbias[2][4], dadd[2][4];
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = r0 + 16 * d + q, j = 16 * pb + 4 * g + r;
+            mbias[d][r] = j <= i ? 0.0f : -INFINITY;
+            dadd[d][r] = j == i ? Dh : 0.0f;
+        }
+
+    // Per-lane LDS addresses of the swizzled fragment reads (stage 0; stages,
+    // row blocks and k-steps over tokens are immediate offsets).
+    //   C rows r0 + q and B rows 16 pb + q: 16 bytes at n = nb' + 16 g + 8 c
+    //   (nb' = this wave's or the partner's half)
+    const int nbp = N / 2 - nb;
+    uint32_t ac_o[NKH], ac_p[NKH], ab_o[NKH], ab_p[NKH];
+#pragma unroll
+    for (int c = 0; c < NKH; ++c) {
+        ac_o[c] = lds_addr(sC) + (r0 + q) * RB + 16 * ((nb / 8 + 2 * g + c) ^ q);
+        ac_p[c] = lds_addr(sC) + (r0 + q) * RB + 16 * ((nbp / 8 + 2 * g + c) ^ q);
+        ab_o[c] = lds_addr(sB) + (16 * pb + q) * RB + 16 * ((nb / 8 + 2 * g + c) ^ q);
+        ab_p[c] = lds_addr(sB) + (16 * pb + q) * RB + 16 * ((nbp / 8 + 2 * g + c) ^ q);
+    }
+    //   transposed reads of B^T for register u: lane q of each 16-lane group
+    //   supplies row kb + q / 4 (+ 4), the 4 values at n = nb + 16 (q mod 4) + 4 (u ^ (q mod 2));
+    //   of x^T: row kb + q / 4 (+ 4), columns 16 pb + 4 (q mod 4); kb = 32 ks + 8 g
+    uint32_t abt[NTH][2], axf[2];
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+        const int r = 8 * g + (q >> 2) + 4 * hi;
+#pragma unroll
+        for (int u = 0; u < NTH; ++u) {
+            const int byte = 2 * nb + 32 * (q & 3) + 8 * (u ^ (q & 1));
+            abt[u][hi] = lds_addr(sB) + r * RB + 16 * ((byte >> 4) ^ (r & 15)) + (byte & 15);
+        }
+        axf[hi] = lds_addr(sX) + r * RX + 16 * ((2 * pb + ((q >> 1) & 1)) ^ SH::swz128(r)) + 8 * (q & 1);
+    }
+    // checkpoint staging (2 KB of a consumed B tile per wave, 8 rows x 256
+    // bytes per round, chunk m of row i at m ^ i)
+    const uint32_t e_base = lds_addr(sB) + 2048 * wave;
+    const int e_row = lane >> 4;   // + 4 i: row within the round, read side
+
+    int nexp = 0;           // checkpoint exports among the last two steps
+    int ex1 = 0;            // did the previous step export
+    int dst = slot_of(0);   // checkpoint slot of the state after the current tile, or -1
+    int t = 0;              // current tile
+
+    // One step: tile t in stage SLOT (= t mod NST).
+    auto step = [&](auto slot_c) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        constexpr int NEXT = (SLOT + 1) % NST, FETCH = (SLOT + NST - 1) % NST;
+        constexpr int OC = SLOT * SH::kTileC, OB = SLOT * SH::kTileB, OX = SLOT * SH::kTileX;
+        const float *tab = tabs + SLOT * TAB;
+        const float *tS = tab, *tE = tab + 64, *tD = tab + 128, *tW = tab + 192;
+
+        wait_stage(nexp);
+        lds_barrier();   // (A) stage SLOT, this tile's tables, the partner's state half and y of tile t-1 are visible
+
+        // ---- phase A
+        const u32x4 yv = *(const lds_u32x4 *)(uintptr_t)y_get;   // y of tile t - 1
+        Frag hp[NKH];   // the partner's half of h_in, from the C blocks of stage FETCH
+#pragma unroll
+        for (int c = 0; c < NKH; ++c) hp[c].w = *(const lds_u32x4 *)(uintptr_t)(x_get + FETCH * SH::kTileC + 8192 * c);
+        const float sL = tS[63];   // total log-decay of the tile (s is constant past its end)
+        // C fragments of this wave's row blocks (own / partner n half) and B
+        // fragments of column block pb, shared by C . h^T and C . B^T
+        Frag co[2][NKH], cp[2][NKH], bo[NKH], bq[NKH];
+        float ei[2], si[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+#pragma unroll
+            for (int c = 0; c < NKH; ++c) {
+                co[d][c] = rf16(ac_o[c] + OC + 16 * RB * d);
+                cp[d][c] = rf16(ac_p[c] + OC + 16 * RB * d);
+            }
+            ei[d] = tE[r0 + 16 * d + q];
+            si[d] = tS[r0 + 16 * d + q];
+        }
+#pragma unroll
+        for (int c = 0; c < NKH; ++c) {
+            bo[c] = rf16(ab_o[c] + OB);
+            bq[c] = rf16(ab_p[c] + OB);
+        }
+        float sj[4], dj[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sj[r] = tS[16 * pb + 4 * g + r];
+            dj[r] = tD[16 * pb + 4 * g + r];
+        }
+
+        // (6) inter-chunk term Y^T = h_in . C^T over all n, then scale column i by 2^(s_i)
+        f32x4 acc[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            acc[d] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < NKH; ++c) {
+                acc[d] = O::mma(acc[d], hown[c], co[d][c]);
+                acc[d] = O::mma(acc[d], hp[c], cp[d][c]);
+            }
+            acc[d] *= ei[d];
+        }
+        store_prev_y(yv);
+
+        // (5) decay-matrix sub-tiles (row block 2 nh + d, column block pb) -> LDS
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            f32x4 cb = {0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < NKH; ++c) {
+                cb = O::mma(cb, bo[c], co[d][c]);
+                cb = O::mma(cb, bq[c], cp[d][c]);
+            }
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // 2^(s_i - s_j) <= 1 for j <= i; 2^(-inf) = 0 above the diagonal
+                const float f = fast_exp2(si[d] - sj[r] + mbias[d][r]) * dj[r];
+                v[r] = fmaf(cb[r], f, dadd[d][r]);
+            }
+            O::mstore4(sM + (r0 + 16 * d + q) * MPB + (16 * pb + 4 * g) * 2, v);
+        }
+
+        // B and C of tile t + NST - 1 into stage FETCH, once this wave's reads
+        // of its C blocks there (the partner's state half) have completed
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        fetch(P0{}, std::integral_constant<int, FETCH>{});
+
+        // (3, 4) this wave's state half: h = 2^(s_last) h + B^T . (w o x)
+        Frag xf[2];
+        {
+            Frag bt[2][NTH];
+            float w[2][8];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                xf[ks] = tr2(axf[0] + OX + 32 * RX * ks, axf[1] + OX + 32 * RX * ks);
+#pragma unroll
+                for (int u = 0; u < NTH; ++u) bt[ks][u] = tr2(abt[u][0] + OB + 32 * RB * ks, abt[u][1] + OB + 32 * RB * ks);
+#pragma unroll
+                for (int sl = 0; sl < 8; ++sl) w[ks][sl] = tW[32 * ks + 8 * g + sl];
+            }
+            const float e = fast_exp2(sL);
+#pragma unroll
+            for (int u = 0; u < NTH; ++u) st[u] *= e;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const Frag xw = O::scale(xf[ks], w[ks]);
+#pragma unroll
+                for (int u = 0; u < NTH; ++u) st[u] = O::mma(st[u], bt[ks][u], xw);
+            }
+        }
+
+        // scan tables of the next tile, from the dt that rode with this stage
+        if (wave < 4 && t + 1 < nt) {
+            const int Ln = clamp_len(L - (t + 1) * TT);
+            tables(tabs + NEXT * TAB, softplus_hw(sDt[SLOT * 64 + lane] + bias + (lane < Ln ? 0.0f : -INFINITY)));
+        }
+        lds_barrier();   // (B) decay matrix and next tables complete; stage SLOT's C and B tiles consumed
+
+        // ---- phase B
+        // this wave's half of h_out for the partner, into stage SLOT's C blocks
+        make_own();
+        put_own(slot_c);
+        // (6) intra-chunk and D terms Y^T += x^T . M^T
+        Frag mf[2][2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) mf[d][ks] = O::mrow(sM + (r0 + 16 * d + q) * MPB + (32 * ks + 8 * g) * 2);
+        fetch(P1{}, std::integral_constant<int, FETCH>{});   // x and dt of tile t + NST - 1
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc[d] = O::mma(acc[d], xf[ks], mf[d][ks]);
+        // y of this tile -> LDS (stored by the next step)
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+            *(lds_u32x2 *)(uintptr_t)(y_put + 16 * RX * d) =
+                u32x2{pack_bf16(acc[d][0], acc[d][1]), pack_bf16(acc[d][2], acc[d][3])};
+        if (t > 0) y_prev += step_x;
+        y_len = clamp_len(L - t * TT);
+
+        // the state half after the tile into its checkpoint slot, if the tile
+        // ends a chunk: two rounds of 8 state rows through 2 KB of stage
+        // SLOT's B tile, each store 4 rows x 256 bytes
+        const bool bad_slot = dst >= a.capacity;
+        if (bad_slot && tid == 0) atomicOr(a.error_flag, SSD_DATA_BAD_SLOT);
+        const int dsl = __builtin_amdgcn_readfirstlane(bad_slot ? -1 : dst);
+        const int ex = dsl >= 0 ? 1 : 0;
+        nexp = ex1 + ex;
+        ex1 = ex;
+        if (dsl >= 0) {
+            const char *cbase = reinterpret_cast<const char *>(a.chunk_states) +
+                                ((((int64_t)dsl * H + h) * P + p0) * N) * 4;
+            const __amdgpu_buffer_rsrc_t re =
+                __builtin_amdgcn_make_buffer_rsrc((void *)cbase, 0, SH::kCols * N * 4, kBufFlags);
+#pragma unroll
+            for (int rnd = 0; rnd < 2; ++rnd) {
+                if ((q >> 3) == rnd) {
+#pragma unroll
+                    for (int u = 0; u < NTH; ++u) {
+                        const int i = q & 7, m = n_of(u) / 4;
+                        *(lds_u32x4 *)(uintptr_t)(e_base + OB + 256 * i + 16 * (m ^ i)) = __builtin_bit_cast(u32x4, st[u]);
+                    }
+                }
+                // lanes read what other lanes wrote: LDS runs one wave's
+                // accesses in order, but the compiler must not reuse values
+                // read before the writes (the staging addresses repeat per round)
+                wave_lds_sync();
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int i = e_row + 4 * k;
+                    const u32x4 v = *(const lds_u32x4 *)(uintptr_t)(e_base + OB + 256 * i + 16 * ((lane & 15) ^ i));
+                    __builtin_amdgcn_raw_buffer_store_b128(v, re, ((16 * pb + 8 * rnd + i) * N + nb) * 4 + 16 * (lane & 15), 0, 0);
+                }
+                wave_lds_sync();
+            }
+        }
+        ++t;
+        dst = slot_of(t);
+    };
+
+    while (t < nt) {
+        step(std::integral_constant<int, 0>{});
+        if (t >= nt) break;
+        step(std::integral_constant<int, 1>{});
+        if (t >= nt) break;
+        step(std::integral_constant<int, 2>{});
+    }
+    if (nt > 0) {   // y of the last tile
+        lds_barrier();
+        store_prev_y(*(const lds_u32x4 *)(uintptr_t)y_get);
+    }
+
+    float *fd = a.final_states + ((int64_t)(s * H + h) * P + pw + q) * N + nb;
+#pragma unroll
+    for (int u = 0; u < NTH; ++u) *reinterpret_cast<f32x4 *>(fd + n_of(u)) = st[u];
+}
+#endif
+
+template <int N>
+hipError_t launch_scan_split_instance(const ScanArgs &a, hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.S * a.H * a.nptiles;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((ssd_scan_split_kernel<N>), dim3((unsigned)blocks), dim3(SplitShape<N>::kThreads), 0,
+                       stream, a, a.chunk_state_dst);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

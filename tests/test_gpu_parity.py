@@ -95,6 +95,10 @@ SHAPES = [
     # dtype, lengths, H, P, N, G, cs
     ("bf16", [300, 77, 1, 0, 513], 4, 64, 128, 2, 256),
     ("bf16", [200, 64, 65, 129], 4, 128, 128, 4, 64),
+    # split-state path (bf16, dstate 128, headdim % 64 == 0) at every tile size
+    ("bf16", [1, 15, 16, 17, 31, 33, 250], 3, 64, 128, 1, 16),
+    ("bf16", [190, 0, 64, 96], 2, 192, 128, 2, 32),
+    ("bf16", [700, 1000, 2], 2, 64, 128, 1, 128),
     ("bf16", [130, 5, 260], 2, 32, 64, 1, 128),
     ("bf16", [40, 3, 17], 2, 16, 16, 1, 16),
     ("bf16", [100, 33], 2, 48, 256, 2, 32),
