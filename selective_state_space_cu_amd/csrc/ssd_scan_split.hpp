@@ -96,11 +96,15 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
 }
-__device__ __forceinline__ u32x4 buf_rsrc(const void *base, int num_records) {
-    const uint64_t b = (uint64_t)(uintptr_t)base;
-    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
-                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu)),
-                 (uint32_t)__builtin_amdgcn_readfirstlane(num_records), (uint32_t)kBufFlags};
+// Wave-uniform 64-bit value (kept in an SGPR pair).
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+}
+// Raw buffer resource: base address, num_records bytes (accesses past it
+// read zero / are dropped), stride 0.
+__device__ __forceinline__ u32x4 buf_rsrc(uint64_t b, int num_records) {
+    return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, (uint32_t)num_records, (uint32_t)kBufFlags};
 }
 
 template <int N>
@@ -198,13 +202,11 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     const int clampTT = TT;
     auto clamp_len = [&](int rem) { return rem < 0 ? 0 : (rem > clampTT ? clampTT : rem); };
 
-    // the state after tile t is exported when the tile ends a chunk: its slot, else -1
-    auto slot_of = [&](int t) -> int {
-        if (a.chunk_states == nullptr || t >= nt) return -1;
-        if (((t + 1) & ((1 << lg_tpc) - 1)) != 0 && t != nt - 1) return -1;
-        const int gc = c0 + (t >> lg_tpc);
-        return (gc >= 0 && gc < a.max_chunks) ? (dstmap ? dstmap[gc] : gc) : -1;
-    };
+    // The state after tile t is exported when the tile ends a chunk (or is
+    // the sequence's last): ex_tile is the next such tile, ex_chunk its chunk.
+    const int tpc = 1 << lg_tpc;
+    int ex_tile = a.chunk_states != nullptr ? min(tpc, nt) - 1 : nt;
+    int ex_chunk = c0;
     // n offset (elements) of register u's 4 values within the lane's 16
     auto n_of = [&](int u) { return 16 * g + 4 * (u ^ (g & 1)); };
 
@@ -221,12 +223,14 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     // Scan tables of a tile from delta (lane j = token j; delta = 0 past the
     // tile end), one table per wave of waves 0-3: S = s_j (inclusive cumulative
     // log2-decay), E = 2^(s_j), Dl = delta_j, W = delta_j 2^(s_last - s_j).
+    // (wave-uniform float selectors instead of branches)
+    const float k_s = wave == 0 ? 1.0f : 0.0f, k_e = wave == 1 ? 1.0f : 0.0f, k_d = wave == 2 ? 1.0f : 0.0f,
+                k_w = wave == 3 ? 1.0f : 0.0f;
     auto tables = [&](float *tab, float d) {
         const float v = wave_scan(d * a2);
         const float e3 = readlane(v, 63);
-        const float ex = fast_exp2(wave == 1 ? v : e3 - v);
-        const float val = wave == 0 ? v : (wave == 1 ? ex : (wave == 2 ? d : d * ex));
-        tab[64 * wave + lane] = val;
+        const float ex = fast_exp2(k_e * v + (1.0f - k_e) * (e3 - v));   // 2^(s_j), or 2^(s_last - s_j)
+        tab[64 * wave + lane] = k_s * v + (k_e + k_w * d) * ex + k_d * d;
     };
     if (nt > 0 && wave < 4) {
         float d = 0.0f;
@@ -288,12 +292,21 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
     // Running global positions of the tile being fetched (tile f) and of the
     // tile whose y is being stored (tile t - 1).
-    const char *f_c = reinterpret_cast<const char *>(a.C) + ((tb * G + grp) * N) * 2;
-    const char *f_b = reinterpret_cast<const char *>(a.B) + ((tb * G + grp) * N) * 2;
-    const char *f_x = reinterpret_cast<const char *>(a.x) + ((tb * H + h) * P + p0) * 2;
-    const char *f_d = reinterpret_cast<const char *>(a.dt) + ((tb + TT) * H + h) * 4;
+    // (buffer resources kept as loop-carried SGPR quads: per tile, the base
+    // address advances and num_records is set to the tile's bytes)
+    u32x4 r_c = buf_rsrc(uni64((uint64_t)(uintptr_t)a.C + (uint64_t)((tb * G + grp) * N) * 2), 0);
+    u32x4 r_b = buf_rsrc(uni64((uint64_t)(uintptr_t)a.B + (uint64_t)((tb * G + grp) * N) * 2), 0);
+    u32x4 r_x = buf_rsrc(uni64((uint64_t)(uintptr_t)a.x + (uint64_t)((tb * H + h) * P + p0) * 2), 0);
+    u32x4 r_d = buf_rsrc(uni64((uint64_t)(uintptr_t)a.dt + (uint64_t)((tb + TT) * H + h) * 4), 0);
     int f_rem = L;                         // tokens from tile f on
-    const int64_t step_bc = (int64_t)TT * browg, step_x = (int64_t)TT * xrow, step_d = (int64_t)TT * H * 4;
+    const uint32_t step_bc = (uint32_t)__builtin_amdgcn_readfirstlane(TT * browg),
+                   step_x = (uint32_t)__builtin_amdgcn_readfirstlane(TT * xrow),
+                   step_d = (uint32_t)__builtin_amdgcn_readfirstlane(TT * H * 4);
+    auto advance = [](u32x4 &r, uint32_t inc) {   // base += inc (48-bit address, stride bits stay 0)
+        const uint64_t v = (((uint64_t)r.y) << 32 | r.x) + inc;
+        r.x = (uint32_t)v;
+        r.y = (uint32_t)(v >> 32);
+    };
 
     // Fetch tile f into stage buffer SLOT (zero-filling loads past the
     // sequence): part 0 loads C and B, part 1 x and the dt of tile f + 1
@@ -302,27 +315,25 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         constexpr int PART = decltype(part)::value, SLOT = decltype(slot_c)::value;
         const int Lt = clamp_len(f_rem);
         if constexpr (PART == 0) {
-            const u32x4 rC = buf_rsrc(f_c, Lt * browg);
-            const u32x4 rB = buf_rsrc(f_b, Lt * browg);
+            r_c.z = r_b.z = (uint32_t)(Lt * browg);
             static_for<SH::kIC>([&](auto i_c) {
                 constexpr int I = decltype(i_c)::value;
-                dma16_at<SLOT * SH::kTileC + 8192 * I>(rC, lds_c, go_c[I]);
+                dma16_at<SLOT * SH::kTileC + 8192 * I>(r_c, lds_c, go_c[I]);
             });
             static_for<SH::kIB>([&](auto i_c) {
                 constexpr int I = decltype(i_c)::value;
-                dma16_at<SLOT * SH::kTileB + 8192 * I>(rB, lds_b, go_b[I]);
+                dma16_at<SLOT * SH::kTileB + 8192 * I>(r_b, lds_b, go_b[I]);
             });
         } else {
-            const u32x4 rX = buf_rsrc(f_x, Lt * xrow);
-            const u32x4 rD = buf_rsrc(f_d, clamp_len(f_rem - TT) * H * 4);
+            r_x.z = (uint32_t)(Lt * xrow);
+            r_d.z = (uint32_t)(clamp_len(f_rem - TT) * H * 4);
             static_for<SH::kIX>([&](auto i_c) {
                 constexpr int I = decltype(i_c)::value;
-                dma16_at<SLOT * SH::kTileX + 8192 * I>(rX, lds_x, go_x[I]);
+                dma16_at<SLOT * SH::kTileX + 8192 * I>(r_x, lds_x, go_x[I]);
             });
-            dma4_at<SLOT * 256>(rD, lds_dt, go_d);
-            if (f_rem > 0) {   // advance to the next tile (past the end: stays, zero-sized)
-                f_c += step_bc; f_b += step_bc; f_x += step_x; f_d += step_d;
-            }
+            dma4_at<SLOT * 256>(r_d, lds_dt, go_d);
+            // next tile (past the sequence end the positions are never dereferenced)
+            advance(r_c, step_bc); advance(r_b, step_bc); advance(r_x, step_x); advance(r_d, step_d);
             f_rem -= TT;
         }
     };
@@ -336,13 +347,15 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
     // y of the previous tile: LDS tile (row rho = token, 128 bytes, chunk k at
     // k ^ ((rho >> 1) & 7)) -> y, one row per 8 lanes
-    char *y_prev = reinterpret_cast<char *>(a.y) + ((tb * H + h) * P + p0) * 2;   // tile t - 1
-    int y_len = 0;                                     // its tokens (0: nothing to store)
+    // tile t - 1 (starts one tile before the sequence, never dereferenced)
+    uint64_t y_prev = uni64((uint64_t)(uintptr_t)a.y + (uint64_t)((tb * H + h) * P + p0) * 2 - step_x);
+    int y_len = 0;    // its tokens (0: nothing to store)
+    int y_rem = L;    // tokens from tile t on
     const int yrow = 8 * wave + (lane >> 3);
     const uint32_t y_get = lds_addr(sY) + yrow * RX + 16 * ((lane & 7) ^ ((yrow >> 1) & 7));
     const uint32_t y_put = lds_addr(sY) + (r0 + q) * RX + 16 * ((2 * pb + (g >> 1)) ^ (((r0 + q) >> 1) & 7)) + 8 * (g & 1);
     auto store_prev_y = [&](const u32x4 &v) {
-        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(y_prev, 0, y_len * xrow, kBufFlags);
+        const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)y_prev, 0, y_len * xrow, kBufFlags);
         __builtin_amdgcn_raw_buffer_store_b128(v, ry, yrow * xrow + 16 * (lane & 7), 0, 0);
     };
 
@@ -400,8 +413,10 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
     int nexp = 0;           // checkpoint exports among the last two steps
     int ex1 = 0;            // did the previous step export
-    int dst = slot_of(0);   // checkpoint slot of the state after the current tile, or -1
     int t = 0;              // current tile
+    // checkpoint slots: a.chunk_states + slot * H P N floats + this workgroup's block
+    const uint64_t ck_base = uni64((uint64_t)(uintptr_t)a.chunk_states + (uint64_t)((h * P + p0) * N) * 4);
+    const uint64_t ck_slot = uni64((uint64_t)H * P * N * 4);
 
     // One step: tile t in stage SLOT (= t mod NST).
     auto step = [&](auto slot_c) {
@@ -410,6 +425,19 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         constexpr int OC = SLOT * SH::kTileC, OB = SLOT * SH::kTileB, OX = SLOT * SH::kTileX;
         const float *tab = tabs + SLOT * TAB;
         const float *tS = tab, *tE = tab + 64, *tD = tab + 128, *tW = tab + 192;
+
+        // checkpoint slot of the state after this tile, or -1
+        int dsl = -1;
+        if (t == ex_tile) {
+            dsl = (ex_chunk >= 0 && ex_chunk < a.max_chunks) ? (dstmap ? dstmap[ex_chunk] : ex_chunk) : -1;
+            if (dsl >= a.capacity) {
+                if (tid == 0) atomicOr(a.error_flag, SSD_DATA_BAD_SLOT);
+                dsl = -1;
+            }
+            dsl = __builtin_amdgcn_readfirstlane(dsl);
+            ++ex_chunk;
+            ex_tile = min(ex_tile + tpc, nt - 1);
+        }
 
         wait_stage(nexp);
         lds_barrier();   // (A) stage SLOT, this tile's tables, the partner's state half and y of tile t-1 are visible
@@ -535,23 +563,20 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         for (int d = 0; d < 2; ++d)
             *(lds_u32x2 *)(uintptr_t)(y_put + 16 * RX * d) =
                 u32x2{pack_bf16(acc[d][0], acc[d][1]), pack_bf16(acc[d][2], acc[d][3])};
-        if (t > 0) y_prev += step_x;
-        y_len = clamp_len(L - t * TT);
+        y_prev += step_x;
+        y_len = clamp_len(y_rem);
+        y_rem -= TT;
 
         // the state half after the tile into its checkpoint slot, if the tile
         // ends a chunk: two rounds of 8 state rows through 2 KB of stage
         // SLOT's B tile, each store 4 rows x 256 bytes
-        const bool bad_slot = dst >= a.capacity;
-        if (bad_slot && tid == 0) atomicOr(a.error_flag, SSD_DATA_BAD_SLOT);
-        const int dsl = __builtin_amdgcn_readfirstlane(bad_slot ? -1 : dst);
         const int ex = dsl >= 0 ? 1 : 0;
         nexp = ex1 + ex;
         ex1 = ex;
         if (dsl >= 0) {
-            const char *cbase = reinterpret_cast<const char *>(a.chunk_states) +
-                                ((((int64_t)dsl * H + h) * P + p0) * N) * 4;
+            const uint64_t cbase = ck_base + (uint64_t)dsl * ck_slot;
             const __amdgpu_buffer_rsrc_t re =
-                __builtin_amdgcn_make_buffer_rsrc((void *)cbase, 0, SH::kCols * N * 4, kBufFlags);
+                __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)cbase, 0, SH::kCols * N * 4, kBufFlags);
 #pragma unroll
             for (int rnd = 0; rnd < 2; ++rnd) {
                 if ((q >> 3) == rnd) {
@@ -575,7 +600,6 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             }
         }
         ++t;
-        dst = slot_of(t);
     };
 
     while (t < nt) {
