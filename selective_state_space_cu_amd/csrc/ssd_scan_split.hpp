@@ -46,7 +46,7 @@
 // values into an LDS tile of the workgroup's 64 tokens x 64 columns, which is
 // written out row by row after the next barrier (one step later); a
 // checkpoint is transposed through the just-consumed B tile, so that each
-// store covers 4 state rows x 256 bytes.
+// store covers 4 state rows x 256 contiguous bytes.
 #pragma once
 
 #include "ssd_scan.hpp"
@@ -90,7 +90,8 @@ __device__ __forceinline__ Ops<uint16_t>::Frag tr2(uint32_t lo_addr, uint32_t hi
     return Ops<uint16_t>::Frag{u32x4{a.x, a.y, b.x, b.y}};
 }
 // Orders LDS accesses across the lanes of one wave at the compiler level
-// (the hardware executes a wave's LDS instructions in order).
+// (the hardware executes a wave's LDS instructions in order): values read
+// before it are not reused for reads after it.
 __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_wave_barrier();
@@ -139,7 +140,6 @@ struct SplitShape {
     // the partner's state fragments use C blocks w + 8 c of a consumed stage
     static_assert(8 * kNKH <= kTileC / 1024, "state exchange needs 8 C blocks per fragment");
     // a checkpoint is staged in 2 KB per wave of a consumed B tile
-    static_assert(kWaves * 2048 <= kTileB, "checkpoint staging");
     static_assert(N == 128, "the swizzles and layouts are laid out for 256-byte B/C rows");
     __device__ static int swz128(int r) { return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
 };
@@ -207,6 +207,15 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     const int tpc = 1 << lg_tpc;
     int ex_tile = a.chunk_states != nullptr ? min(tpc, nt) - 1 : nt;
     int ex_chunk = c0;
+    // Checkpoint slots of 64 chunks at a time, lane k holding chunk ex_win + k
+    // (-1: none), so that an export reads its slot with v_readlane instead of
+    // a scalar load whose latency the next barrier would wait for.
+    int ex_win = c0;
+    auto load_slots = [&](int c) {
+        const int gc = c + lane;
+        return (gc >= 0 && gc < a.max_chunks) ? (dstmap ? dstmap[gc] : gc) : -1;
+    };
+    int slots = a.chunk_states != nullptr ? load_slots(ex_win) : -1;
     // n offset (elements) of register u's 4 values within the lane's 16
     auto n_of = [&](int u) { return 16 * g + 4 * (u ^ (g & 1)); };
 
@@ -406,11 +415,6 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         }
         axf[hi] = lds_addr(sX) + r * RX + 16 * ((2 * pb + ((q >> 1) & 1)) ^ SH::swz128(r)) + 8 * (q & 1);
     }
-    // checkpoint staging (2 KB of a consumed B tile per wave, 8 rows x 256
-    // bytes per round, chunk m of row i at m ^ i)
-    const uint32_t e_base = lds_addr(sB) + 2048 * wave;
-    const int e_row = lane >> 4;   // + 4 i: row within the round, read side
-
     int nexp = 0;           // checkpoint exports among the last two steps
     int ex1 = 0;            // did the previous step export
     int t = 0;              // current tile
@@ -429,7 +433,14 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         // checkpoint slot of the state after this tile, or -1
         int dsl = -1;
         if (t == ex_tile) {
-            dsl = (ex_chunk >= 0 && ex_chunk < a.max_chunks) ? (dstmap ? dstmap[ex_chunk] : ex_chunk) : -1;
+            if (ex_chunk - ex_win >= 64) {   // next window (once per 64 checkpoints)
+                ex_win = ex_chunk;
+                slots = load_slots(ex_win);
+                // wait here, on this rare path, so that no later use of the
+                // window waits for vector memory (the pipeline's loads included)
+                __builtin_amdgcn_s_waitcnt(WaitVm<0>::imm);
+            }
+            dsl = __builtin_amdgcn_readlane(slots, ex_chunk - ex_win);
             if (dsl >= a.capacity) {
                 if (tid == 0) atomicOr(a.error_flag, SSD_DATA_BAD_SLOT);
                 dsl = -1;
@@ -569,7 +580,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
         // the state half after the tile into its checkpoint slot, if the tile
         // ends a chunk: two rounds of 8 state rows through 2 KB of stage
-        // SLOT's B tile, each store 4 rows x 256 bytes
+        // SLOT's B tile (consumed), each store 4 rows x 256 bytes
         const int ex = dsl >= 0 ? 1 : 0;
         nexp = ex1 + ex;
         ex1 = ex;
@@ -577,6 +588,8 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             const uint64_t cbase = ck_base + (uint64_t)dsl * ck_slot;
             const __amdgpu_buffer_rsrc_t re =
                 __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)cbase, 0, SH::kCols * N * 4, kBufFlags);
+            const uint32_t e_base = lds_addr(sB) + 2048 * wave;   // chunk m of row i at m ^ i
+            const int e_row = lane >> 4;
 #pragma unroll
             for (int rnd = 0; rnd < 2; ++rnd) {
                 if ((q >> 3) == rnd) {
@@ -586,9 +599,6 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                         *(lds_u32x4 *)(uintptr_t)(e_base + OB + 256 * i + 16 * (m ^ i)) = __builtin_bit_cast(u32x4, st[u]);
                     }
                 }
-                // lanes read what other lanes wrote: LDS runs one wave's
-                // accesses in order, but the compiler must not reuse values
-                // read before the writes (the staging addresses repeat per round)
                 wave_lds_sync();
 #pragma unroll
                 for (int k = 0; k < 2; ++k) {
