@@ -97,6 +97,8 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
 }
+// Cache policy of the y and checkpoint stores: non-temporal (written once, not re-read here).
+constexpr int kStoreNT = 2;
 // Wave-uniform 64-bit value (kept in an SGPR pair).
 __device__ __forceinline__ uint64_t uni64(uint64_t v) {
     return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32) |
@@ -128,7 +130,9 @@ struct SplitShape {
     static constexpr int kMPB = (kTile + 16) * kES;  // decay matrix row pitch (160 bytes)
     static constexpr int kTab = 4 * 64;              // S, E, Dl, W
     static constexpr int kStage = kTileC + kTileB + kTileX + 256;
-    static constexpr int bytes(int n) { return n * (kStage + kTab * 4) + kTile * kMPB + kTileX; }
+    static constexpr int kStageE = 1024;             // checkpoint staging per wave (4 rows x 256 bytes)
+    // stages, decay matrix, y tile, x . w tile, checkpoint staging
+    static constexpr int bytes(int n) { return n * (kStage + kTab * 4) + kTile * kMPB + 2 * kTileX + kWaves * kStageE; }
     static constexpr bool fit(int n) { return bytes(n) <= kLdsLimit; }
     // vector memory instructions issued after the last load of the stage
     // waited for: one y store and the next stage's loads per step since, and
@@ -167,6 +171,8 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     __shared__ __align__(16) unsigned char sM[kTile * MPB];
     __shared__ __align__(16) unsigned char sY[SH::kTileX];   // y of the previous tile
     __shared__ __align__(16) float tabs[NST * TAB];
+    __shared__ __align__(16) unsigned char sXW[SH::kTileX];   // x . w of the current tile (x tile layout)
+    __shared__ __align__(16) unsigned char sE[SH::kWaves * SH::kStageE];   // checkpoint staging
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (kept in an SGPR)
@@ -365,7 +371,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     const uint32_t y_put = lds_addr(sY) + (r0 + q) * RX + 16 * ((2 * pb + (g >> 1)) ^ (((r0 + q) >> 1) & 7)) + 8 * (g & 1);
     auto store_prev_y = [&](const u32x4 &v) {
         const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)y_prev, 0, y_len * xrow, kBufFlags);
-        __builtin_amdgcn_raw_buffer_store_b128(v, ry, yrow * xrow + 16 * (lane & 7), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, yrow * xrow + 16 * (lane & 7), 0, kStoreNT);
     };
 
     // prologue: stages of tiles 0 .. NST-2 (and the y store slot of step -1)
@@ -417,6 +423,15 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     }
     int nexp = 0;           // checkpoint exports among the last two steps
     int ex1 = 0;            // did the previous step export
+    // the x . w pass: lane 64 wave + lane scales one 16-byte chunk (8 headdim
+    // columns of token row xw_row) of the swizzled x tile, in place of layout
+    const int xw_row = (64 * wave + lane) >> 3;
+    const uint32_t xw_off = xw_row * RX + 16 * (lane & 7);
+    // checkpoint staging: 4 state rows x 256 bytes per round, chunk m of row
+    // i at m ^ i; round r holds the lanes' rows q = 4 r .. 4 r + 3, and its
+    // store reads row lane / 16, chunk lane mod 16
+    const uint32_t e_base = lds_addr(sE) + SH::kStageE * wave;
+    const uint32_t e_get = e_base + 256 * (lane >> 4) + 16 * ((lane & 15) ^ (lane >> 4));
     int t = 0;              // current tile
     // checkpoint slots: a.chunk_states + slot * H P N floats + this workgroup's block
     const uint64_t ck_base = uni64((uint64_t)(uintptr_t)a.chunk_states + (uint64_t)((h * P + p0) * N) * 4);
@@ -484,6 +499,16 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             sj[r] = tS[16 * pb + 4 * g + r];
             dj[r] = tD[16 * pb + 4 * g + r];
         }
+        // (3) x . w of this tile, once per workgroup, for the state update
+        // after the next barrier: w_j = delta_j 2^(s_last - s_j) per token row
+        {
+            const u32x4 xv = *(const lds_u32x4 *)(uintptr_t)(lds_addr(sX) + OX + xw_off);
+            const float wr = tW[xw_row];
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = pack_bf16(bf16_lo(xv[i]) * wr, bf16_hi(xv[i]) * wr);
+            *(lds_u32x4 *)(uintptr_t)(lds_addr(sXW) + xw_off) = o;
+        }
 
         // (6) inter-chunk term Y^T = h_in . C^T over all n, then scale column i by 2^(s_i)
         f32x4 acc[2];
@@ -523,38 +548,34 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         fetch(P0{}, std::integral_constant<int, FETCH>{});
 
-        // (3, 4) this wave's state half: h = 2^(s_last) h + B^T . (w o x)
-        Frag xf[2];
-        {
-            Frag bt[2][NTH];
-            float w[2][8];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                xf[ks] = tr2(axf[0] + OX + 32 * RX * ks, axf[1] + OX + 32 * RX * ks);
-#pragma unroll
-                for (int u = 0; u < NTH; ++u) bt[ks][u] = tr2(abt[u][0] + OB + 32 * RB * ks, abt[u][1] + OB + 32 * RB * ks);
-#pragma unroll
-                for (int sl = 0; sl < 8; ++sl) w[ks][sl] = tW[32 * ks + 8 * g + sl];
-            }
-            const float e = fast_exp2(sL);
-#pragma unroll
-            for (int u = 0; u < NTH; ++u) st[u] *= e;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const Frag xw = O::scale(xf[ks], w[ks]);
-#pragma unroll
-                for (int u = 0; u < NTH; ++u) st[u] = O::mma(st[u], bt[ks][u], xw);
-            }
-        }
-
         // scan tables of the next tile, from the dt that rode with this stage
         if (wave < 4 && t + 1 < nt) {
             const int Ln = clamp_len(L - (t + 1) * TT);
             tables(tabs + NEXT * TAB, softplus_hw(sDt[SLOT * 64 + lane] + bias + (lane < Ln ? 0.0f : -INFINITY)));
         }
-        lds_barrier();   // (B) decay matrix and next tables complete; stage SLOT's C and B tiles consumed
+        lds_barrier();   // (B) decay matrix, x . w and next tables complete; stage SLOT's C tile consumed
 
         // ---- phase B
+        // (4) this wave's state half: h = 2^(s_last) h + B^T . (w o x)
+        Frag xf[2];   // x^T fragments (tokens 32 ks + ..) of this wave's columns, for the intra term
+        {
+            Frag bt[2][NTH], xw[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                xf[ks] = tr2(axf[0] + OX + 32 * RX * ks, axf[1] + OX + 32 * RX * ks);
+                xw[ks] = tr2(axf[0] - lds_addr(sX) + lds_addr(sXW) + 32 * RX * ks,
+                             axf[1] - lds_addr(sX) + lds_addr(sXW) + 32 * RX * ks);
+#pragma unroll
+                for (int u = 0; u < NTH; ++u) bt[ks][u] = tr2(abt[u][0] + OB + 32 * RB * ks, abt[u][1] + OB + 32 * RB * ks);
+            }
+            const float e = fast_exp2(sL);
+#pragma unroll
+            for (int u = 0; u < NTH; ++u) st[u] *= e;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int u = 0; u < NTH; ++u) st[u] = O::mma(st[u], bt[ks][u], xw[ks]);
+        }
         // this wave's half of h_out for the partner, into stage SLOT's C blocks
         make_own();
         put_own(slot_c);
@@ -579,8 +600,8 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         y_rem -= TT;
 
         // the state half after the tile into its checkpoint slot, if the tile
-        // ends a chunk: two rounds of 8 state rows through 2 KB of stage
-        // SLOT's B tile (consumed), each store 4 rows x 256 bytes
+        // ends a chunk: four rounds of 4 state rows through the wave's staging
+        // area, each store 4 rows x 256 bytes
         const int ex = dsl >= 0 ? 1 : 0;
         nexp = ex1 + ex;
         ex1 = ex;
@@ -588,24 +609,18 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             const uint64_t cbase = ck_base + (uint64_t)dsl * ck_slot;
             const __amdgpu_buffer_rsrc_t re =
                 __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)cbase, 0, SH::kCols * N * 4, kBufFlags);
-            const uint32_t e_base = lds_addr(sB) + 2048 * wave;   // chunk m of row i at m ^ i
-            const int e_row = lane >> 4;
 #pragma unroll
-            for (int rnd = 0; rnd < 2; ++rnd) {
-                if ((q >> 3) == rnd) {
+            for (int rnd = 0; rnd < 4; ++rnd) {
+                if ((q >> 2) == rnd) {
 #pragma unroll
                     for (int u = 0; u < NTH; ++u) {
-                        const int i = q & 7, m = n_of(u) / 4;
-                        *(lds_u32x4 *)(uintptr_t)(e_base + OB + 256 * i + 16 * (m ^ i)) = __builtin_bit_cast(u32x4, st[u]);
+                        const int i = q & 3, m = n_of(u) / 4;
+                        *(lds_u32x4 *)(uintptr_t)(e_base + 256 * i + 16 * (m ^ i)) = __builtin_bit_cast(u32x4, st[u]);
                     }
                 }
                 wave_lds_sync();
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const int i = e_row + 4 * k;
-                    const u32x4 v = *(const lds_u32x4 *)(uintptr_t)(e_base + OB + 256 * i + 16 * ((lane & 15) ^ i));
-                    __builtin_amdgcn_raw_buffer_store_b128(v, re, ((16 * pb + 8 * rnd + i) * N + nb) * 4 + 16 * (lane & 15), 0, 0);
-                }
+                const u32x4 v = *(const lds_u32x4 *)(uintptr_t)e_get;
+                __builtin_amdgcn_raw_buffer_store_b128(v, re, ((16 * pb + 4 * rnd + (lane >> 4)) * N + nb) * 4 + 16 * (lane & 15), 0, kStoreNT);
                 wave_lds_sync();
             }
         }
