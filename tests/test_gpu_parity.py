@@ -99,6 +99,7 @@ SHAPES = [
     ("bf16", [1, 15, 16, 17, 31, 33, 250], 3, 64, 128, 1, 16),
     ("bf16", [190, 0, 64, 96], 2, 192, 128, 2, 32),
     ("bf16", [700, 1000, 2], 2, 64, 128, 1, 128),
+    ("bf16", [150, 64, 0, 33], 2, 256, 128, 2, 64),
     ("bf16", [130, 5, 260], 2, 32, 64, 1, 128),
     ("bf16", [40, 3, 17], 2, 16, 16, 1, 16),
     ("bf16", [100, 33], 2, 48, 256, 2, 32),
@@ -235,3 +236,47 @@ def test_plan_with_computed_prefix_bit_exact():
         assert np.array_equal(src.cpu().numpy(), rs), trial
         assert np.array_equal(dst.cpu().numpy(), rd), trial
         assert int(meta.error_flag.item()) == 0
+
+
+def test_bad_checkpoint_slot_sets_error_flag():
+    """A checkpoint slot at or past the cache's capacity is reported through the
+    metadata error flag and skipped (no write outside the cache); every other
+    output is unaffected. Split-state path (bf16, dstate 128) and four-wave path."""
+    for dtype, P, N in (("bf16", 64, 128), ("f32", 32, 64)):
+        w = make_inputs([130, 70], 2, P, N, 1, 64, dtype=dtype, init_seqs=[0], seed=5)
+        d = to_dev(w)
+        log(f"bad slot {dtype} P={P} N={N}")
+        meta = ssd.varlen_metadata(d["cu_seqlens"], 64, total_tokens=w.total_tokens)
+        nch = int(meta.nchunks.item())
+        slots = 8
+        dst = torch.full((meta.max_chunks,), -1, dtype=torch.int32)   # one entry per chunk capacity
+        dst[:nch] = torch.arange(nch, dtype=torch.int32)
+        dst[1] = slots + 3                    # out of range: must be flagged, not written
+        cache = torch.full((slots + 4, 2, P, N), 7.0, device="cuda")   # guard slots past `slots`
+        y, fin = ssd.chunk_scan_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], meta,
+                                       dt_bias=d["dt_bias"], D=d["D"],
+                                       initial_states=d["initial_states"],
+                                       has_initial_state=d["has_initial_state"],
+                                       chunk_states=cache[:slots], chunk_state_dst=dst.cuda())
+        torch.cuda.synchronize()
+        flag = int(meta.error_flag.item())
+        assert flag & ssd.DATA_BAD_SLOT, flag
+        assert torch.all(cache[slots:] == 7.0), "write past the cache capacity"
+        _, y_ref, fin_ref, _ = gpu_run(w, d=d)
+        assert torch.equal(y.view(torch.int16) if dtype == "bf16" else y,
+                           y_ref.view(torch.int16) if dtype == "bf16" else y_ref)
+        assert torch.equal(fin, fin_ref)
+
+
+def test_scan_bit_deterministic():
+    """Two launches of the same problem give bit-identical y, final and chunk states
+    (no atomics or order-dependent reductions in the data path)."""
+    w = make_inputs([500, 77, 1000], 4, 128, 128, 2, 64, dtype="bf16", init_seqs=[1], seed=11)
+    d = to_dev(w)
+    log("determinism")
+    _, y1, f1, c1 = gpu_run(w, export="dense", d=d)
+    _, y2, f2, c2 = gpu_run(w, export="dense", d=d)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(f1, f2)
+    n = c1.shape[0]
+    assert torch.equal(torch.nan_to_num(c1[:n], nan=-1.0), torch.nan_to_num(c2[:n], nan=-1.0))
