@@ -23,7 +23,8 @@
 //   CB[i, j]    = C[i, :] . B[j, :]^T -> decay matrix M[i, j] (sub-tiles (I, J))
 //   h_out[p, n] = 2^(s_last) h_in[p, n] + sum_j B[j, n] w_j x[j, p]  (own n half)
 //   Y^T[p, i]  += sum_j x[j, p] M[i, j]                 (after the second barrier)
-// with the scan tables (s, 2^s, delta, w) of the next tile computed by waves 0-3.
+// with the scan tables (s, 2^s, delta, w) of the next tile computed by waves 0-3
+// (and, after the second barrier, each wave's decay factors of the next tile).
 // The tile pipeline (NST stages of direct-to-LDS loads, exact vmcnt waits) is
 // that of the four-wave kernel.
 //
@@ -57,13 +58,21 @@ namespace ssd {
 // offset (m0 = base + OFF), so that per-stage addresses need no extra registers.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// A wave-uniform resource quad as SGPRs (the asm operands below need them;
+// readfirstlane is free for a value the compiler already keeps in SGPRs).
+__device__ __forceinline__ u32x4 sgpr4(const u32x4 &r) {
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)r.x), (uint32_t)__builtin_amdgcn_readfirstlane((int)r.y),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)r.z), (uint32_t)__builtin_amdgcn_readfirstlane((int)r.w)};
+}
 template <int OFF>
-__device__ __forceinline__ void dma16_at(const u32x4 &r, uint32_t lds_base, int voff) {
+__device__ __forceinline__ void dma16_at(const u32x4 &r0, uint32_t lds_base, int voff) {
+    const u32x4 r = sgpr4(r0);
     asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF) : "memory", "m0", "scc");
 }
 template <int OFF>
-__device__ __forceinline__ void dma4_at(const u32x4 &r, uint32_t lds_base, int voff) {
+__device__ __forceinline__ void dma4_at(const u32x4 &r0, uint32_t lds_base, int voff) {
+    const u32x4 r = sgpr4(r0);
     asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF) : "memory", "m0", "scc");
 }
@@ -394,6 +403,36 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             dadd[d][r] = j == i ? Dh : 0.0f;
         }
 
+    // Decay factors of this wave's sub-tiles (f = 2^(s_i - s_j) delta_j: at most
+    // delta_j for j <= i, 2^(-inf) = 0 above the diagonal) and the inter-chunk
+    // row scales 2^(s_i) of a tile, computed from its tables after the barrier
+    // before the one that starts its step, off that step's critical path
+    float fdec[2][4], eic[2];
+    auto decay_of = [&](const float *tab) {
+        const float *tS = tab, *tE = tab + 64, *tD = tab + 128;
+        float sj[4], dj[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sj[r] = tS[16 * pb + 4 * g + r];
+            dj[r] = tD[16 * pb + 4 * g + r];
+        }
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            eic[d] = tE[r0 + 16 * d + q];
+            const float si = tS[r0 + 16 * d + q];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) fdec[d][r] = fast_exp2(si - sj[r] + mbias[d][r]) * dj[r];
+        }
+    };
+    auto pin_decay = [&]() {   // keeps the computation where it is written
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            asm volatile("" : "+v"(eic[d]));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(fdec[d][r]));
+        }
+    };
+
     // Per-lane LDS addresses of the swizzled fragment reads (stage 0; stages,
     // row blocks and k-steps over tokens are immediate offsets).
     //   C rows r0 + q and B rows 16 pb + q: 16 bytes at n = nb' + 16 g + 8 c
@@ -443,7 +482,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         constexpr int NEXT = (SLOT + 1) % NST, FETCH = (SLOT + NST - 1) % NST;
         constexpr int OC = SLOT * SH::kTileC, OB = SLOT * SH::kTileB, OX = SLOT * SH::kTileX;
         const float *tab = tabs + SLOT * TAB;
-        const float *tS = tab, *tE = tab + 64, *tD = tab + 128, *tW = tab + 192;
+        const float *tS = tab, *tW = tab + 192;
 
         // checkpoint slot of the state after this tile, or -1
         int dsl = -1;
@@ -477,7 +516,6 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         // C fragments of this wave's row blocks (own / partner n half) and B
         // fragments of column block pb, shared by C . h^T and C . B^T
         Frag co[2][NKH], cp[2][NKH], bo[NKH], bq[NKH];
-        float ei[2], si[2];
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
 #pragma unroll
@@ -485,19 +523,11 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 co[d][c] = rf16(ac_o[c] + OC + 16 * RB * d);
                 cp[d][c] = rf16(ac_p[c] + OC + 16 * RB * d);
             }
-            ei[d] = tE[r0 + 16 * d + q];
-            si[d] = tS[r0 + 16 * d + q];
         }
 #pragma unroll
         for (int c = 0; c < NKH; ++c) {
             bo[c] = rf16(ab_o[c] + OB);
             bq[c] = rf16(ab_p[c] + OB);
-        }
-        float sj[4], dj[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            sj[r] = tS[16 * pb + 4 * g + r];
-            dj[r] = tD[16 * pb + 4 * g + r];
         }
         // (3) x . w of this tile, once per workgroup, for the state update
         // after the next barrier: w_j = delta_j 2^(s_last - s_j) per token row
@@ -520,7 +550,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 acc[d] = O::mma(acc[d], hown[c], co[d][c]);
                 acc[d] = O::mma(acc[d], hp[c], cp[d][c]);
             }
-            acc[d] *= ei[d];
+            acc[d] *= eic[d];
         }
         store_prev_y(yv);
 
@@ -535,11 +565,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             }
             float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // 2^(s_i - s_j) <= 1 for j <= i; 2^(-inf) = 0 above the diagonal
-                const float f = fast_exp2(si[d] - sj[r] + mbias[d][r]) * dj[r];
-                v[r] = fmaf(cb[r], f, dadd[d][r]);
-            }
+            for (int r = 0; r < 4; ++r) v[r] = fmaf(cb[r], fdec[d][r], dadd[d][r]);
             O::mstore4(sM + (r0 + 16 * d + q) * MPB + (16 * pb + 4 * g) * 2, v);
         }
 
@@ -568,6 +594,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #pragma unroll
                 for (int u = 0; u < NTH; ++u) bt[ks][u] = tr2(abt[u][0] + OB + 32 * RB * ks, abt[u][1] + OB + 32 * RB * ks);
             }
+            decay_of(tabs + NEXT * TAB);   // of the next tile (its tables are visible since the last barrier)
             const float e = fast_exp2(sL);
 #pragma unroll
             for (int u = 0; u < NTH; ++u) st[u] *= e;
@@ -624,9 +651,12 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 wave_lds_sync();
             }
         }
+        pin_decay();
         ++t;
     };
 
+    lds_barrier();   // tile 0's tables are visible
+    decay_of(tabs);
     while (t < nt) {
         step(std::integral_constant<int, 0>{});
         if (t >= nt) break;
