@@ -25,8 +25,12 @@
 //   Y^T[p, i]  += sum_j x[j, p] M[i, j]                 (after the second barrier)
 // with the scan tables (s, 2^s, delta, w) of the next tile computed by waves 0-3
 // (and, after the second barrier, each wave's decay factors of the next tile).
-// The tile pipeline (NST stages of direct-to-LDS loads, exact vmcnt waits) is
-// that of the four-wave kernel.
+// The tile pipeline (NST stages, exact vmcnt waits) is that of the four-wave
+// kernel for B, C and dt (direct-to-LDS loads two tiles ahead). x, the stream
+// that comes from HBM, runs deeper through registers: each wave loads its 1 KB
+// of x for tile t + 5 at the end of step t and writes it into the stage three
+// steps later, once that stage has been consumed (4 VGPRs per step of depth
+// instead of another 41 KB stage).
 //
 // LDS tiles are unpadded (a C or B tile is 16 KB, an x tile 8 KB, so each of
 // the eight waves fills whole 1 KB blocks of every tile) and conflict-free by
@@ -76,6 +80,15 @@ __device__ __forceinline__ void dma4_at(const u32x4 &r0, uint32_t lds_base, int 
     asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF) : "memory", "m0", "scc");
 }
+// A 16-byte buffer load into registers that the compiler does not track (like
+// the direct-to-LDS loads): the caller waits for it with an explicit vmcnt and
+// then passes the value through reg_fence, so that no use moves above the wait.
+template <int OFF>
+__device__ __forceinline__ void load16_untracked(u32x4 &dst, const u32x4 &r0, int voff) {
+    const u32x4 r = sgpr4(r0);
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3" : "=v"(dst) : "v"(voff), "s"(r), "i"(OFF) : "memory");
+}
+__device__ __forceinline__ void reg_fence(u32x4 &v) { asm volatile("" : "+v"(v)); }
 #pragma clang diagnostic pop
 
 // Compile-time loop: f(integral_constant<int, i>) for i = 0 .. N-1.
@@ -144,9 +157,9 @@ struct SplitShape {
     static constexpr int bytes(int n) { return n * (kStage + kTab * 4) + kTile * kMPB + 2 * kTileX + kWaves * kStageE; }
     static constexpr bool fit(int n) { return bytes(n) <= kLdsLimit; }
     // vector memory instructions issued after the last load of the stage
-    // waited for: one y store and the next stage's loads per step since, and
-    // kNTH stores per step that exported a checkpoint
-    static constexpr int vm_wait(int exports) { return 1 + kLoads + exports * kNTH; }
+    // waited for: that step's register load of x, then one y store and the
+    // next step's loads, and kNTH stores per step that exported a checkpoint
+    static constexpr int vm_wait(int exports) { return 2 + kLoads + exports * kNTH; }
     static constexpr int kNST = 3;
     static_assert(fit(kNST), "three stages must fit in LDS");
     static_assert(vm_wait(2) <= 63, "vmcnt range");
@@ -335,7 +348,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     // Fetch tile f into stage buffer SLOT (zero-filling loads past the
     // sequence): part 0 loads C and B, part 1 x and the dt of tile f + 1
     // (then advances f); always kLoads instructions per wave in all.
-    auto fetch = [&](auto part, auto slot_c) {
+    auto fetch = [&](auto part, auto slot_c, auto with_x) {
         constexpr int PART = decltype(part)::value, SLOT = decltype(slot_c)::value;
         const int Lt = clamp_len(f_rem);
         if constexpr (PART == 0) {
@@ -351,10 +364,12 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         } else {
             r_x.z = (uint32_t)(Lt * xrow);
             r_d.z = (uint32_t)(clamp_len(f_rem - TT) * H * 4);
-            static_for<SH::kIX>([&](auto i_c) {
-                constexpr int I = decltype(i_c)::value;
-                dma16_at<SLOT * SH::kTileX + 8192 * I>(r_x, lds_x, go_x[I]);
-            });
+            if constexpr (decltype(with_x)::value) {
+                static_for<SH::kIX>([&](auto i_c) {
+                    constexpr int I = decltype(i_c)::value;
+                    dma16_at<SLOT * SH::kTileX + 8192 * I>(r_x, lds_x, go_x[I]);
+                });
+            }
             dma4_at<SLOT * 256>(r_d, lds_dt, go_d);
             // next tile (past the sequence end the positions are never dereferenced)
             advance(r_c, step_bc); advance(r_b, step_bc); advance(r_x, step_x); advance(r_d, step_d);
@@ -363,6 +378,21 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
+    using WithX = std::true_type;
+    using NoX = std::false_type;
+    static_assert(SH::kIX == 1, "one 1 KB block of x per wave per tile");
+    // x of tile t + 5 goes into register set t mod 3 at the end of step t and
+    // from there into its stage in step t + 3 (tiles 0 and 1 by direct loads)
+    u32x4 xr[NST];
+    u32x4 r_xg = buf_rsrc(uni64((uint64_t)(uintptr_t)a.x + (uint64_t)(((tb + 2 * TT) * H + h) * P + p0) * 2), 0);
+    int xg_rem = L - 2 * TT;   // tokens from the tile whose x is loaded next
+    auto xload = [&](auto set_c) {
+        constexpr int SET = decltype(set_c)::value;
+        r_xg.z = (uint32_t)(clamp_len(xg_rem) * xrow);
+        load16_untracked<0>(xr[SET], r_xg, go_x[0]);
+        advance(r_xg, step_x);
+        xg_rem -= TT;
+    };
     auto wait_stage = [&](int exports) {   // checkpoint exports among the last two steps
         if (exports == 0) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(0)>::imm);
         else if (exports == 1) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(1)>::imm);
@@ -384,11 +414,14 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     };
 
     // prologue: stages of tiles 0 .. NST-2 (and the y store slot of step -1)
-    fetch(P0{}, std::integral_constant<int, 0>{});
-    fetch(P1{}, std::integral_constant<int, 0>{});
+    xload(std::integral_constant<int, 0>{});   // x of tile 2
+    fetch(P0{}, std::integral_constant<int, 0>{}, WithX{});
+    fetch(P1{}, std::integral_constant<int, 0>{}, WithX{});
+    xload(std::integral_constant<int, 1>{});   // x of tile 3
     store_prev_y(u32x4{0, 0, 0, 0});   // zero-sized: keeps the per-step count of vector memory ops
-    fetch(P0{}, std::integral_constant<int, 1>{});
-    fetch(P1{}, std::integral_constant<int, 1>{});
+    fetch(P0{}, std::integral_constant<int, 1>{}, WithX{});
+    fetch(P1{}, std::integral_constant<int, 1>{}, WithX{});
+    xload(std::integral_constant<int, 2>{});   // x of tile 4
 
     // Diagonal structure of this wave's decay-matrix sub-tiles (rows
     // i = r0 + 16 d + q, columns j = 16 pb + 4 g + r): exponent bias 0 for
@@ -505,6 +538,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         }
 
         wait_stage(nexp);
+        reg_fence(xr[SLOT]);   // x of tile t + 2, loaded three steps ago
         lds_barrier();   // (A) stage SLOT, this tile's tables, the partner's state half and y of tile t-1 are visible
 
         // ---- phase A
@@ -572,7 +606,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         // B and C of tile t + NST - 1 into stage FETCH, once this wave's reads
         // of its C blocks there (the partner's state half) have completed
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        fetch(P0{}, std::integral_constant<int, FETCH>{});
+        fetch(P0{}, std::integral_constant<int, FETCH>{}, NoX{});
 
         // scan tables of the next tile, from the dt that rode with this stage
         if (wave < 4 && t + 1 < nt) {
@@ -612,7 +646,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         for (int d = 0; d < 2; ++d)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) mf[d][ks] = O::mrow(sM + (r0 + 16 * d + q) * MPB + (32 * ks + 8 * g) * 2);
-        fetch(P1{}, std::integral_constant<int, FETCH>{});   // x and dt of tile t + NST - 1
+        fetch(P1{}, std::integral_constant<int, FETCH>{}, NoX{});   // dt of tile t + NST
 #pragma unroll
         for (int d = 0; d < 2; ++d)
 #pragma unroll
@@ -622,6 +656,8 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         for (int d = 0; d < 2; ++d)
             *(lds_u32x2 *)(uintptr_t)(y_put + 16 * RX * d) =
                 u32x2{pack_bf16(acc[d][0], acc[d][1]), pack_bf16(acc[d][2], acc[d][3])};
+        // x of tile t + 2 into stage FETCH (consumed by the previous step)
+        *(lds_u32x4 *)(uintptr_t)(lds_x + FETCH * SH::kTileX + 16 * lane) = xr[SLOT];
         y_prev += step_x;
         y_len = clamp_len(y_rem);
         y_rem -= TT;
@@ -652,6 +688,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             }
         }
         pin_decay();
+        xload(slot_c);   // x of tile t + 5 (set SLOT is free again)
         ++t;
     };
 
@@ -664,6 +701,8 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         if (t >= nt) break;
         step(std::integral_constant<int, 2>{});
     }
+    // register loads of x past the last step are still in flight
+    __builtin_amdgcn_s_waitcnt(WaitVm<0>::imm);
     if (nt > 0) {   // y of the last tile
         lds_barrier();
         store_prev_y(*(const lds_u32x4 *)(uintptr_t)y_get);
