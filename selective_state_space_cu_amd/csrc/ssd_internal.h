@@ -30,9 +30,23 @@ struct ScanArgs {
     const int32_t *seq_order;
     int32_t *error_flag;
     int32_t T, S, H, P, G, cs, max_chunks, capacity, nptiles;
-    // 1: workgroups of one (sequence, group) run on one XCD (needs S*G % 8 == 0)
-    int32_t xcd_pairs;
+    // workgroup -> XCD mapping (see decode_block): one of the kXcd* values
+    int32_t xcd_mode;
 };
+
+enum : int32_t { kXcdNone = 0, kXcdPairs = 1, kXcdSplit = 2, kXcdPairsIfEqual = 3, kXcdPairsIfEqualElseNone = 4 };
+
+// Mapping for a launch: pairs when that balances the XCDs whatever the lengths
+// (G a multiple of 8); else pairs only where the lengths turn out equal
+// (checked on the device), and otherwise an even split of every sequence
+// across the XCDs, or block order where the split does not divide.
+inline int32_t xcd_mode_for(int32_t nseqs, int32_t nheads, int32_t ngroups, int32_t nptiles) {
+    const bool pairs = (int64_t)nseqs * ngroups % 8 == 0;
+    const bool split = (int64_t)nheads * nptiles % 8 == 0;
+    if (pairs && ngroups % 8 == 0) return kXcdPairs;
+    if (pairs) return split ? kXcdPairsIfEqual : kXcdPairsIfEqualElseNone;
+    return split ? kXcdSplit : kXcdNone;
+}
 
 // Launches the scan for one (dtype, waves-per-workgroup, dstate) instance.
 hipError_t launch_scan_bf16(const ScanArgs &a, int waves, int dstate, hipStream_t stream);

@@ -365,19 +365,47 @@ __device__ __forceinline__ void tile_tables(float *tab, float *sink, float d, fl
 }
 
 // Workgroup -> (sequence rank, head, headdim tile). Workgroups are handed to
-// the 8 XCDs round-robin (block b runs on XCD b mod 8), each with its own L2:
-// with xcd_pairs, all workgroups of one (sequence, group) pair -- which read
-// the same B and C tiles -- land on one XCD, pairs p = x, x + 8, ... on XCD x
-// (longest sequences first on every XCD).
+// the 8 XCDs round-robin (block b runs on XCD b mod 8), each with its own L2,
+// and within an XCD in block order (sequence ranks ascend, so the longest
+// sequences start first on every XCD). Mappings (ScanArgs::xcd_mode):
+//   kXcdPairs: all workgroups of one (sequence, group) pair -- which read the
+//     same B and C tiles -- land on one XCD, pairs p = x, x + 8, ... on XCD x.
+//     Every XCD gets the same work when G is a multiple of 8 (XCD x takes
+//     groups x, x + 8, ... of every sequence) or when all sequences have the
+//     same length.
+//   kXcdSplit: every XCD takes 1/8 of each sequence's workgroups, a contiguous
+//     run of heads (so a group's B and C tiles are read by as few XCDs as
+//     this balance allows): the same work on every XCD for any length mix.
+//   kXcdPairsIfEqual (kXcdPairsIfEqualElseNone): kXcdPairs when all sequence
+//     lengths are equal, else kXcdSplit (kXcdNone); decided here from
+//     cu_seqlens, every wave gets the same answer.
+//   kXcdNone: block order (sequence rank, head, tile); consecutive heads of a
+//     sequence go to different XCDs.
+__device__ __forceinline__ bool all_lengths_equal(const ScanArgs &a) {
+    const int lane = threadIdx.x & 63;
+    const int l0 = a.cu_seqlens[1] - a.cu_seqlens[0];
+    bool eq = true;
+    for (int i = lane; i < a.S; i += 64) eq = eq && (a.cu_seqlens[i + 1] - a.cu_seqlens[i]) == l0;
+    return __builtin_amdgcn_ballot_w64(!eq) == 0;
+}
 __device__ __forceinline__ void decode_block(const ScanArgs &a, int b, int &rank, int &h, int &pt) {
-    const int hpg = a.H / a.G;
-    if (a.xcd_pairs) {
+    int mode = a.xcd_mode;
+    if (mode == kXcdPairsIfEqual || mode == kXcdPairsIfEqualElseNone)
+        mode = all_lengths_equal(a) ? kXcdPairs : (mode == kXcdPairsIfEqual ? kXcdSplit : kXcdNone);
+    const int x = b & 7, i = b >> 3;
+    if (mode == kXcdPairs) {
+        const int hpg = a.H / a.G;
         const int wpp = hpg * a.nptiles;   // workgroups per pair
-        const int x = b & 7, i = b >> 3;
         const int pair = x + 8 * (i / wpp), loc = i - (i / wpp) * wpp;
         rank = pair / a.G;
         h = (pair - rank * a.G) * hpg + loc / a.nptiles;
         pt = loc - (loc / a.nptiles) * a.nptiles;
+    } else if (mode == kXcdSplit) {
+        const int per_x = a.H * a.nptiles / 8;   // workgroups of one sequence per XCD
+        rank = i / per_x;
+        const int loc = x * per_x + (i - rank * per_x);
+        h = loc / a.nptiles;
+        pt = loc - h * a.nptiles;
     } else {
         const int per_seq = a.H * a.nptiles;
         rank = b / per_seq;

@@ -104,6 +104,11 @@ SHAPES = [
     ("bf16", [40, 3, 17], 2, 16, 16, 1, 16),
     ("bf16", [100, 33], 2, 48, 256, 2, 32),
     ("bf16", [1], 2, 64, 32, 2, 64),
+    # workgroup -> XCD mappings: pairs picked on the device for equal lengths
+    # (headdim split three ways, so no even split), and an even split of
+    # every sequence across the XCDs (unequal lengths, no pairs)
+    ("bf16", [96, 96, 96, 96], 2, 192, 128, 2, 32),
+    ("bf16", [100, 257, 31], 8, 64, 128, 1, 64),
     ("f32", [300, 9], 2, 64, 128, 1, 256),
     ("f32", [70, 0, 10], 3, 16, 32, 3, 64),
     ("f32", [50, 64, 16], 2, 32, 64, 1, 16),
