@@ -36,6 +36,10 @@ def load(path=LIB):
     lib.oracle_checkpoint_plan.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32, _I32P,
                                            _I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            _I32P, _I32P]
+    lib.oracle_ssd_decode.restype = ctypes.c_int
+    lib.oracle_ssd_decode.argtypes = [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, ctypes.c_int32, _I32P, _I32P, _F64P]
     lib.oracle_num_threads.restype = ctypes.c_int
     _cache[path] = lib
     return lib
@@ -122,3 +126,26 @@ def checkpoint_plan(cu_seqlens, seq_chunk_start, max_chunks, block_table, block_
     if rc != 0:
         raise ValueError(f"oracle_checkpoint_plan failed ({rc})")
     return src, dst
+
+
+def ssd_decode(x, dt, dt_bias, A, B, C, D, state_cache, read_slot, write_slot, lib=None):
+    """One decode token per sequence with dual state anchors (float64).
+    x (S,H,P), dt (S,H), B, C (S,G,N), state_cache (slots,H,P,N); read_slot /
+    write_slot (S,) int, < 0 meaning zero state / no write.
+    Returns (y (S,H,P), updated copy of the cache, status: 0, or -2 if a slot
+    was out of range and its sequence skipped)."""
+    lib = lib or load()
+    x, dt, B, C = (_np(v, np.float64) for v in (x, dt, B, C))
+    dt_bias, A, D = (_np(v, np.float64) for v in (dt_bias, A, D))
+    cache = _np(state_cache, np.float64).copy()
+    rs, ws = _np(read_slot, np.int32), _np(write_slot, np.int32)
+    S, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    y = np.zeros((S, H, P), np.float64)
+    rc = lib.oracle_ssd_decode(S, H, P, N, G, _p(x, _F64P), _p(dt, _F64P), _p(dt_bias, _F64P),
+                               _p(A, _F64P), _p(B, _F64P), _p(C, _F64P), _p(D, _F64P),
+                               _p(cache, _F64P), cache.shape[0], _p(rs, _I32P), _p(ws, _I32P),
+                               _p(y, _F64P))
+    if rc == -1:
+        raise ValueError("oracle_ssd_decode: bad shapes")
+    return y, cache, rc

@@ -251,3 +251,75 @@ int oracle_checkpoint_plan(int32_t nseqs, const int32_t *cu_seqlens, const int32
     }
     return 0;
 }
+
+/*
+ * One decode step with dual state anchors. The prefix-caching page's decode
+ * kernels read a request's running state from one cache slot (the previous
+ * step's write anchor) and write the advanced state to another (the current
+ * anchor), so that a cached checkpoint is never overwritten in place.
+ * Here, for each sequence s (one new token each) and head h:
+ *     S     = state_cache[read_slot[s], h]      (all zero when read_slot[s] < 0)
+ *     delta = softplus(dt[s,h] + dt_bias[h])
+ *     S'    = exp(A[h] * delta) * S + delta * x[s,h] (outer) B[s,g]
+ *     y[s,h] = S' . C[s,g] + D[h] * x[s,h]
+ *     state_cache[write_slot[s], h] = S'        (skipped when write_slot[s] < 0)
+ * All slot reads happen before any slot write, so read_slot == write_slot is an
+ * in-place update. Layouts: x, y (S,H,P); dt (S,H); B, C (S,G,N); cache
+ * (num_slots,H,P,N). A sequence with a slot >= num_slots is skipped (y left
+ * as is, nothing written) and the call returns -2; -1 on bad shapes.
+ */
+int oracle_ssd_decode(int32_t nseqs, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                      const double *x, const double *dt, const double *dt_bias, const double *A,
+                      const double *B, const double *C, const double *D, double *state_cache,
+                      int32_t num_slots, const int32_t *read_slot, const int32_t *write_slot,
+                      double *y)
+{
+    const int64_t H = nheads, P = headdim, N = dstate, G = ngroups;
+    if (nseqs < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0 || num_slots < 0)
+        return -1;
+    const int64_t per_state = H * P * N;
+    int bad = 0;
+    /* gather every sequence's entering state first (reads before writes) */
+    double *h_in = (double *)calloc((size_t)(nseqs > 0 ? nseqs : 1) * (size_t)per_state, sizeof(double));
+    if (!h_in)
+        return -1;
+    for (int64_t s = 0; s < nseqs; ++s) {
+        const int32_t r = read_slot ? read_slot[s] : -1;
+        const int32_t w = write_slot ? write_slot[s] : -1;
+        if (r >= num_slots || w >= num_slots) {
+            bad = 1;
+            continue;
+        }
+        if (r >= 0)
+            memcpy(h_in + s * per_state, state_cache + (int64_t)r * per_state,
+                   (size_t)per_state * sizeof(double));
+    }
+    for (int64_t s = 0; s < nseqs; ++s) {
+        const int32_t r = read_slot ? read_slot[s] : -1;
+        const int32_t w = write_slot ? write_slot[s] : -1;
+        if (r >= num_slots || w >= num_slots)
+            continue;
+        for (int64_t hd = 0; hd < H; ++hd) {
+            const int64_t g = hd / (H / G);
+            const double delta = oracle_softplus(dt[s * H + hd] + (dt_bias ? dt_bias[hd] : 0.0));
+            const double decay = exp(delta * A[hd]);
+            const double *xs = x + (s * H + hd) * P;
+            const double *Bs = B + (s * G + g) * N;
+            const double *Cs = C + (s * G + g) * N;
+            double *hs = h_in + s * per_state + hd * P * N;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    hs[p * N + n] = decay * hs[p * N + n] + delta * xs[p] * Bs[n];
+                    acc += Cs[n] * hs[p * N + n];
+                }
+                y[(s * H + hd) * P + p] = acc + (D ? D[hd] : 0.0) * xs[p];
+            }
+        }
+        if (w >= 0)
+            memcpy(state_cache + (int64_t)w * per_state, h_in + s * per_state,
+                   (size_t)per_state * sizeof(double));
+    }
+    free(h_in);
+    return bad ? -2 : 0;
+}

@@ -159,3 +159,72 @@ def make_config(index: int, chunk_size: Optional[int] = None) -> Workload:
                        chunk_size or cfg["chunk_size"], dtype=cfg["dtype"],
                        init_seqs=cfg["init_seqs"], rng=rng, block_size=cfg.get("block_size"),
                        num_slots=cfg.get("num_slots"), name=cfg["name"])
+
+
+@dataclasses.dataclass
+class DecodeBatch:
+    """One decode token for each of `nseqs` sequences, with a state cache and
+    the read / write cache slot of every sequence (dual anchors)."""
+    x: torch.Tensor            # (S, H, P)
+    dt: torch.Tensor           # (S, H) float32, raw (before bias and softplus)
+    dt_bias: torch.Tensor      # (H,)
+    A: torch.Tensor            # (H,)
+    B: torch.Tensor            # (S, G, N)
+    C: torch.Tensor            # (S, G, N)
+    D: torch.Tensor            # (H,)
+    state_cache: torch.Tensor  # (num_slots, H, P, N) float32
+    read_slot: torch.Tensor    # (S,) int32, < 0: start from zero
+    write_slot: torch.Tensor   # (S,) int32, < 0: no write
+    dtype: str
+    name: str = ""
+
+    @property
+    def nseqs(self):
+        return self.x.shape[0]
+
+
+# Decode workload timed next to the prefill scan: the prefix-cache layer shape,
+# 256 sequences each reading one slot of a 512-slot cache and writing another.
+DECODE_CONFIG = dict(name="decode_dual_anchor_256x_h32p128n128g4", nseqs=256, nheads=32,
+                     headdim=128, dstate=128, ngroups=4, num_slots=512, dtype="bf16", seed=5)
+
+
+def make_decode_inputs(nseqs, nheads, headdim, dstate, ngroups, num_slots, dtype="f32", seed=0,
+                       anchors="dual", name=""):
+    """Draw one decode batch (same distributions as the prefill inputs; cache
+    states ~ N(0, 0.5^2)). Draw order: x -> dt -> dt_bias -> A -> B -> C -> D ->
+    cache -> slot permutation. anchors: "dual" (read and write slots all
+    distinct; needs num_slots >= 2 S), "inplace" (write slot = read slot), or
+    "mixed" (dual, with every fourth sequence in place, every seventh reading
+    no slot and every fifth writing none)."""
+    rng = np.random.default_rng(seed)
+    S, H, P, N, G = nseqs, nheads, headdim, dstate, ngroups
+    x = rng.standard_normal((S, H, P))
+    dt = rng.standard_normal((S, H))
+    dt_bias = rng.uniform(-4.0, -2.0, size=H)
+    A = -np.exp(rng.uniform(0.0, float(np.log(16.0)), size=H))
+    B = rng.standard_normal((S, G, N)) / np.sqrt(N)
+    C = rng.standard_normal((S, G, N)) / np.sqrt(N)
+    D = rng.standard_normal(H)
+    cache = rng.standard_normal((num_slots, H, P, N)).astype(np.float32) * np.float32(0.5)
+    perm = rng.permutation(num_slots).astype(np.int32)
+    if anchors == "inplace":
+        rs = perm[:S].copy()
+        ws = rs.copy()
+    else:
+        assert num_slots >= 2 * S, "dual anchors need two distinct slots per sequence"
+        rs, ws = perm[:S].copy(), perm[S:2 * S].copy()
+        if anchors == "mixed":
+            ws[::4] = rs[::4]
+            rs[3::7] = -1
+            ws[2::5] = -1
+    return DecodeBatch(x=_cast(x, dtype), dt=_cast(dt, "f32"), dt_bias=_cast(dt_bias, "f32"),
+                       A=_cast(A, "f32"), B=_cast(B, dtype), C=_cast(C, dtype), D=_cast(D, "f32"),
+                       state_cache=torch.from_numpy(cache), read_slot=torch.from_numpy(rs),
+                       write_slot=torch.from_numpy(ws), dtype=dtype, name=name)
+
+
+def make_decode_config() -> DecodeBatch:
+    c = DECODE_CONFIG
+    return make_decode_inputs(c["nseqs"], c["nheads"], c["headdim"], c["dstate"], c["ngroups"],
+                              c["num_slots"], dtype=c["dtype"], seed=c["seed"], name=c["name"])

@@ -12,7 +12,7 @@ import numpy as np
 
 import oracle
 from ssd_brute import chunked, semiseparable
-from selective_state_space_cu_amd.workloads import make_config, make_inputs
+from selective_state_space_cu_amd.workloads import make_config, make_decode_inputs, make_inputs
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -342,9 +342,144 @@ def pin_plan_scatter_equals_gather(lib):
         assert list(dst) == list(ref), f"trial {trial}"
 
 
+# ---- decode step with dual state anchors -------------------------------------
+
+def _decode(lib, b, cache=None, rs=None, ws=None, dt_bias=None, A=None):
+    return oracle.ssd_decode(b.x, b.dt, b.dt_bias if dt_bias is None else dt_bias,
+                             b.A if A is None else A, b.B, b.C, b.D,
+                             b.state_cache if cache is None else cache,
+                             b.read_slot if rs is None else rs, b.write_slot if ws is None else ws,
+                             lib=lib)
+
+
+def _decode_cases():
+    # (S, H, P, N, G, slots, anchors, seed)
+    return [(7, 4, 3, 2, 2, 16, "mixed", 21), (3, 2, 4, 5, 1, 6, "dual", 22),
+            (4, 6, 2, 3, 3, 4, "inplace", 23)]
+
+
+def pin_decode_is_one_recurrence_token(lib):
+    """A decode step equals the recurrence oracle over one-token sequences whose
+    initial states are the read slots (zero for none); the write slots then hold
+    its final states and every other slot is untouched."""
+    for S, H, P, N, G, slots, anchors, seed in _decode_cases():
+        b = make_decode_inputs(S, H, P, N, G, slots, anchors=anchors, seed=seed)
+        y, cache, rc = _decode(lib, b)
+        assert rc == 0, "decode refused valid slots"
+        rs, ws = b.read_slot.numpy(), b.write_slot.numpy()
+        c0 = b.state_cache.double().numpy()
+        init = np.where((rs >= 0)[:, None, None, None], c0[np.maximum(rs, 0)], 0.0)
+        yr, fr, _ = oracle.ssd_varlen(b.x, b.dt, b.dt_bias, b.A, b.B, b.C, b.D,
+                                      np.arange(S + 1, dtype=np.int32), init,
+                                      np.ones(S, np.int32), lib=lib)
+        _close(y, yr, 1e-12, f"decode y vs recurrence ({anchors})")
+        want = c0.copy()
+        for i in range(S):
+            if ws[i] >= 0:
+                want[ws[i]] = fr[i]
+        _close(cache, want, 1e-12, f"decode cache vs recurrence ({anchors})")
+        untouched = np.setdiff1d(np.arange(slots), ws[ws >= 0])
+        assert np.array_equal(cache[untouched], c0[untouched]), "decode wrote an unlisted slot"
+
+
+def pin_decode_limits(lib):
+    """dt_bias = -1e4 (delta = 0): the read state reaches the write slot bit for bit
+    and y = C.h + D x; A = -1e6 (decay underflows to 0): the new state is
+    delta x B^T alone and y = delta (C.B) x + D x."""
+    b = make_decode_inputs(4, 3, 4, 5, 1, 8, anchors="dual", seed=31)
+    rs, ws = b.read_slot.numpy(), b.write_slot.numpy()
+    x, B, C, D = (v.double().numpy() for v in (b.x, b.B, b.C, b.D))
+    c0 = b.state_cache.double().numpy()
+    y, cache, _ = _decode(lib, b, dt_bias=np.full(3, -1e4))
+    assert np.array_equal(cache[ws], c0[rs]), "delta = 0 changed the state"
+    for i in range(4):
+        yr = np.einsum("hpn,n->hp", c0[rs[i]], C[i, 0]) + D[:, None] * x[i]
+        _close(y[i], yr, 1e-12, "delta = 0 y")
+    delta = 0.75
+    u = math.log(math.expm1(delta))
+    y, cache, _ = oracle.ssd_decode(b.x, np.full((4, 3), u), np.zeros(3), np.full(3, -1e6), b.B,
+                                    b.C, b.D, b.state_cache, b.read_slot, b.write_slot, lib=lib)
+    for i in range(4):
+        _close(cache[ws[i]], delta * np.einsum("hp,n->hpn", x[i], B[i, 0]), 1e-12, "no-decay state")
+        yr = delta * float(C[i, 0] @ B[i, 0]) * x[i] + D[:, None] * x[i]
+        _close(y[i], yr, 1e-12, "no-decay y")
+
+
+def pin_decode_anchor_rules(lib):
+    """Read slot < 0 equals reading an all-zero slot; write slot < 0 leaves the
+    cache alone; in place (read == write) equals reading one slot and writing
+    another; a slot past the cache is refused (-2) and its sequence skipped."""
+    b = make_decode_inputs(5, 2, 3, 4, 2, 12, anchors="dual", seed=41)
+    rs, ws = b.read_slot.numpy().copy(), b.write_slot.numpy().copy()
+    c0 = b.state_cache.double().numpy()
+    y_ref, cache_ref, _ = _decode(lib, b)
+    zc = c0.copy()
+    zc[rs[1]] = 0.0
+    rs_none = rs.copy()
+    rs_none[1] = -1
+    y1, c1, _ = _decode(lib, b, rs=rs_none)
+    y2, c2, _ = _decode(lib, b, cache=zc)
+    assert np.array_equal(y1, y2) and np.array_equal(c1[ws], c2[ws]), "read < 0 is not a zero state"
+    ws_none = np.full_like(ws, -1)
+    y3, c3, _ = _decode(lib, b, ws=ws_none)
+    assert np.array_equal(c3, c0) and np.array_equal(y3, y_ref), "write < 0 wrote or changed y"
+    y4, c4, _ = _decode(lib, b, ws=rs)
+    assert np.array_equal(y4, y_ref) and np.array_equal(c4[rs], cache_ref[ws]), "in place differs"
+    bad = rs.copy()
+    bad[2] = 12
+    y5, c5, rc = _decode(lib, b, rs=bad)
+    assert rc == -2, "out-of-range slot accepted"
+    assert np.all(y5[2] == 0.0) and np.array_equal(c5[ws[2]], c0[ws[2]]), "bad sequence not skipped"
+    others = [0, 1, 3, 4]
+    assert np.array_equal(y5[others], y_ref[others]), "a bad slot disturbed other sequences"
+
+
+def pin_decode_continues_prefill(lib):
+    """Prefill of L tokens == prefill of L - 1 tokens whose final state sits in a
+    cache slot, then one decode step reading it (last y and final state, 1e-12);
+    and two decode steps chained through the cache (read a, write b; read b,
+    write c) == the recurrence over two tokens."""
+    L, H, P, N, G = 9, 4, 3, 5, 2
+    w = make_inputs([L, L + 3], H, P, N, G, 4, init_seqs=[0], seed=51)
+    y, fin, _ = _run(lib, w)
+    cu = w.cu_seqlens.numpy()
+    part = make_inputs([L - 1, L + 2], H, P, N, G, 4, init_seqs=[0], seed=51)
+    keep = np.concatenate([np.arange(cu[0], cu[1] - 1), np.arange(cu[1], cu[2] - 1)])
+    yp, fp, _ = oracle.ssd_varlen(w.x[keep], w.dt[keep], w.dt_bias, w.A, w.B[keep], w.C[keep], w.D,
+                                  part.cu_seqlens, w.initial_states, w.has_initial_state, lib=lib)
+    last = cu[1:] - 1
+    cache = np.zeros((6, H, P, N))
+    cache[[4, 1]] = fp
+    yd, cd, rc = oracle.ssd_decode(w.x[last], w.dt[last], w.dt_bias, w.A, w.B[last], w.C[last], w.D,
+                                   cache, np.array([4, 1], np.int32), np.array([0, 5], np.int32),
+                                   lib=lib)
+    assert rc == 0
+    _close(yd, y[last], 1e-12, "decode after prefill y")
+    _close(cd[[0, 5]], fin, 1e-12, "decode after prefill state")
+    _close(yp, y[keep], 1e-12, "prefill prefix y")
+    b = make_decode_inputs(6, 2, 3, 4, 1, 18, anchors="dual", seed=52)
+    b2 = make_decode_inputs(6, 2, 3, 4, 1, 18, anchors="dual", seed=53)
+    rs, ws = b.read_slot.numpy(), b.write_slot.numpy()
+    free = np.setdiff1d(np.arange(18), np.concatenate([rs, ws]))
+    ya, ca, _ = _decode(lib, b)
+    yb, cb, _ = oracle.ssd_decode(b2.x, b2.dt, b.dt_bias, b.A, b2.B, b2.C, b.D, ca, ws, free,
+                                  lib=lib)
+    xs = np.stack([b.x.double().numpy(), b2.x.double().numpy()], 1).reshape(12, 2, 3)
+    dts = np.stack([b.dt.double().numpy(), b2.dt.double().numpy()], 1).reshape(12, 2)
+    Bs = np.stack([b.B.double().numpy(), b2.B.double().numpy()], 1).reshape(12, 1, 4)
+    Cs = np.stack([b.C.double().numpy(), b2.C.double().numpy()], 1).reshape(12, 1, 4)
+    c0 = b.state_cache.double().numpy()
+    yr, fr, _ = oracle.ssd_varlen(xs, dts, b.dt_bias, b.A, Bs, Cs, b.D,
+                                  np.arange(0, 13, 2, dtype=np.int32), c0[rs], np.ones(6, np.int32),
+                                  lib=lib)
+    _close(np.stack([ya, yb], 1).reshape(12, 2, 3), yr, 1e-12, "two chained decode steps y")
+    _close(cb[free], fr, 1e-12, "two chained decode steps state")
+
+
 ALL_PINS = [pin_brute_force_semiseparable, pin_scalar_closed_form, pin_linear_attention,
             pin_diagonal_limit, pin_zero_dt, pin_superposition, pin_no_leakage,
             pin_chunked_decomposition, pin_initial_state_decay, pin_768_token_chunk128,
             pin_metadata_enumeration, pin_metadata_golden_tiny,
             pin_plan_prefix_cache_closed_form, pin_plan_misaligned_and_resume,
-            pin_plan_scatter_equals_gather]
+            pin_plan_scatter_equals_gather, pin_decode_is_one_recurrence_token,
+            pin_decode_limits, pin_decode_anchor_rules, pin_decode_continues_prefill]

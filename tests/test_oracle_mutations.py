@@ -32,6 +32,19 @@ MUTATIONS = [
     ("plan_no_alignment_skip", [("if (ncomp % chunk_size == 0) {", "if (1) {")]),
     ("plan_no_final_block", [("ckpt_src[s * max_blocks + last] = (int32_t)hi;", "")]),
     ("order_tie_break", [("(lu == lv && u < v)", "(lu == lv && u > v)")]),
+    # the decode step with dual state anchors
+    ("decode_drop_decay", [("hs[p * N + n] = decay * hs[p * N + n] + delta * xs[p] * Bs[n];",
+                            "hs[p * N + n] = hs[p * N + n] + delta * xs[p] * Bs[n];")]),
+    ("decode_y_from_entering_state", [(
+        "hs[p * N + n] = decay * hs[p * N + n] + delta * xs[p] * Bs[n];\n                    acc += Cs[n] * hs[p * N + n];",
+        "acc += Cs[n] * hs[p * N + n];\n                    hs[p * N + n] = decay * hs[p * N + n] + delta * xs[p] * Bs[n];")]),
+    ("decode_read_slot_ignored", [("if (r >= 0)\n            memcpy(h_in", "if (0)\n            memcpy(h_in")]),
+    ("decode_writes_read_anchor", [("memcpy(state_cache + (int64_t)w * per_state",
+                                    "memcpy(state_cache + (int64_t)(r >= 0 ? r : w) * per_state")]),
+    ("decode_wrong_group", [("const int64_t g = hd / (H / G);", "const int64_t g = hd % G;")]),
+    ("decode_no_bias", [("dt[s * H + hd] + (dt_bias ? dt_bias[hd] : 0.0)", "dt[s * H + hd]")]),
+    ("decode_drop_D", [("(D ? D[hd] : 0.0) * xs[p]", "0.0 * xs[p]")]),
+    ("decode_bad_slot_not_refused", [("            bad = 1;", "            bad = 0;")]),
 ]
 
 
