@@ -112,6 +112,96 @@ def cpu_baseline(w, heads):
                        f"{dt_s:.2f} s wall; value scaled to whole-workload tokens/s")
 
 
+def decode_work(b):
+    """Algorithmic bytes of one decode step: every read slot read once, every
+    write slot written once (float32 states), x, dt, B, C read and y written once."""
+    S, H, P = b.x.shape
+    G, N = b.B.shape[1], b.B.shape[2]
+    sx = 2 if b.dtype == "bf16" else 4
+    state = H * P * N * 4
+    n_read = int((b.read_slot >= 0).sum())
+    n_write = int((b.write_slot >= 0).sum())
+    return (n_read + n_write) * state + S * (2 * H * P * sx + 4 * H + 2 * G * N * sx)
+
+
+def bench_decode(args):
+    """One JSON line for the decode step (dual anchors) on the decode batch."""
+    import torch
+    from selective_state_space_cu_amd import ssd
+    from selective_state_space_cu_amd.workloads import DECODE_CONFIG, make_decode_config
+
+    b = make_decode_config()
+    dev = torch.device("cuda:0")
+    d = {k: getattr(b, k).to(dev).contiguous() for k in
+         ("x", "dt", "dt_bias", "A", "B", "C", "D", "state_cache", "read_slot", "write_slot")}
+    y = torch.empty_like(d["x"])
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev = []
+
+    def step(timed):
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        ssd.decode_step(d["x"], d["dt"], d["A"], d["B"], d["C"], d["state_cache"], d["read_slot"],
+                        d["write_slot"], dt_bias=d["dt_bias"], D=d["D"], y=y, error_flag=flag)
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    if int(flag.item()) != 0:
+        raise RuntimeError("device error flag set")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = sum(a.elapsed_time(e) for a, e in ev) / len(ev)
+    alg = decode_work(b)
+    ms_per_step = wall * 1e3 / args.steps
+    out = {
+        "metric": "SSD decode step (dual state anchors) tokens/s on 1 MI355X; % of HBM roofline",
+        "value": b.nseqs / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype,
+        "data": "synthetic (seeded; inputs and state cache resident in HBM)",
+        "config": {"workload": DECODE_CONFIG["name"], "nseqs": b.nseqs,
+                   "nheads": DECODE_CONFIG["nheads"], "headdim": DECODE_CONFIG["headdim"],
+                   "dstate": DECODE_CONFIG["dstate"], "ngroups": DECODE_CONFIG["ngroups"],
+                   "num_slots": DECODE_CONFIG["num_slots"],
+                   "step": "one token per sequence: read slot -> state update -> write slot"},
+        "roofline": {"bound": "hbm", "kernel": "ssd_decode_kernel",
+                     "achieved": alg / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": alg, "kernel_ms": k_ms},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(b)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_decode(b, nseqs=64):
+    """The float64 decode oracle on the host cores over the first `nseqs`
+    sequences, their read slots gathered into a small cache."""
+    import numpy as np
+    import oracle
+    rs = b.read_slot.numpy()[:nseqs]
+    small = b.state_cache.numpy()[np.maximum(rs, 0)]
+    t = time.perf_counter()
+    oracle.ssd_decode(b.x[:nseqs], b.dt[:nseqs], b.dt_bias, b.A, b.B[:nseqs], b.C[:nseqs], b.D,
+                      small, np.where(rs >= 0, np.arange(nseqs), -1).astype(np.int32),
+                      np.arange(nseqs, dtype=np.int32))
+    dt_s = time.perf_counter() - t
+    return dict(value=nseqs / dt_s, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {nseqs} of {b.nseqs} sequences (all heads), float64, single thread "
+                       f"(the decode oracle is not threaded); {dt_s:.2f} s wall including the "
+                       f"float64 widening of their {nseqs} state slots")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +212,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--workload", choices=("prefill", "decode"), default="prefill",
+                    help="prefill (default): the scan step; decode: one dual-anchor decode step "
+                         "per sequence on the 256-sequence decode batch")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from two rocprofv3 counter CSVs and exit "
                          "(with --copy-calib-mib giving the calibration size)")
@@ -135,6 +228,9 @@ def main():
               "(see DESIGN.md for how the scan would shard)", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "decode":
+        bench_decode(args)
+        return
     import torch
     from selective_state_space_cu_amd import ssd
     from selective_state_space_cu_amd.workloads import CONFIGS, make_config

@@ -183,6 +183,43 @@ ssd_status ssd_export_chunk_states(
     const float *chunk_states, int32_t state_elems, float *state_cache, int32_t num_slots,
     void *stream);
 
+/*
+ * One decode step with dual state anchors (the decode kernels' read/write
+ * anchor split on the prefix-caching page: a step reads the running state from
+ * the previous step's anchor slot and writes to the current one, so a cached
+ * block checkpoint is never overwritten in place). One new token per sequence:
+ *     S     = state_cache[read_slot[s], h]     (zero when read_slot[s] < 0)
+ *     delta = softplus(dt[s,h] + dt_bias[h])
+ *     S'    = exp(delta * A[h]) * S + delta * x[s,h] (outer) B[s,g]
+ *     y[s,h] = S' . C[s,g] + D[h] * x[s,h]
+ *     state_cache[write_slot[s], h] = S'       (skipped when write_slot[s] < 0)
+ * with g = h / (nheads / ngroups): the same recurrence as the scan, one token.
+ *
+ *  x, B, C, y      element type `in_dtype`; x, y (nseqs, H, P); B, C (nseqs, G, N)
+ *  dt              float32 (nseqs, H), raw; dt_bias, D float32 (H) or NULL (= 0)
+ *  A               float32 (H)
+ *  state_cache     float32 (num_slots, H, P, N), 16-byte aligned, updated in place
+ *  read_slot,      int32 (nseqs) device arrays. read_slot[s] == write_slot[s]
+ *  write_slot      is an in-place update. Write slots must be unique and must
+ *                  not be another sequence's read slot (else unspecified).
+ *  error_flag      int32 [1] device sticky flag, or NULL. A slot >= num_slots
+ *                  sets SSD_DATA_BAD_SLOT; that sequence is skipped entirely
+ *                  (no y, no state written).
+ * Supported: dstate in {16, 32, 64, 128, 256}, any headdim >= 1.
+ * Precision: float32 state and arithmetic (hardware exp2/log2); y rounded to
+ * x's type (round to nearest even for bf16).
+ * Errors (returned before any launch): SSD_ERR_DTYPE, SSD_ERR_SHAPE (sizes,
+ * nheads % ngroups, unaligned state_cache), SSD_ERR_UNSUPPORTED (dstate),
+ * SSD_ERR_NULL_ARG; SSD_ERR_HIP on a failed launch. Asynchronous on `stream`;
+ * the caller owns every buffer.
+ */
+ssd_status ssd_decode_step(
+    const void *x, const float *dt, const float *dt_bias, const float *A, const void *B,
+    const void *C, const float *D, ssd_dtype in_dtype, int32_t nseqs, int32_t nheads,
+    int32_t headdim, int32_t dstate, int32_t ngroups, float *state_cache, int32_t num_slots,
+    const int32_t *read_slot, const int32_t *write_slot, void *y, int32_t *error_flag,
+    void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -133,4 +133,31 @@ ssd_status ssd_export_chunk_states(const ssd_varlen_meta *meta, const int32_t *n
     return ssd::launch_plan(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
+ssd_status ssd_decode_step(const void *x, const float *dt, const float *dt_bias, const float *A,
+                           const void *B, const void *C, const float *D, ssd_dtype in_dtype,
+                           int32_t nseqs, int32_t nheads, int32_t headdim, int32_t dstate,
+                           int32_t ngroups, float *state_cache, int32_t num_slots,
+                           const int32_t *read_slot, const int32_t *write_slot, void *y,
+                           int32_t *error_flag, void *stream) {
+    if (in_dtype != SSD_F32 && in_dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    if (nseqs < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        nheads % ngroups != 0 || num_slots < 0)
+        return SSD_ERR_SHAPE;
+    if (!(dstate == 16 || dstate == 32 || dstate == 64 || dstate == 128 || dstate == 256))
+        return SSD_ERR_UNSUPPORTED;
+    if (A == nullptr) return SSD_ERR_NULL_ARG;
+    if (nseqs > 0 && (x == nullptr || dt == nullptr || B == nullptr || C == nullptr || y == nullptr ||
+                      state_cache == nullptr || read_slot == nullptr || write_slot == nullptr))
+        return SSD_ERR_NULL_ARG;
+    if (state_cache != nullptr && !aligned16(state_cache)) return SSD_ERR_SHAPE;
+    ssd::DecodeArgs a{};
+    a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
+    a.cache = state_cache; a.read_slot = read_slot; a.write_slot = write_slot; a.y = y;
+    a.error_flag = error_flag;
+    a.S = nseqs; a.H = nheads; a.P = headdim; a.G = ngroups; a.num_slots = num_slots;
+    a.pchunks = ssd::decode_pchunks(headdim, dstate);
+    return ssd::launch_decode(a, in_dtype == SSD_BF16, dstate, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SSD_OK : SSD_ERR_HIP;
+}
+
 }  // extern "C"

@@ -54,6 +54,23 @@ hipError_t launch_scan_f32(const ScanArgs &a, int waves, int dstate, hipStream_t
 // Split-state bf16 scan (eight waves per 64 headdim columns; dstate 128).
 hipError_t launch_scan_split_bf16(const ScanArgs &a, int dstate, hipStream_t stream);
 
+// Decode step with dual state anchors (one token per sequence).
+struct DecodeArgs {
+    const void *x;            // (S, H, P) bf16 or f32
+    const float *dt;          // (S, H)
+    const float *dt_bias;     // nullable
+    const float *A;
+    const void *B, *C;        // (S, G, N)
+    const float *D;           // nullable
+    float *cache;             // (num_slots, H, P, N)
+    const int32_t *read_slot, *write_slot;   // (S)
+    void *y;                  // (S, H, P)
+    int32_t *error_flag;      // nullable
+    int32_t S, H, P, G, num_slots, pchunks;
+};
+int32_t decode_pchunks(int32_t headdim, int32_t dstate);   // workgroups per (sequence, head)
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, int dstate, hipStream_t stream);
+
 struct MetaArgs {
     const int32_t *cu_seqlens;
     int32_t *chunk_offsets, *chunk_seq_idx, *seq_chunk_start, *nchunks, *seq_order, *error_flag;

@@ -21,7 +21,7 @@ DATA_BAD_CU_SEQLENS, DATA_TOO_MANY_CHUNKS, DATA_BAD_SLOT, DATA_BAD_BLOCK = 1, 2,
 
 # names exported by libssd.so (checked by the CPU tests against include/ssd.h)
 EXPORTS = ("ssd_varlen_metadata", "ssd_chunk_scan_varlen", "ssd_export_chunk_states",
-           "ssd_status_string")
+           "ssd_decode_step", "ssd_status_string")
 
 
 class SSDError(RuntimeError):
@@ -64,6 +64,9 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_export_chunk_states.restype = st
     lib.ssd_export_chunk_states.argtypes = [ctypes.POINTER(_Meta), vp, vp, i32, i32, vp, vp, vp,
                                             i32, vp, i32, vp]
+    lib.ssd_decode_step.restype = st
+    lib.ssd_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, st, i32, i32, i32, i32, i32, vp, i32,
+                                    vp, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -233,3 +236,39 @@ def export_chunk_states(meta: VarlenMeta, block_table: torch.Tensor, block_size:
         ctypes.byref(m), _ptr(ncomp), _ptr(bt), maxb, int(block_size), _ptr(ckpt_src), _ptr(dst),
         _ptr(chunk_states), state_elems, _ptr(state_cache), int(num_slots or 0), _stream(device)))
     return ckpt_src, dst[: meta.max_chunks]
+
+
+def decode_step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                C: torch.Tensor, state_cache: torch.Tensor, read_slot: torch.Tensor,
+                write_slot: torch.Tensor, dt_bias: Optional[torch.Tensor] = None,
+                D: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                error_flag: Optional[torch.Tensor] = None):
+    """ssd_decode_step: one token per sequence, state read from
+    state_cache[read_slot[s]] (zero if < 0) and written to
+    state_cache[write_slot[s]] (skipped if < 0). x (S,H,P), dt (S,H), A (H,),
+    B/C (S,G,N), state_cache float32 (slots,H,P,N). Returns y (S,H,P)."""
+    lib = load_library()
+    device = x.device
+    S, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    _data(x, "x", device)
+    dtype = x.dtype
+    for name, t in (("B", B), ("C", C)):
+        _data(t, name, device, dtype)
+    _data(dt, "dt", device, torch.float32)
+    _data(A, "A", device, torch.float32)
+    _data(state_cache, "state_cache", device, torch.float32)
+    for name, t in (("dt_bias", dt_bias), ("D", D)):
+        if t is not None:
+            _data(t, name, device, torch.float32)
+    if y is None:
+        y = torch.empty_like(x)
+    _data(y, "y", device, dtype)
+    rs, ws = _index(read_slot, device), _index(write_slot, device)
+    if error_flag is not None:
+        _data(error_flag, "error_flag", device, torch.int32)
+    _check("ssd_decode_step", lib.ssd_decode_step(
+        _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _dtype_code(x),
+        S, H, P, N, G, _ptr(state_cache), state_cache.shape[0], _ptr(rs), _ptr(ws), _ptr(y),
+        _ptr(error_flag), _stream(device)))
+    return y

@@ -106,3 +106,27 @@ def test_export_argument_errors():
     assert call(cst=FAKE, cache=None) == 1
     assert call(cst=FAKE, cache=FAKE, elems=6) == 3
     assert call(maxb=-1) == 3
+
+
+def _decode(**kw):
+    args = dict(x=FAKE, dt=FAKE, dt_bias=None, A=FAKE, B=FAKE, C=FAKE, D=None, dtype=1, S=4, H=4,
+                P=64, N=128, G=2, cache=FAKE, slots=8, rs=FAKE, ws=FAKE, y=FAKE, flag=None)
+    args.update(kw)
+    lib = ssd.load_library()
+    return lib.ssd_decode_step(args["x"], args["dt"], args["dt_bias"], args["A"], args["B"],
+                               args["C"], args["D"], args["dtype"], args["S"], args["H"],
+                               args["P"], args["N"], args["G"], args["cache"], args["slots"],
+                               args["rs"], args["ws"], args["y"], args["flag"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 6), (dict(G=3), 3), (dict(H=0), 3), (dict(S=-1), 3), (dict(slots=-1), 3),
+    (dict(N=48), 8), (dict(N=512), 8), (dict(x=None), 1), (dict(rs=None), 1), (dict(ws=None), 1),
+    (dict(cache=None), 1), (dict(A=None), 1), (dict(cache=FAKE + 4), 3),
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_empty_batch_launches_nothing():
+    assert _decode(S=0, x=None, dt=None, B=None, C=None, y=None, cache=None, rs=None, ws=None) == 0
