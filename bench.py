@@ -24,23 +24,28 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "scan_prefix_cache_4x8894_counters.json")
+DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_dual_anchor_256_counters.json")
 KERNEL_SOURCES = ["ssd_scan.hpp", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_internal.h",
                   "ssd_scan_split.hpp", "ssd_scan_split_bf16.hip"]
+DECODE_SOURCES = ["ssd_decode.hip", "ssd_scan.hpp", "ssd_internal.h"]
 
 
-def kernel_hash():
+def kernel_hash(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "selective_state_space_cu_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def ingest_counters(fetch_csv, write_csv, config, calib_mib, out=COUNTERS):
+def ingest_counters(fetch_csv, write_csv, config, calib_mib, workload="prefill"):
     """Turn two rocprofv3 --pmc runs of `bench.py --copy-calib-mib M` (FETCH_SIZE,
-    then WRITE_SIZE; KiB per dispatch) into the HBM traffic of one scan launch,
-    each counter scaled by what it reads for the calibration kernel (one
-    elementwise pass that reads and writes M MiB)."""
+    then WRITE_SIZE; KiB per dispatch) into the HBM traffic of one launch of the
+    workload's kernel, each counter scaled by what it reads for the calibration
+    kernel (one elementwise pass that reads and writes M MiB)."""
+    decode = workload == "decode"
+    out = DECODE_COUNTERS if decode else COUNTERS
+    tag = "ssd_decode" if decode else "ssd_scan"
     import csv
 
     def per_kernel(path):
@@ -50,15 +55,17 @@ def ingest_counters(fetch_csv, write_csv, config, calib_mib, out=COUNTERS):
         return vals
 
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
-    scan_f = [v for k, v in fetch.items() if "ssd_scan" in k][0]
-    scan_w = [v for k, v in write.items() if "ssd_scan" in k][0]
+    scan_f = [v for k, v in fetch.items() if tag in k][0]
+    scan_w = [v for k, v in write.items() if tag in k][0]
     calib_kib = calib_mib * 1024.0
     # calibration dispatch: the elementwise kernel with the largest reading (the add)
     cal_f = max(x for k, v in fetch.items() if "elementwise" in k for x in v)
     cal_w = max(x for k, v in write.items() if "elementwise" in k for x in v)
     ff, fw = calib_kib / cal_f, calib_kib / cal_w
     fk, wk = sum(scan_f) / len(scan_f), sum(scan_w) / len(scan_w)
-    rec = {"kernel": scan_kernel_name(config), "kernel_hash": kernel_hash(), "config": config,
+    rec = {"kernel": "ssd_decode_kernel" if decode else scan_kernel_name(config),
+           "kernel_hash": kernel_hash(DECODE_SOURCES if decode else KERNEL_SOURCES),
+           "config": "decode" if decode else config,
            "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": len(scan_f),
            "calibration_mib": calib_mib, "calibration_fetch_kib": cal_f, "calibration_write_kib": cal_w,
            "fetch_scale": ff, "write_scale": fw,
@@ -112,6 +119,18 @@ def cpu_baseline(w, heads):
                        f"{dt_s:.2f} s wall; value scaled to whole-workload tokens/s")
 
 
+def calib_copy(mib, dev):
+    """One plain elementwise kernel that reads and writes `mib` MiB each (the
+    scale for the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dstb = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.add(src, 1.0, out=dstb)
+    torch.cuda.synchronize()
+
+
 def decode_work(b):
     """Algorithmic bytes of one decode step: every read slot read once, every
     write slot written once (float32 states), x, dt, B, C read and y written once."""
@@ -160,7 +179,15 @@ def bench_decode(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     k_ms = sum(a.elapsed_time(e) for a, e in ev) / len(ev)
+    if args.copy_calib_mib:
+        calib_copy(args.copy_calib_mib, dev)
     alg = decode_work(b)
+    traffic = None
+    if os.path.exists(DECODE_COUNTERS):
+        with open(DECODE_COUNTERS) as f:
+            c = json.load(f)
+        if c.get("kernel_hash") == kernel_hash(DECODE_SOURCES):
+            traffic = c["hbm_bytes_per_launch"]
     ms_per_step = wall * 1e3 / args.steps
     out = {
         "metric": "SSD decode step (dual state anchors) tokens/s on 1 MI355X; % of HBM roofline",
@@ -175,7 +202,7 @@ def bench_decode(args):
                    "step": "one token per sequence: read slot -> state update -> write slot"},
         "roofline": {"bound": "hbm", "kernel": "ssd_decode_kernel",
                      "achieved": alg / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": alg, "kernel_ms": k_ms},
         "cpu_baseline": None,
     }
@@ -221,7 +248,8 @@ def main():
     args = ap.parse_args()
     if args.ingest_counters:
         print(json.dumps(ingest_counters(*args.ingest_counters, config=args.config,
-                                         calib_mib=args.copy_calib_mib or 512)))
+                                         calib_mib=args.copy_calib_mib or 512,
+                                         workload=args.workload)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -282,14 +310,7 @@ def main():
     scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
 
     if args.copy_calib_mib:
-        # one plain elementwise kernel that reads and writes copy_calib_mib MiB each
-        # (the scale for the FETCH_SIZE / WRITE_SIZE counters)
-        n = args.copy_calib_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dstb = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.add(src, 1.0, out=dstb)
-        torch.cuda.synchronize()
+        calib_copy(args.copy_calib_mib, dev)
 
     n_ckpt = 0
     if has_blocks:
