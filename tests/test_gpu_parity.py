@@ -285,3 +285,22 @@ def test_scan_bit_deterministic():
     assert torch.equal(f1, f2)
     n = c1.shape[0]
     assert torch.equal(torch.nan_to_num(c1[:n], nan=-1.0), torch.nan_to_num(c2[:n], nan=-1.0))
+
+
+@pytest.mark.parametrize("dtype,P,N", [("bf16", 64, 128), ("f32", 32, 64)])
+def test_all_sequences_empty(dtype, P, N):
+    """T = 0 with three sequences: no y, each final state is its initial state (or
+    zero), the chunk grid is empty."""
+    w = make_inputs([0, 0, 0], 4, P, N, 2, 64, dtype=dtype, init_seqs=[0, 2], seed=7)
+    log(f"empty batch {dtype} P={P} N={N}")
+    meta, y, fin, _ = gpu_run(w)
+    assert y.shape[0] == 0 and int(meta.nchunks.item()) == 0 and int(meta.error_flag.item()) == 0
+    _, fr, _ = oracle_run(w)
+    check_close(fin, fr, TOL[dtype], "empty batch final states")
+    assert torch.count_nonzero(fin[1]).item() == 0
+
+
+def test_no_sequences():
+    w = make_inputs([], 2, 64, 128, 1, 64, dtype="bf16", seed=8)
+    meta, y, fin, _ = gpu_run(w)
+    assert y.shape[0] == 0 and fin.shape[0] == 0 and int(meta.nchunks.item()) == 0
