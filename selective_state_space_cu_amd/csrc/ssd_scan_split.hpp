@@ -493,12 +493,24 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         }
         axf[hi] = lds_addr(sX) + r * RX + 16 * ((2 * pb + ((q >> 1) & 1)) ^ SH::swz128(r)) + 8 * (q & 1);
     }
+    // Held as whole per-lane addresses: left visible, the compiler factors them
+    // into shared row and swizzle parts and re-adds those in every step.
+#pragma unroll
+    for (int c = 0; c < NKH; ++c) {
+        asm volatile("" : "+v"(ac_o[c]), "+v"(ac_p[c]), "+v"(ab_o[c]), "+v"(ab_p[c]));
+    }
+#pragma unroll
+    for (int u = 0; u < NTH; ++u) asm volatile("" : "+v"(abt[u][0]), "+v"(abt[u][1]));
     int nexp = 0;           // checkpoint exports among the last two steps
     int ex1 = 0;            // did the previous step export
     // the x . w pass: lane 64 wave + lane scales one 16-byte chunk (8 headdim
     // columns of token row xw_row) of the swizzled x tile, in place of layout
     const int xw_row = (64 * wave + lane) >> 3;
     const uint32_t xw_off = xw_row * RX + 16 * (lane & 7);
+    // (whole addresses, so that the stage offsets fit the LDS instructions' immediates)
+    uint32_t xw_src = lds_addr(sX) + xw_off, xw_dst = lds_addr(sXW) + xw_off;
+    uint32_t axw[2] = {axf[0] - lds_addr(sX) + lds_addr(sXW), axf[1] - lds_addr(sX) + lds_addr(sXW)};
+    asm volatile("" : "+v"(xw_src), "+v"(xw_dst), "+v"(axw[0]), "+v"(axw[1]));
     // checkpoint staging: 4 state rows x 256 bytes per round, chunk m of row
     // i at m ^ i; round r holds the lanes' rows q = 4 r .. 4 r + 3, and its
     // store reads row lane / 16, chunk lane mod 16
@@ -566,15 +578,18 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         // (3) x . w of this tile, once per workgroup, for the state update
         // after the next barrier: w_j = delta_j 2^(s_last - s_j) per token row
         {
-            const u32x4 xv = *(const lds_u32x4 *)(uintptr_t)(lds_addr(sX) + OX + xw_off);
+            const u32x4 xv = *(const lds_u32x4 *)(uintptr_t)(xw_src + OX);
             const float wr = tW[xw_row];
             u32x4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = pack_bf16(bf16_lo(xv[i]) * wr, bf16_hi(xv[i]) * wr);
-            *(lds_u32x4 *)(uintptr_t)(lds_addr(sXW) + xw_off) = o;
+            *(lds_u32x4 *)(uintptr_t)xw_dst = o;
         }
 
         // (6) inter-chunk term Y^T = h_in . C^T over all n, then scale column i by 2^(s_i)
+        // (raised wave priority while the matrix products issue: of the two waves
+        // on a SIMD, the one feeding the matrix core goes first)
+        __builtin_amdgcn_s_setprio(1);
         f32x4 acc[2];
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
@@ -602,6 +617,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             for (int r = 0; r < 4; ++r) v[r] = fmaf(cb[r], fdec[d][r], dadd[d][r]);
             O::mstore4(sM + (r0 + 16 * d + q) * MPB + (16 * pb + 4 * g) * 2, v);
         }
+        __builtin_amdgcn_s_setprio(0);
 
         // B and C of tile t + NST - 1 into stage FETCH, once this wave's reads
         // of its C blocks there (the partner's state half) have completed
@@ -623,19 +639,20 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 xf[ks] = tr2(axf[0] + OX + 32 * RX * ks, axf[1] + OX + 32 * RX * ks);
-                xw[ks] = tr2(axf[0] - lds_addr(sX) + lds_addr(sXW) + 32 * RX * ks,
-                             axf[1] - lds_addr(sX) + lds_addr(sXW) + 32 * RX * ks);
+                xw[ks] = tr2(axw[0] + 32 * RX * ks, axw[1] + 32 * RX * ks);
 #pragma unroll
                 for (int u = 0; u < NTH; ++u) bt[ks][u] = tr2(abt[u][0] + OB + 32 * RB * ks, abt[u][1] + OB + 32 * RB * ks);
             }
             decay_of(tabs + NEXT * TAB);   // of the next tile (its tables are visible since the last barrier)
             const float e = fast_exp2(sL);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int u = 0; u < NTH; ++u) st[u] *= e;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int u = 0; u < NTH; ++u) st[u] = O::mma(st[u], bt[ks][u], xw[ks]);
+            __builtin_amdgcn_s_setprio(0);
         }
         // this wave's half of h_out for the partner, into stage SLOT's C blocks
         make_own();
