@@ -83,6 +83,12 @@ __device__ __forceinline__ void dma4_at(const u32x4 &r0, uint32_t lds_base, int 
 // A 16-byte buffer load into registers that the compiler does not track (like
 // the direct-to-LDS loads): the caller waits for it with an explicit vmcnt and
 // then passes the value through reg_fence, so that no use moves above the wait.
+// The compiler takes the destination as written at once, so on EVERY path from
+// the load the value must stay live until a wait covers it: a path on which it
+// is dead (an early return, a skipped store) lets the compiler give those
+// registers to other values, which the late load then overwrites. The CPU
+// tests check the compiled code for this (first touch of the registers on
+// every path is their LDS store, or a vmcnt(0) wait comes first).
 template <int OFF>
 __device__ __forceinline__ void load16_untracked(u32x4 &dst, const u32x4 &r0, int voff) {
     const u32x4 r = sgpr4(r0);

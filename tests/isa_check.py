@@ -1,0 +1,82 @@
+"""Checks of compiled gfx950 code for the split-state scan (CPU only).
+
+The scan loads x into registers with inline-assembly buffer loads that the
+compiler does not track: it takes their destination registers as written at
+once, waits for them only through the kernel's own explicit vmcnt waits, and
+may hand a register it believes dead to another value while the load is still
+in flight (the late load then overwrites that value). The invariant checked
+here on the compiled code: on every control-flow path from such a load, the
+first instruction that touches its destination registers is the store of
+those registers into their LDS stage (which the kernel places after the wait
+that covers the load), unless an `s_waitcnt vmcnt(0)` comes first.
+"""
+import os
+import re
+import subprocess
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "selective_state_space_cu_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def compile_asm(src, out, defines=()):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", f"-I{os.path.join(ROOT, 'include')}",
+           *[f"-D{d}" for d in defines], "--cuda-device-only", "-S", src, "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out
+
+
+def _vregs(line):
+    line = line.split(";")[0]
+    out = set()
+    for a, b in re.findall(r"\bv\[(\d+):(\d+)\]", line):
+        out |= set(range(int(a), int(b) + 1))
+    out |= {int(a) for a in re.findall(r"\bv(\d+)\b", line)}
+    return out
+
+
+def untracked_load_violations(asm_text):
+    """(load line, path description) for every path that touches an untracked
+    load's registers before its stage store or a vmcnt(0) wait; and the number
+    of untracked loads found."""
+    lines = asm_text.split("\n")
+    labels = {}
+    for i, l in enumerate(lines):
+        m = re.match(r"^(\.LBB\d+_\d+):", l)
+        if m:
+            labels[m.group(1)] = i
+    bad, count = [], 0
+    for i, l in enumerate(lines):
+        s = l.strip()
+        if not (s.startswith("buffer_load_dwordx4") and " lds" not in s and " offen" in s):
+            continue
+        m = re.search(r"v\[(\d+):(\d+)\]", s)
+        a, b = int(m.group(1)), int(m.group(2))
+        dst, tag = set(range(a, b + 1)), f"v[{a}:{b}]"
+        count += 1
+        stack, seen = [i + 1], set()
+        while stack:
+            j = stack.pop()
+            while j < len(lines):
+                if j in seen:
+                    break
+                seen.add(j)
+                t = lines[j].strip()
+                j += 1
+                if not t or t.startswith(";") or t.startswith("."):
+                    continue
+                if t.startswith("s_endpgm"):
+                    break
+                if t.startswith("s_waitcnt") and "vmcnt(0)" in t:
+                    break
+                if t.startswith("ds_write_b128") and tag in t:
+                    break
+                if _vregs(t) & dst:
+                    bad.append((i + 1, f"line {j}: {t}"))
+                    break
+                if t.startswith("s_branch"):
+                    j = labels[t.split()[-1]]
+                elif t.startswith("s_cbranch"):
+                    stack.append(labels[t.split()[-1]])
+    return bad, count
