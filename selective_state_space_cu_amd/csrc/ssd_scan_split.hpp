@@ -59,7 +59,8 @@
 namespace ssd {
 
 // Direct-to-LDS loads with the LDS address as an SGPR base plus a compile-time
-// offset (m0 = base + OFF), so that per-stage addresses need no extra registers.
+// offset (m0 = base + OFF), so that per-stage addresses need no extra registers;
+// one wait state between the M0 write and the load (the gfx9 M0 / LDS-DMA hazard).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // A wave-uniform resource quad as SGPRs (the asm operands below need them;
@@ -71,13 +72,13 @@ __device__ __forceinline__ u32x4 sgpr4(const u32x4 &r) {
 template <int OFF>
 __device__ __forceinline__ void dma16_at(const u32x4 &r0, uint32_t lds_base, int voff) {
     const u32x4 r = sgpr4(r0);
-    asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF) : "memory", "m0", "scc");
 }
 template <int OFF>
 __device__ __forceinline__ void dma4_at(const u32x4 &r0, uint32_t lds_base, int voff) {
     const u32x4 r = sgpr4(r0);
-    asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dword %0, %1, 0 offen lds"
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF) : "memory", "m0", "scc");
 }
 // A 16-byte buffer load into registers that the compiler does not track (like

@@ -80,3 +80,23 @@ def untracked_load_violations(asm_text):
                 elif t.startswith("s_cbranch"):
                     stack.append(labels[t.split()[-1]])
     return bad, count
+
+
+def m0_lds_dma_hazards(asm_text):
+    """Direct-to-LDS loads (`... lds`) whose previous instruction writes M0.
+
+    gfx9 parts need one wait state between a scalar write of M0 and an LDS-DMA
+    load that reads it; without it the load may use the previous M0 (its data
+    then lands on the previous block's LDS address). Returns (line, text) of
+    each offending load and the number of LDS-DMA loads seen."""
+    prev, bad, count = None, [], 0
+    for i, l in enumerate(asm_text.split("\n")):
+        t = l.strip()
+        if not t or t.startswith(";") or t.startswith(".") or t.endswith(":"):
+            continue
+        if t.startswith("buffer_load") and t.endswith(" lds"):
+            count += 1
+            if prev is not None and re.match(r"^s_\w+\s+m0\b", prev):
+                bad.append((i + 1, t))
+        prev = t
+    return bad, count

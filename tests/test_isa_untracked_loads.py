@@ -1,11 +1,12 @@
-"""The split-state scan's untracked register loads of x are never overwritten
-or reused before their wait, on any path of the compiled gfx950 code (CPU)."""
+"""Checks of the compiled gfx950 scan kernels (CPU): the split-state scan's
+untracked register loads of x are never overwritten or reused before their
+wait, on any path; and no direct-to-LDS load directly follows a write of M0."""
 import os
 import shutil
 
 import pytest
 
-from isa_check import CSRC, HIPCC, compile_asm, untracked_load_violations
+from isa_check import CSRC, HIPCC, compile_asm, m0_lds_dma_hazards, untracked_load_violations
 
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None,
                                 reason="hipcc not available")
@@ -37,3 +38,19 @@ def test_checker_flags_a_reused_register():
         "\tds_write_b128 v9, v[4:7]",
         "\ts_endpgm"])
     assert untracked_load_violations(ok) == ([], 1)
+
+
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip"])
+def test_m0_written_a_wait_state_before_lds_dma(src, tmp_path):
+    asm = compile_asm(os.path.join(CSRC, src), str(tmp_path / "k.s"))
+    bad, count = m0_lds_dma_hazards(open(asm).read())
+    assert count > 0, "no direct-to-LDS loads found"
+    assert not bad, f"{len(bad)} of {count} LDS-DMA loads right after an M0 write, e.g. line {bad[0][0]}"
+
+
+def test_m0_checker_flags_a_planted_hazard():
+    text = "\n".join(["\ts_mov_b32 m0, s4", "\tbuffer_load_dword v1, s[0:3], 0 offen lds",
+                      "\ts_add_u32 m0, s5, 0x400", "\ts_nop 0",
+                      "\tbuffer_load_dwordx4 v2, s[0:3], 0 offen lds"])
+    bad, count = m0_lds_dma_hazards(text)
+    assert count == 2 and [b[0] for b in bad] == [2]
