@@ -140,17 +140,20 @@ __device__ __forceinline__ u32x4 dma_rsrc(const void *base, int num_records) {
                  (uint32_t)__builtin_amdgcn_readfirstlane(num_records), (uint32_t)kBufFlags};
 }
 // gfx9 parts need one wait state between a scalar write of M0 and an LDS-DMA
-// load that reads it (the compiler puts an s_nop there in its own code; it
-// cannot see inside this asm): without it the load may take the previous M0
-// and land on the previous block's LDS address.
+// load that reads it, and five between a VALU write of an SGPR (the
+// readfirstlane of a resource word) and a vector memory instruction reading it.
+// The compiler pads its own code for both but cannot see inside this asm, so
+// the asm carries them itself: s_mov m0 + s_nop 4 is six wait states before the
+// load, whatever precedes the asm. Without them a load may take the previous
+// M0 (landing on the previous block's LDS address) or a stale resource word.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const u32x4 &r, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const u32x4 &r, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
 }
 #pragma clang diagnostic pop

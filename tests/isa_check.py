@@ -10,9 +10,11 @@ first instruction that touches its destination registers is the store of
 those registers into their LDS stage (which the kernel places after the wait
 that covers the load), unless an `s_waitcnt vmcnt(0)` comes first.
 """
+import functools
 import os
 import re
 import subprocess
+import tempfile
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "selective_state_space_cu_amd", "csrc")
@@ -25,6 +27,15 @@ def compile_asm(src, out, defines=()):
            *[f"-D{d}" for d in defines], "--cuda-device-only", "-S", src, "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
     return out
+
+
+@functools.lru_cache(maxsize=None)
+def kernel_asm(src):
+    """Assembly text of one kernel source of the library, compiled once per session."""
+    out = os.path.join(tempfile.mkdtemp(prefix="isa_"), os.path.basename(src) + ".s")
+    compile_asm(os.path.join(CSRC, src), out)
+    with open(out) as f:
+        return f.read()
 
 
 def _vregs(line):
@@ -100,3 +111,41 @@ def m0_lds_dma_hazards(asm_text):
                 bad.append((i + 1, t))
         prev = t
     return bad, count
+
+
+def _sregs(text):
+    out = set()
+    for a, b in re.findall(r"\bs\[(\d+):(\d+)\]", text):
+        out |= set(range(int(a), int(b) + 1))
+    out |= {int(a) for a in re.findall(r"\bs(\d+)\b", text)}
+    return out
+
+
+def valu_sgpr_vmem_hazards(asm_text, need=5):
+    """Vector memory instructions that read an SGPR written by a VALU
+    instruction (v_readfirstlane, v_readlane, v_cmp ... into SGPRs) fewer than
+    `need` wait states earlier (gfx9 needs 5; each instruction in between is
+    one wait state, s_nop N is N + 1). Straight-line view of the code (a branch
+    target is treated as following the instruction above it)."""
+    ins = []
+    for i, l in enumerate(asm_text.split("\n")):
+        t = l.strip()
+        if t and not t.startswith(";") and not t.startswith(".") and not t.endswith(":"):
+            ins.append((i + 1, t))
+    bad = []
+    for k, (ln, t) in enumerate(ins):
+        if not (t.startswith("buffer_") or t.startswith("global_")):
+            continue
+        rd = _sregs(t.split(None, 1)[1]) if " " in t else set()
+        ws = 0
+        for j in range(k - 1, -1, -1):
+            p = ins[j][1]
+            if p.startswith("v_") and " " in p:
+                dst = p.split(None, 1)[1].split(",")[0]
+                if _sregs(dst) & rd:
+                    bad.append((ln, t, ins[j][1], ws))
+                    break
+            ws += int(p.split()[1]) + 1 if p.startswith("s_nop") else 1
+            if ws >= need:
+                break
+    return bad
