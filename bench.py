@@ -350,9 +350,39 @@ def main():
                      "mfma_frac": alg_flops / (scan_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
     }
+    if has_blocks:
+        out["checkpoint_export"] = export_overhead(ssd, d, meta, bt, w, init, has, y, fin, cache)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, H))
     print(json.dumps(out), flush=True)
+
+
+def export_overhead(ssd, d, meta, bt, w, init, has, y, fin, cache, rounds=6, per=10):
+    """Scan time with the at-source block-checkpoint export against the same scan
+    without it (interleaved rounds of HIP-event-timed launches, medians): the
+    kernel-level cost of writing the checkpoints."""
+    import statistics
+    import torch
+    _, dst = ssd.export_chunk_states(meta, bt, w.block_size, num_slots=w.num_slots)
+    t = {True: [], False: []}
+    for _ in range(rounds):
+        for exp in (True, False):
+            for _ in range(per):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                ssd.chunk_scan_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], meta,
+                                      dt_bias=d["dt_bias"], D=d["D"], initial_states=init,
+                                      has_initial_state=has, y=y, final_states=fin,
+                                      chunk_states=cache if exp else None,
+                                      chunk_state_dst=dst if exp else None)
+                e1.record()
+                t[exp].append((e0, e1))
+    torch.cuda.synchronize()
+    med = {k: statistics.median(a.elapsed_time(b) for a, b in v) for k, v in t.items()}
+    return {"scan_ms_with": med[True], "scan_ms_without": med[False],
+            "overhead_frac": med[True] / med[False] - 1.0,
+            "note": "kernel-level: the same scan with and without writing the block checkpoints"}
 
 
 if __name__ == "__main__":
