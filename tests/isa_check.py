@@ -50,7 +50,7 @@ def _vregs(line):
 def untracked_load_violations(asm_text):
     """(load line, path description) for every path that touches an untracked
     load's registers before its stage store or a vmcnt(0) wait; and the number
-    of untracked loads found."""
+    of untracked loads found (register loads inside inline-assembly blocks)."""
     lines = asm_text.split("\n")
     labels = {}
     for i, l in enumerate(lines):
@@ -58,9 +58,15 @@ def untracked_load_violations(asm_text):
         if m:
             labels[m.group(1)] = i
     bad, count = [], 0
+    in_asm = False
     for i, l in enumerate(lines):
         s = l.strip()
-        if not (s.startswith("buffer_load_dwordx4") and " lds" not in s and " offen" in s):
+        # only loads written in inline assembly (the compiler tracks its own)
+        if s.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif s.startswith(";;#ASMEND"):
+            in_asm = False
+        if not (in_asm and s.startswith("buffer_load_dwordx4") and " lds" not in s and " offen" in s):
             continue
         m = re.search(r"v\[(\d+):(\d+)\]", s)
         a, b = int(m.group(1)), int(m.group(2))

@@ -23,21 +23,24 @@ def test_split_scan_untracked_x_loads():
 
 
 def test_checker_flags_a_reused_register():
-    """A planted reuse: the destination is overwritten before any wait."""
+    """A planted reuse: the destination is overwritten before any wait. Loads
+    the compiler emits itself (outside inline assembly) are not counted."""
     text = "\n".join([
-        "\tbuffer_load_dwordx4 v[4:7], v1, s[0:3], 0 offen offset:0",
+        "\t;;#ASMSTART", "\tbuffer_load_dwordx4 v[4:7], v1, s[0:3], 0 offen offset:0", "\t;;#ASMEND",
         "\tv_mov_b32_e32 v5, 0",
         "\ts_waitcnt vmcnt(0)",
         "\ts_endpgm"])
     bad, count = untracked_load_violations(text)
     assert count == 1 and len(bad) == 1
     ok = "\n".join([
-        "\tbuffer_load_dwordx4 v[4:7], v1, s[0:3], 0 offen offset:0",
+        "\t;;#ASMSTART", "\tbuffer_load_dwordx4 v[4:7], v1, s[0:3], 0 offen offset:0", "\t;;#ASMEND",
+        "\tbuffer_load_dwordx4 v[8:11], v1, s[0:3], 0 offen offset:0",
         "\ts_cbranch_scc1 .LBB0_2",
         "\ts_waitcnt vmcnt(0)",
         "\tv_mov_b32_e32 v5, 0",
         ".LBB0_2:",
         "\tds_write_b128 v9, v[4:7]",
+        "\tv_mov_b32_e32 v9, v8",
         "\ts_endpgm"])
     assert untracked_load_violations(ok) == ([], 1)
 
