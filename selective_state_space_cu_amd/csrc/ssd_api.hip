@@ -96,6 +96,9 @@ ssd_status ssd_chunk_scan_varlen(const void *x, const float *dt, const float *dt
     const bool split = in_dtype == SSD_BF16 && dstate == 128 && headdim % 64 == 0;
     a.nptiles = headdim / (16 * waves);
     a.xcd_mode = ssd::xcd_mode_for(meta->nseqs, nheads, ngroups, a.nptiles);
+    a.items = split ? ssd::split_items_for(a.xcd_mode, (int64_t)meta->nseqs * nheads * a.nptiles,
+                                           nheads / ngroups)
+                    : 1;
     if (meta->nseqs == 0) return SSD_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = split ? ssd::launch_scan_split_bf16(a, dstate, s)

@@ -32,6 +32,8 @@ struct ScanArgs {
     int32_t T, S, H, P, G, cs, max_chunks, capacity, nptiles;
     // workgroup -> XCD mapping (see decode_block): one of the kXcd* values
     int32_t xcd_mode;
+    // consecutive heads walked by one workgroup (split-state kernel; 1 = one head)
+    int32_t items;
 };
 
 enum : int32_t { kXcdNone = 0, kXcdPairs = 1, kXcdSplit = 2, kXcdPairsIfEqual = 3, kXcdPairsIfEqualElseNone = 4 };
@@ -46,6 +48,17 @@ inline int32_t xcd_mode_for(int32_t nseqs, int32_t nheads, int32_t ngroups, int3
     if (pairs && ngroups % 8 == 0) return kXcdPairs;
     if (pairs) return split ? kXcdPairsIfEqual : kXcdPairsIfEqualElseNone;
     return split ? kXcdSplit : kXcdNone;
+}
+
+// Heads walked by one workgroup of the split-state kernel: with the pair
+// mapping and at least 16 workgroups per CU (256 CUs) to begin with, merge
+// heads of one (sequence, group) pair so that each workgroup walks 2 or 4 of
+// them as one tile stream, keeping at least 8 workgroups per CU.
+inline int32_t split_items_for(int32_t xcd_mode, int64_t blocks, int32_t heads_per_group) {
+    if (xcd_mode != kXcdPairs) return 1;
+    for (int32_t k : {4, 2})
+        if (heads_per_group % k == 0 && blocks / k >= 2048) return k;
+    return 1;
 }
 
 // Launches the scan for one (dtype, waves-per-workgroup, dstate) instance.

@@ -169,7 +169,7 @@ struct SplitShape {
     static constexpr int vm_wait(int exports) { return 2 + kLoads + exports * kNTH; }
     static constexpr int kNST = 3;
     static_assert(fit(kNST), "three stages must fit in LDS");
-    static_assert(vm_wait(2) <= 63, "vmcnt range");
+    static_assert(vm_wait(4) <= 63, "vmcnt range");
     // the partner's state fragments use C blocks w + 8 c of a consumed stage
     static_assert(8 * kNKH <= kTileC / 1024, "state exchange needs 8 C blocks per fragment");
     // a checkpoint is staged in 2 KB per wave of a consumed B tile
@@ -177,7 +177,24 @@ struct SplitShape {
     __device__ static int swz128(int r) { return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
 };
 
-template <int N>
+// Workgroup -> (sequence rank, first head, headdim tile) when each workgroup
+// walks a.items consecutive heads of one (sequence, group) pair (the pair
+// mapping of decode_block, with a.items heads per workgroup).
+__device__ __forceinline__ void decode_block_multi(const ScanArgs &a, int b, int &rank, int &h0, int &pt) {
+    const int hpg = a.H / a.G, K = a.items;
+    const int wpp = hpg / K * a.nptiles;   // workgroups per pair
+    const int x = b & 7, i = b >> 3;
+    const int pair = x + 8 * (i / wpp), loc = i - (i / wpp) * wpp;
+    rank = pair / a.G;
+    h0 = (pair - rank * a.G) * hpg + (loc / a.nptiles) * K;
+    pt = loc - (loc / a.nptiles) * a.nptiles;
+}
+
+// MULTI: the workgroup walks the tiles of a.items consecutive heads as one
+// stream (same sequence and group, so the same B and C tiles): the pipeline
+// runs on from one head into the next, so a head's start-up (initial state,
+// first stages, tables) overlaps the previous head's last tiles.
+template <int N, bool MULTI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #if !defined(__HIP_DEVICE_COMPILE__)
@@ -210,8 +227,10 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     const bool godd = (g & 1) != 0;
 
     if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
-    int rank, h, pt;
-    decode_block(a, blockIdx.x, rank, h, pt);
+    int rank, h, pt;   // (with MULTI, h is the workgroup's first head)
+    if constexpr (MULTI) decode_block_multi(a, blockIdx.x, rank, h, pt);
+    else decode_block(a, blockIdx.x, rank, h, pt);
+    const int K = MULTI ? a.items : 1;   // heads walked by this workgroup
     const int s = a.seq_order[rank];
     if (s < 0 || s >= a.S) return;
     const int grp = h / (a.H / a.G);
@@ -229,9 +248,19 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     const int pw = p0 + 16 * pb;         // first headdim column of this wave
     const int nb = nh * (N / 2);         // first state row of this wave's half
     const int r0 = 32 * nh;              // first token row of this wave's half
-    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-    const float a2 = a.A[h] * kLog2e;
+    // (with MULTI: bias and a2 are those of the head whose tables are computed
+    // next; lane k of cb_l, ca_l, cd_l holds head h + k's)
+    float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    float a2 = a.A[h] * kLog2e;
     const float Dh = a.D ? a.D[h] : 0.0f;
+    float cb_l = 0.0f, ca_l = 0.0f, cd_l = 0.0f;
+    if constexpr (MULTI) {
+        if (lane < K) {
+            cb_l = a.dt_bias ? a.dt_bias[h + lane] : 0.0f;
+            ca_l = a.A[h + lane] * kLog2e;
+            cd_l = a.D ? a.D[h + lane] : 0.0f;
+        }
+    }
     const int xrow = H * P * 2;     // bytes between tokens of x / y
     const int browg = G * N * 2;    // bytes between tokens of B / C
     const int clampTT = TT;
@@ -258,11 +287,35 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     f32x4 st[NTH];
 #pragma unroll
     for (int u = 0; u < NTH; ++u) st[u] = f32x4{0, 0, 0, 0};
-    if (a.init != nullptr && (a.has_init == nullptr || a.has_init[s] != 0)) {
+    const bool has_init = a.init != nullptr && (a.has_init == nullptr || a.has_init[s] != 0);
+    if (has_init) {
         const float *src = a.init + ((int64_t)(s * H + h) * P + pw + q) * N + nb;
 #pragma unroll
         for (int u = 0; u < NTH; ++u) st[u] = *reinterpret_cast<const f32x4 *>(src + n_of(u));
     }
+    // MULTI: the initial and final states of head h + k, through buffer
+    // resources spanning this sequence's H P N floats (offsets out of that
+    // range read zero / are dropped); stn holds the next head's initial state.
+    f32x4 stn[NTH];
+    const int seq_bytes = H * P * N * 4;
+    const uint64_t init_seq = uni64((uint64_t)(uintptr_t)a.init + (uint64_t)s * (uint64_t)seq_bytes);
+    const uint64_t fin_seq = uni64((uint64_t)(uintptr_t)a.final_states + (uint64_t)s * (uint64_t)seq_bytes);
+    auto state_off = [&](int k, int u) { return (((h + k) * P + pw + q) * N + nb + n_of(u)) * 4; };
+    auto load_init = [&](f32x4 (&dst)[NTH], int k) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(uintptr_t)init_seq, 0, has_init && k < K ? seq_bytes : 0, kBufFlags);
+#pragma unroll
+        for (int u = 0; u < NTH; ++u)
+            dst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, state_off(k, u), 0, 0));
+    };
+    auto store_final = [&](int k) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(uintptr_t)fin_seq, 0, k < K ? seq_bytes : 0, kBufFlags);
+#pragma unroll
+        for (int u = 0; u < NTH; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st[u]), r, state_off(k, u), 0, 0);
+    };
+    if constexpr (MULTI) load_init(stn, 1);
 
     // Scan tables of a tile from delta (lane j = token j; delta = 0 past the
     // tile end), one table per wave of waves 0-3: S = s_j (inclusive cumulative
@@ -351,6 +404,24 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         r.x = (uint32_t)v;
         r.y = (uint32_t)(v >> 32);
     };
+    // MULTI: stream positions (head k, tile) of the fetch cursor; the dt that
+    // rides with a stage is that of the stream's next tile (d_rem its tokens)
+    int fi = 0, ft = 0, d_rem = 0;
+    auto next_pos = [&](int &k, int &tl) {
+        if (++tl == nt) { tl = 0; ++k; }
+    };
+    auto set_fetch = [&]() {
+        const int64_t tok = tb + (int64_t)ft * TT;
+        r_c = buf_rsrc(uni64((uint64_t)(uintptr_t)a.C + (uint64_t)((tok * G + grp) * N) * 2), 0);
+        r_b = buf_rsrc(uni64((uint64_t)(uintptr_t)a.B + (uint64_t)((tok * G + grp) * N) * 2), 0);
+        r_x = buf_rsrc(uni64((uint64_t)(uintptr_t)a.x + (uint64_t)((tok * H + h + fi) * P + p0) * 2), 0);
+        int di = fi, dtl = ft;
+        next_pos(di, dtl);
+        r_d = buf_rsrc(uni64((uint64_t)(uintptr_t)a.dt + (uint64_t)((tb + (int64_t)dtl * TT) * H + h + di) * 4), 0);
+        f_rem = fi < K ? L - ft * TT : 0;
+        d_rem = di < K ? L - dtl * TT : 0;
+    };
+    if constexpr (MULTI) set_fetch();
 
     // Fetch tile f into stage buffer SLOT (zero-filling loads past the
     // sequence): part 0 loads C and B, part 1 x and the dt of tile f + 1
@@ -370,7 +441,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             });
         } else {
             r_x.z = (uint32_t)(Lt * xrow);
-            r_d.z = (uint32_t)(clamp_len(f_rem - TT) * H * 4);
+            r_d.z = (uint32_t)(clamp_len(MULTI ? d_rem : f_rem - TT) * H * 4);
             if constexpr (decltype(with_x)::value) {
                 static_for<SH::kIX>([&](auto i_c) {
                     constexpr int I = decltype(i_c)::value;
@@ -379,8 +450,13 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             }
             dma4_at<SLOT * 256>(r_d, lds_dt, go_d);
             // next tile (past the sequence end the positions are never dereferenced)
-            advance(r_c, step_bc); advance(r_b, step_bc); advance(r_x, step_x); advance(r_d, step_d);
-            f_rem -= TT;
+            if constexpr (MULTI) {
+                next_pos(fi, ft);
+                set_fetch();
+            } else {
+                advance(r_c, step_bc); advance(r_b, step_bc); advance(r_x, step_x); advance(r_d, step_d);
+                f_rem -= TT;
+            }
         }
     };
     using P0 = std::integral_constant<int, 0>;
@@ -393,17 +469,35 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     u32x4 xr[NST];
     u32x4 r_xg = buf_rsrc(uni64((uint64_t)(uintptr_t)a.x + (uint64_t)(((tb + 2 * TT) * H + h) * P + p0) * 2), 0);
     int xg_rem = L - 2 * TT;   // tokens from the tile whose x is loaded next
+    int xi = 0, xt = 0;        // (MULTI) its stream position
+    auto set_xg = [&]() {
+        r_xg = buf_rsrc(uni64((uint64_t)(uintptr_t)a.x +
+                              (uint64_t)(((tb + (int64_t)xt * TT) * H + h + xi) * P + p0) * 2), 0);
+        xg_rem = xi < K ? L - xt * TT : 0;
+    };
+    if constexpr (MULTI) {
+        if (nt > 0) { next_pos(xi, xt); next_pos(xi, xt); }
+        else xi = K;
+        set_xg();
+    }
     auto xload = [&](auto set_c) {
         constexpr int SET = decltype(set_c)::value;
         r_xg.z = (uint32_t)(clamp_len(xg_rem) * xrow);
         load16_untracked<0>(xr[SET], r_xg, go_x[0]);
-        advance(r_xg, step_x);
-        xg_rem -= TT;
+        if constexpr (MULTI) {
+            next_pos(xi, xt);
+            set_xg();
+        } else {
+            advance(r_xg, step_x);
+            xg_rem -= TT;
+        }
     };
     auto wait_stage = [&](int exports) {   // checkpoint exports among the last two steps
         if (exports == 0) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(0)>::imm);
         else if (exports == 1) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(1)>::imm);
-        else __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(2)>::imm);
+        else if (!MULTI || exports == 2) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(2)>::imm);
+        else if (exports == 3) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(3)>::imm);
+        else __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(4)>::imm);
     };
 
     // y of the previous tile: LDS tile (row rho = token, 128 bytes, chunk k at
@@ -523,9 +617,11 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     // store reads row lane / 16, chunk lane mod 16
     const uint32_t e_base = lds_addr(sE) + SH::kStageE * wave;
     const uint32_t e_get = e_base + 256 * (lane >> 4) + 16 * ((lane & 15) ^ (lane >> 4));
-    int t = 0;              // current tile
+    int t = 0;              // current tile (of the stream, with MULTI)
+    const int ntot = nt * K;  // tiles of the stream
+    int ic = 0, tc = 0;       // head (of the workgroup's K) and tile of tile t
     // checkpoint slots: a.chunk_states + slot * H P N floats + this workgroup's block
-    const uint64_t ck_base = uni64((uint64_t)(uintptr_t)a.chunk_states + (uint64_t)((h * P + p0) * N) * 4);
+    uint64_t ck_base = uni64((uint64_t)(uintptr_t)a.chunk_states + (uint64_t)((h * P + p0) * N) * 4);
     const uint64_t ck_slot = uni64((uint64_t)H * P * N * 4);
 
     // One step: tile t in stage SLOT (= t mod NST).
@@ -538,7 +634,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
         // checkpoint slot of the state after this tile, or -1
         int dsl = -1;
-        if (t == ex_tile) {
+        if ((MULTI ? tc : t) == ex_tile) {
             if (ex_chunk - ex_win >= 64) {   // next window (once per 64 checkpoints)
                 ex_win = ex_chunk;
                 slots = load_slots(ex_win);
@@ -632,8 +728,14 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         fetch(P0{}, std::integral_constant<int, FETCH>{}, NoX{});
 
         // scan tables of the next tile, from the dt that rode with this stage
-        if (wave < 4 && t + 1 < nt) {
-            const int Ln = clamp_len(L - (t + 1) * TT);
+        if (wave < 4 && t + 1 < (MULTI ? ntot : nt)) {
+            const int tn = MULTI ? (tc + 1 < nt ? tc + 1 : 0) : t + 1;   // tile index of tile t + 1
+            if constexpr (MULTI) {   // that tile's head
+                const int kn = tc + 1 < nt ? ic : ic + 1;
+                bias = readlane(cb_l, kn);
+                a2 = readlane(ca_l, kn);
+            }
+            const int Ln = clamp_len(L - tn * TT);
             tables(tabs + NEXT * TAB, softplus_hw(sDt[SLOT * 64 + lane] + bias + (lane < Ln ? 0.0f : -INFINITY)));
         }
         lds_barrier();   // (B) decay matrix, x . w and next tables complete; stage SLOT's C tile consumed
@@ -682,14 +784,22 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 u32x2{pack_bf16(acc[d][0], acc[d][1]), pack_bf16(acc[d][2], acc[d][3])};
         // x of tile t + 2 into stage FETCH (consumed by the previous step)
         *(lds_u32x4 *)(uintptr_t)(lds_x + FETCH * SH::kTileX + 16 * lane) = xr[SLOT];
-        y_prev += step_x;
-        y_len = clamp_len(y_rem);
-        y_rem -= TT;
+        if constexpr (MULTI) {
+            y_prev = uni64((uint64_t)(uintptr_t)a.y + (uint64_t)(((tb + (int64_t)tc * TT) * H + h + ic) * P + p0) * 2);
+            y_len = clamp_len(L - tc * TT);
+        } else {
+            y_prev += step_x;
+            y_len = clamp_len(y_rem);
+            y_rem -= TT;
+        }
 
         // the state half after the tile into its checkpoint slot, if the tile
         // ends a chunk: four rounds of 4 state rows through the wave's staging
         // area, each store 4 rows x 256 bytes
-        const int ex = dsl >= 0 ? 1 : 0;
+        // (MULTI: the last tile of a head that is not the workgroup's last also
+        // stores that head's final state: NTH more stores, counted as an export)
+        const bool bnd = MULTI && tc == nt - 1 && ic + 1 < K;
+        const int ex = (dsl >= 0 ? 1 : 0) + (bnd ? 1 : 0);
         nexp = ex1 + ex;
         ex1 = ex;
         if (dsl >= 0) {
@@ -711,18 +821,45 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 wave_lds_sync();
             }
         }
+        if constexpr (MULTI) {
+            if (bnd) {
+                // head ic is done: its final state out, the next head's initial
+                // state in (and to the partner, in place of h_out), its D on the
+                // diagonal, its checkpoint columns; the chunk walk restarts
+                store_final(ic);
+#pragma unroll
+                for (int u = 0; u < NTH; ++u) st[u] = stn[u];
+                load_init(stn, ic + 2);
+                make_own();
+                put_own(slot_c);
+                const float dn = readlane(cd_l, ic + 1);
+#pragma unroll
+                for (int d = 0; d < 2; ++d)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dadd[d][r] = (16 * pb + 4 * g + r == r0 + 16 * d + q) ? dn : 0.0f;
+                ck_base += (uint64_t)P * N * 4;
+                ex_tile = a.chunk_states != nullptr ? min(tpc, nt) - 1 : nt;
+                ex_chunk = c0;
+                if (a.chunk_states != nullptr && ex_win != c0) {
+                    ex_win = c0;
+                    slots = load_slots(ex_win);
+                    __builtin_amdgcn_s_waitcnt(WaitVm<0>::imm);
+                }
+            }
+        }
         pin_decay();
         xload(slot_c);   // x of tile t + 5 (set SLOT is free again)
         ++t;
+        if constexpr (MULTI) next_pos(ic, tc);
     };
 
     lds_barrier();   // tile 0's tables are visible
     decay_of(tabs);
-    while (t < nt) {
+    while (t < ntot) {
         step(std::integral_constant<int, 0>{});
-        if (t >= nt) break;
+        if (t >= ntot) break;
         step(std::integral_constant<int, 1>{});
-        if (t >= nt) break;
+        if (t >= ntot) break;
         step(std::integral_constant<int, 2>{});
     }
     // register loads of x past the last step are still in flight
@@ -732,18 +869,33 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         store_prev_y(*(const lds_u32x4 *)(uintptr_t)y_get);
     }
 
-    float *fd = a.final_states + ((int64_t)(s * H + h) * P + pw + q) * N + nb;
+    if constexpr (MULTI) {
+        if (nt == 0) {   // empty sequence: every head's final state is its initial state
+            for (int k = 0; k < K; ++k) {
+                if (k > 0) load_init(st, k);
+                store_final(k);
+            }
+        } else {
+            store_final(K - 1);
+        }
+    } else {
+        float *fd = a.final_states + ((int64_t)(s * H + h) * P + pw + q) * N + nb;
 #pragma unroll
-    for (int u = 0; u < NTH; ++u) *reinterpret_cast<f32x4 *>(fd + n_of(u)) = st[u];
+        for (int u = 0; u < NTH; ++u) *reinterpret_cast<f32x4 *>(fd + n_of(u)) = st[u];
+    }
 }
 #endif
 
 template <int N>
 hipError_t launch_scan_split_instance(const ScanArgs &a, hipStream_t stream) {
-    const int64_t blocks = (int64_t)a.S * a.H * a.nptiles;
+    const int64_t blocks = (int64_t)a.S * a.H * a.nptiles / a.items;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((ssd_scan_split_kernel<N>), dim3((unsigned)blocks), dim3(SplitShape<N>::kThreads), 0,
-                       stream, a, a.chunk_state_dst);
+    if (a.items > 1)
+        hipLaunchKernelGGL((ssd_scan_split_kernel<N, true>), dim3((unsigned)blocks), dim3(SplitShape<N>::kThreads), 0,
+                           stream, a, a.chunk_state_dst);
+    else
+        hipLaunchKernelGGL((ssd_scan_split_kernel<N, false>), dim3((unsigned)blocks), dim3(SplitShape<N>::kThreads), 0,
+                           stream, a, a.chunk_state_dst);
     return hipGetLastError();
 }
 

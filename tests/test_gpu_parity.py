@@ -304,3 +304,17 @@ def test_no_sequences():
     w = make_inputs([], 2, 64, 128, 1, 64, dtype="bf16", seed=8)
     meta, y, fin, _ = gpu_run(w)
     assert y.shape[0] == 0 and fin.shape[0] == 0 and int(meta.nchunks.item()) == 0
+
+
+@pytest.mark.parametrize("S,seed", [(64, 21), (32, 22)], ids=["4-heads-per-workgroup", "2-heads-per-workgroup"])
+def test_multi_head_workgroups(S, seed):
+    """Many short sequences with G a multiple of 8: each workgroup walks 4 (S = 64) or
+    2 (S = 32) consecutive heads of one (sequence, group) as one tile stream. Lengths
+    include empty, one-token and tile-boundary cases; initial states on most
+    sequences; every chunk state exported."""
+    rng = np.random.default_rng(seed)
+    L = [int(v) for v in rng.integers(1, 200, size=S)]
+    L[:6] = [0, 1, 63, 64, 65, 129]
+    w = make_inputs(L, 128, 64, 128, 8, 64, dtype="bf16", init_seqs=[i for i in range(S) if i % 5],
+                    seed=seed)
+    _full_compare(w, what=f"multi-head S={S}")
