@@ -38,29 +38,32 @@ def kernel_hash(sources=KERNEL_SOURCES):
     return h.hexdigest()[:16]
 
 
-def ingest_counters(fetch_csv, write_csv, config, calib_mib, workload="prefill"):
+def ingest_counters(fetch_csv, write_csv, config, calib_mib, workload="prefill", out=None):
     """Turn two rocprofv3 --pmc runs of `bench.py --copy-calib-mib M` (FETCH_SIZE,
     then WRITE_SIZE; KiB per dispatch) into the HBM traffic of one launch of the
     workload's kernel, each counter scaled by what it reads for the calibration
     kernel (one elementwise pass that reads and writes M MiB)."""
     decode = workload == "decode"
-    out = DECODE_COUNTERS if decode else COUNTERS
+    out = out or (DECODE_COUNTERS if decode else COUNTERS)
     tag = "ssd_decode" if decode else "ssd_scan"
     import csv
 
-    def per_kernel(path):
-        vals = {}
-        for r in csv.DictReader(open(path)):
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return vals
+    def read(path):
+        """(scan readings, calibration reading) of one pass: the calibration
+        dispatch is the elementwise kernel with the largest reading (the add);
+        only the scan dispatches issued before it count, which are the warm-up
+        and timed steps (the export-overhead runs after it include launches
+        that write no checkpoints)."""
+        rows = [(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                for r in csv.DictReader(open(path))]
+        cal_id, cal = max(((i, v) for i, k, v in rows if "elementwise" in k), key=lambda t: t[1])
+        scan = [v for i, k, v in rows if tag in k and i < cal_id]
+        if not scan:
+            raise ValueError(f"{path}: no {tag} dispatch before the calibration copy")
+        return scan, cal
 
-    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
-    scan_f = [v for k, v in fetch.items() if tag in k][0]
-    scan_w = [v for k, v in write.items() if tag in k][0]
+    (scan_f, cal_f), (scan_w, cal_w) = read(fetch_csv), read(write_csv)
     calib_kib = calib_mib * 1024.0
-    # calibration dispatch: the elementwise kernel with the largest reading (the add)
-    cal_f = max(x for k, v in fetch.items() if "elementwise" in k for x in v)
-    cal_w = max(x for k, v in write.items() if "elementwise" in k for x in v)
     ff, fw = calib_kib / cal_f, calib_kib / cal_w
     fk, wk = sum(scan_f) / len(scan_f), sum(scan_w) / len(scan_w)
     rec = {"kernel": "ssd_decode_kernel" if decode else scan_kernel_name(config),

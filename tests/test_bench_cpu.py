@@ -48,3 +48,35 @@ def test_decode_batches_respect_the_slot_precondition():
             if slot >= 0:
                 others = np.delete(rs, i)
                 assert slot not in others
+
+
+def test_counter_ingest_counts_only_the_steps_before_the_calibration_copy(tmp_path):
+    """rocprofv3 --pmc rows: two scan steps (800 KiB), small torch kernels, the
+    calibration copy (512 MiB read and written: FETCH_SIZE reads half, as in the
+    real counter), then export-overhead launches that write less. Only the two
+    steps before the copy count."""
+    import csv as _csv
+    import json as _json
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Value"]
+
+    def write(path, calib, late):
+        rows = [(1, "void at::native::vectorized_elementwise_kernel<fill>", 0.03),
+                (2, "void ssd::ssd_scan_split_kernel<128, false>(ssd::ScanArgs)", 800.0),
+                (3, "void at::native::vectorized_elementwise_kernel<fill>", 0.03),
+                (4, "void ssd::ssd_scan_split_kernel<128, false>(ssd::ScanArgs)", 800.0),
+                (5, "void at::native::vectorized_elementwise_kernel<add>", calib),
+                (6, "void at::native::vectorized_elementwise_kernel<fill>", 0.5)]
+        rows += [(7 + i, "void ssd::ssd_scan_split_kernel<128, false>(ssd::ScanArgs)", late) for i in range(10)]
+        with open(path, "w", newline="") as f:
+            wr = _csv.writer(f)
+            wr.writerow(hdr)
+            wr.writerows(rows)
+
+    fc, wc, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "rec.json"
+    write(fc, 512 * 1024 / 2, 100.0)
+    write(wc, 512 * 1024, 100.0)
+    rec = bench.ingest_counters(str(fc), str(wc), 4, 512, out=str(out))
+    assert rec["dispatches"] == 2
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["hbm_bytes_per_launch"] == (800.0 * 2.0 + 800.0 * 1.0) * 1024.0
+    assert _json.load(open(out)) == rec
