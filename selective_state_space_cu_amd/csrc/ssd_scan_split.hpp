@@ -126,8 +126,11 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
 }
-// Cache policy of the y and checkpoint stores: non-temporal (written once, not re-read here).
-constexpr int kStoreNT = 2;
+// Cache policy of the y and checkpoint stores (written once, not re-read
+// here): non-temporal with the sc1 scope bit, which timed 1-1.5 % faster on the
+// prefix-cache workload than non-temporal alone (plain, sc1 alone and sc0 + nt
+// were no faster).
+constexpr int kStoreNT = 2 | 16;
 // Wave-uniform 64-bit value (kept in an SGPR pair).
 __device__ __forceinline__ uint64_t uni64(uint64_t v) {
     return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32) |
