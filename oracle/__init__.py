@@ -4,5 +4,5 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
 benchmark's CPU-baseline leg, never by the product path. It shares no code with
 the HIP library.
 """
-from .oracle import (load, ssd_varlen, ssd_decode, varlen_metadata, checkpoint_plan,  # noqa: F401
-                     num_threads)
+from .oracle import (load, ssd_varlen, ssd_decode, causal_conv1d, varlen_metadata,  # noqa: F401
+                     checkpoint_plan, num_threads)

@@ -40,6 +40,9 @@ def load(path=LIB):
     lib.oracle_ssd_decode.argtypes = [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, _F64P, ctypes.c_int32, _I32P, _I32P, _F64P]
+    lib.oracle_causal_conv1d.argtypes = [
+        ctypes.c_int32, _I32P, ctypes.c_int32, ctypes.c_int32, _F64P, _F64P, _F64P, ctypes.c_int32,
+        _F64P, ctypes.c_int32, _I32P, _I32P, _F64P]
     lib.oracle_num_threads.restype = ctypes.c_int
     _cache[path] = lib
     return lib
@@ -149,3 +152,26 @@ def ssd_decode(x, dt, dt_bias, A, B, C, D, state_cache, read_slot, write_slot, l
     if rc == -1:
         raise ValueError("oracle_ssd_decode: bad shapes")
     return y, cache, rc
+
+
+def causal_conv1d(x, cu_seqlens, weight, bias, silu, conv_states, read_slot, write_slot, lib=None):
+    """Varlen causal conv1d with a conv-state cache (float64).
+    x (T, C); weight (C, W); bias (C,) or None; conv_states (slots, W-1, C);
+    read_slot / write_slot (S,) int, < 0 meaning zero leading inputs / no write.
+    Returns (out (T, C), updated copy of conv_states, status: 0, or -2 if a slot
+    was out of range and its sequence skipped)."""
+    lib = lib or load()
+    x, weight = _np(x, np.float64), _np(weight, np.float64)
+    bias = None if bias is None else _np(bias, np.float64)
+    states = _np(conv_states, np.float64).copy()
+    cu = _np(cu_seqlens, np.int32)
+    rs, ws = _np(read_slot, np.int32), _np(write_slot, np.int32)
+    T, C = x.shape
+    W = weight.shape[1]
+    out = np.zeros((T, C), np.float64)
+    rc = lib.oracle_causal_conv1d(len(cu) - 1, _p(cu, _I32P), C, W, _p(x, _F64P), _p(weight, _F64P),
+                                  _p(bias, _F64P), int(bool(silu)), _p(states, _F64P), states.shape[0],
+                                  _p(rs, _I32P), _p(ws, _I32P), _p(out, _F64P))
+    if rc == -1:
+        raise ValueError("oracle_causal_conv1d: bad shapes")
+    return out, states, rc

@@ -323,3 +323,83 @@ int oracle_ssd_decode(int32_t nseqs, int32_t nheads, int32_t headdim, int32_t ds
     free(h_in);
     return bad ? -2 : 0;
 }
+
+/*
+ * Varlen causal conv1d (the causal_conv1d step that runs before the scan and
+ * whose metadata the prefix-caching page builds together with the other batch
+ * metadata). The pages name the kernel without giving its formula; this is the
+ * standard depthwise causal convolution of the Mamba2 block, read plainly:
+ * each channel c has its own `width` taps weight[c, 0..W-1] (tap W-1 on the
+ * current token), the window never reaches across a sequence start, and the
+ * W-1 inputs before a sequence's first token come from a conv-state cache slot
+ * (dual anchors, as for the SSM state: read from read_slot[s], zero when < 0;
+ * the sequence's last W-1 inputs are written to write_slot[s], skipped when < 0).
+ * For sequence s with L tokens at rows cu[s] .. cu[s+1]-1 and j in [0, L):
+ *     u_j      = x[cu[s] + j, c]                            (j >= 0)
+ *     u_j      = conv_states[read_slot[s], W-1+j, c]        (-(W-1) <= j < 0)
+ *     out[cu[s]+j, c] = act(bias[c] + sum_k weight[c,k] * u_{j-(W-1)+k})
+ *     conv_states[write_slot[s], i, c] = u_{L-(W-1)+i}      (i = 0 .. W-2)
+ * act = identity (silu = 0) or SiLU z / (1 + e^-z) (silu = 1). Layouts: x, out
+ * (T, channels); weight (channels, W); bias (channels) or NULL; conv_states
+ * (num_slots, W-1, channels). Every state read happens before any state write.
+ * A sequence with a slot >= num_slots is skipped (its rows of out left as
+ * they are, nothing written) and the call returns -2; -1 on bad shapes.
+ */
+int oracle_causal_conv1d(int32_t nseqs, const int32_t *cu_seqlens, int32_t channels, int32_t width,
+                         const double *x, const double *weight, const double *bias, int32_t silu,
+                         double *conv_states, int32_t num_slots, const int32_t *read_slot,
+                         const int32_t *write_slot, double *out)
+{
+    const int64_t Cn = channels, W = width;
+    if (nseqs < 0 || Cn <= 0 || W < 1 || num_slots < 0)
+        return -1;
+    for (int32_t s = 0; s < nseqs; ++s)
+        if (cu_seqlens[s + 1] < cu_seqlens[s])
+            return -1;
+    const int64_t per_slot = (W - 1) * Cn;
+    int bad = 0;
+    /* each sequence's W-1 leading inputs, gathered before any slot write */
+    double *pre = (double *)calloc((size_t)(nseqs > 0 ? nseqs : 1) * (size_t)(per_slot > 0 ? per_slot : 1),
+                                   sizeof(double));
+    if (!pre)
+        return -1;
+    for (int32_t s = 0; s < nseqs; ++s) {
+        const int32_t r = read_slot ? read_slot[s] : -1;
+        const int32_t w = write_slot ? write_slot[s] : -1;
+        if (r >= num_slots || w >= num_slots) {
+            bad |= 1;
+            continue;
+        }
+        if (r >= 0 && per_slot > 0)
+            memcpy(pre + (int64_t)s * per_slot, conv_states + (int64_t)r * per_slot,
+                   (size_t)per_slot * sizeof(double));
+    }
+    for (int32_t s = 0; s < nseqs; ++s) {
+        const int32_t r = read_slot ? read_slot[s] : -1;
+        const int32_t w = write_slot ? write_slot[s] : -1;
+        if (r >= num_slots || w >= num_slots)
+            continue;
+        const int64_t t0 = cu_seqlens[s], L = cu_seqlens[s + 1] - cu_seqlens[s];
+        const double *ps = pre + (int64_t)s * per_slot;
+        for (int64_t c = 0; c < Cn; ++c) {
+            for (int64_t j = 0; j < L; ++j) {
+                double z = bias ? bias[c] : 0.0;
+                for (int64_t k = 0; k < W; ++k) {
+                    const int64_t jj = j - (W - 1) + k;   /* input position of tap k */
+                    const double u = jj >= 0 ? x[(t0 + jj) * Cn + c] : ps[(W - 1 + jj) * Cn + c];
+                    z += weight[c * W + k] * u;
+                }
+                out[(t0 + j) * Cn + c] = silu ? z / (1.0 + exp(-z)) : z;
+            }
+            if (w >= 0) {
+                for (int64_t i = 0; i < W - 1; ++i) {
+                    const int64_t jj = L - (W - 1) + i;
+                    conv_states[(int64_t)w * per_slot + i * Cn + c] =
+                        jj >= 0 ? x[(t0 + jj) * Cn + c] : ps[(W - 1 + jj) * Cn + c];
+                }
+            }
+        }
+    }
+    free(pre);
+    return bad ? -2 : 0;
+}

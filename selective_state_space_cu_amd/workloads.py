@@ -228,3 +228,59 @@ def make_decode_config() -> DecodeBatch:
     c = DECODE_CONFIG
     return make_decode_inputs(c["nseqs"], c["nheads"], c["headdim"], c["dstate"], c["ngroups"],
                               c["num_slots"], dtype=c["dtype"], seed=c["seed"], name=c["name"])
+
+
+@dataclasses.dataclass
+class ConvBatch:
+    """Inputs of one varlen causal conv1d call (the step before the scan)."""
+    x: torch.Tensor             # (T, C) in dtype
+    weight: torch.Tensor        # (C, W) float32
+    bias: torch.Tensor          # (C,) float32
+    cu_seqlens: torch.Tensor    # (S+1,) int32
+    conv_states: torch.Tensor   # (num_slots, W-1, C) in dtype
+    read_slot: torch.Tensor     # (S,) int32, < 0: zero leading inputs
+    write_slot: torch.Tensor    # (S,) int32, < 0: no state written
+    silu: bool
+    dtype: str
+    name: str = ""
+
+
+# The channels of the prefix-cache workload's layer: x (H P = 4096) then B and C
+# (2 G N = 1024), convolved with width 4 before the scan.
+CONV_CONFIG = dict(name="conv1d_prefix_cache_4x8894_c5120_w4", lengths=[8894] * 4, channels=5120,
+                   width=4, silu=True, chunk_size=64, num_slots=8, dtype="bf16", seed=6)
+
+
+def make_conv_inputs(lengths, channels, width, num_slots, dtype="f32", seed=0, anchors="dual",
+                     silu=True, name=""):
+    """Draw one conv1d batch. Draw order: x ~ N(0,1) -> weight, bias ~ U(-1/sqrt(W),
+    1/sqrt(W)) (the usual fan-in init) -> cached states ~ N(0,1) -> slot
+    permutation. anchors: "dual" (read and write slots all distinct; needs
+    num_slots >= 2 S) or "mixed" (dual, with every third sequence reading no
+    slot and every fourth writing none)."""
+    rng = np.random.default_rng(seed)
+    S, C, W = len(lengths), channels, width
+    cu = np.zeros(S + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    k = 1.0 / np.sqrt(W)
+    x = rng.standard_normal((T, C))
+    weight = rng.uniform(-k, k, size=(C, W))
+    bias = rng.uniform(-k, k, size=C)
+    states = rng.standard_normal((num_slots, max(W - 1, 0), C))
+    assert num_slots >= 2 * S, "dual anchors need two distinct slots per sequence"
+    perm = rng.permutation(num_slots).astype(np.int32)
+    rs, ws = perm[:S].copy(), perm[S:2 * S].copy()
+    if anchors == "mixed":
+        rs[1::3] = -1
+        ws[2::4] = -1
+    return ConvBatch(x=_cast(x, dtype), weight=_cast(weight, "f32"), bias=_cast(bias, "f32"),
+                     cu_seqlens=torch.from_numpy(cu), conv_states=_cast(states, dtype),
+                     read_slot=torch.from_numpy(rs), write_slot=torch.from_numpy(ws), silu=silu,
+                     dtype=dtype, name=name)
+
+
+def make_conv_config() -> ConvBatch:
+    c = CONV_CONFIG
+    return make_conv_inputs(c["lengths"], c["channels"], c["width"], c["num_slots"], dtype=c["dtype"],
+                            seed=c["seed"], silu=c["silu"], name=c["name"])

@@ -12,7 +12,8 @@ import numpy as np
 
 import oracle
 from ssd_brute import chunked, semiseparable
-from selective_state_space_cu_amd.workloads import make_config, make_decode_inputs, make_inputs
+from selective_state_space_cu_amd.workloads import (make_config, make_conv_inputs, make_decode_inputs,
+                                                     make_inputs)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -476,10 +477,129 @@ def pin_decode_continues_prefill(lib):
     _close(cb[free], fr, 1e-12, "two chained decode steps state")
 
 
+# ---- varlen causal conv1d with a conv-state cache ------------------------------
+
+def _conv(lib, b, states=None, rs=None, ws=None, silu=None, bias="keep"):
+    return oracle.causal_conv1d(b.x, b.cu_seqlens, b.weight, b.bias if bias == "keep" else bias,
+                                b.silu if silu is None else silu,
+                                b.conv_states if states is None else states,
+                                b.read_slot if rs is None else rs, b.write_slot if ws is None else ws,
+                                lib=lib)
+
+
+def pin_conv_is_numpy_convolve(lib):
+    """No cached state, identity activation: each sequence's channel c is
+    numpy.convolve(x_s[:, c], weight[c] reversed) truncated to the sequence,
+    plus bias[c] (widths 1-4, empty and shorter-than-window sequences). Then
+    with a cached state: the convolution of the cached rows followed by the
+    sequence, keeping the sequence's outputs."""
+    for W, lengths, seed in ((4, [7, 0, 2, 11], 61), (3, [1, 5], 62), (2, [6, 3, 4], 63), (1, [3, 4], 64)):
+        b = make_conv_inputs(lengths, 5, W, 2 * len(lengths), seed=seed, silu=False)
+        none = -np.ones(len(lengths), np.int32)
+        out, _, rc = _conv(lib, b, rs=none)
+        assert rc == 0
+        x, w, bias = b.x.double().numpy(), b.weight.double().numpy(), b.bias.double().numpy()
+        cu = b.cu_seqlens.numpy()
+        states = b.conv_states.double().numpy()
+        out2, _, _ = _conv(lib, b)
+        for s in range(len(lengths)):
+            xs = x[cu[s]:cu[s + 1]]
+            if len(xs) == 0:   # no outputs (its state is pinned below)
+                continue
+            pre = np.concatenate([states[b.read_slot[s]], xs], 0)
+            for c in range(5):
+                want = np.convolve(xs[:, c], w[c, ::-1])[:len(xs)] + bias[c]
+                _close(out[cu[s]:cu[s + 1], c], want, 1e-13, f"conv vs numpy.convolve W={W} s={s}")
+                want2 = np.convolve(pre[:, c], w[c, ::-1])[W - 1:W - 1 + len(xs)] + bias[c]
+                _close(out2[cu[s]:cu[s + 1], c], want2, 1e-13, f"conv after cached rows W={W} s={s}")
+
+
+def pin_conv_silu(lib):
+    """Width 1, weight 1, bias 0: the output is SiLU(x) = x * logistic(x), with
+    the logistic from scipy; with silu off it is x itself."""
+    from scipy.special import expit
+    b = make_conv_inputs([9, 4], 6, 1, 4, seed=65)
+    b.weight = torch_ones(6, 1)
+    b.x = b.x * 4.0
+    x = b.x.double().numpy()
+    out, _, _ = _conv(lib, b, silu=True, bias=None)
+    _close(out, x * expit(x), 1e-14, "SiLU")
+    out, _, _ = _conv(lib, b, silu=False, bias=None)
+    _close(out, x, 0.0, "identity activation")
+
+
+def torch_ones(*shape):
+    import torch
+    return torch.ones(*shape)
+
+
+def pin_conv_state_rows(lib):
+    """The written state is the last W-1 rows of (cached rows, then the
+    sequence): for long sequences the sequence's last W-1 inputs in order; for
+    short and empty ones the tail of the cached rows followed by the inputs.
+    Slots not written keep their contents; a write slot of -1 writes nothing;
+    a read slot of -1 means zero leading inputs; a slot past the cache is
+    refused (status -2, that sequence skipped)."""
+    W = 4
+    b = make_conv_inputs([10, 2, 0, 1, 5], 3, W, 12, seed=66, anchors="dual")
+    _, st, rc = _conv(lib, b)
+    assert rc == 0
+    x, s0 = b.x.double().numpy(), b.conv_states.double().numpy()
+    cu = b.cu_seqlens.numpy()
+    for s in range(5):
+        rows = np.concatenate([s0[b.read_slot[s]], x[cu[s]:cu[s + 1]]], 0)[-(W - 1):]
+        assert np.array_equal(st[b.write_slot[s]], rows), f"state rows of sequence {s}"
+    untouched = np.setdiff1d(np.arange(12), b.write_slot.numpy())
+    assert np.array_equal(st[untouched], s0[untouched]), "conv wrote an unlisted slot"
+    ws = b.write_slot.numpy().copy()
+    ws[1] = -1
+    _, st2, _ = _conv(lib, b, ws=ws)
+    assert np.array_equal(st2[b.write_slot[1]], s0[b.write_slot[1]]), "write slot -1 wrote"
+    zero = s0.copy()
+    zero[b.read_slot[3]] = 0.0
+    rs = b.read_slot.numpy().copy()
+    rs[3] = -1
+    o1, _, _ = _conv(lib, b, rs=rs)
+    o2, _, _ = _conv(lib, b, states=zero)
+    assert np.array_equal(o1, o2), "read slot -1 differs from a zero state"
+    bad = b.read_slot.numpy().copy()
+    bad[2] = 12
+    o3, st3, rc = _conv(lib, b, rs=bad)
+    o4, st4, _ = _conv(lib, b)
+    assert rc == -2, "slot past the cache not refused"
+    keep = np.setdiff1d(np.arange(5), [2])
+    assert np.array_equal(st3[b.write_slot[keep]], st4[b.write_slot[keep]])
+    assert np.array_equal(st3[b.write_slot[2]], s0[b.write_slot[2]]), "refused sequence wrote"
+
+
+def pin_conv_split_invariance(lib):
+    """A sequence convolved in two parts, the first part's state written to a
+    slot that the second part reads, gives the same outputs and final state as
+    the whole sequence (split points inside and at the window's reach)."""
+    W, L = 4, 13
+    whole = make_conv_inputs([L], 4, W, 2, seed=67)
+    x = whole.x.double().numpy()
+    out, st, _ = _conv(lib, whole)
+    for cut in (1, 2, 3, 7, 12):
+        b1 = make_conv_inputs([cut], 4, W, 2, seed=67)
+        b1.x = whole.x[:cut]
+        b1.weight, b1.bias, b1.conv_states = whole.weight, whole.bias, whole.conv_states
+        o1, s1, _ = _conv(lib, b1, rs=whole.read_slot, ws=np.array([1 - whole.read_slot[0]], np.int32))
+        b2 = make_conv_inputs([L - cut], 4, W, 2, seed=67)
+        b2.x = whole.x[cut:]
+        b2.weight, b2.bias = whole.weight, whole.bias
+        o2, s2, _ = _conv(lib, b2, states=s1, rs=np.array([1 - whole.read_slot[0]], np.int32),
+                          ws=whole.write_slot)
+        _close(np.concatenate([o1, o2], 0), out, 1e-14, f"split at {cut}: outputs")
+        assert np.array_equal(s2[whole.write_slot[0]], st[whole.write_slot[0]]), f"split at {cut}: state"
+    del x
+
+
 ALL_PINS = [pin_brute_force_semiseparable, pin_scalar_closed_form, pin_linear_attention,
             pin_diagonal_limit, pin_zero_dt, pin_superposition, pin_no_leakage,
             pin_chunked_decomposition, pin_initial_state_decay, pin_768_token_chunk128,
             pin_metadata_enumeration, pin_metadata_golden_tiny,
             pin_plan_prefix_cache_closed_form, pin_plan_misaligned_and_resume,
             pin_plan_scatter_equals_gather, pin_decode_is_one_recurrence_token,
-            pin_decode_limits, pin_decode_anchor_rules, pin_decode_continues_prefill]
+            pin_decode_limits, pin_decode_anchor_rules, pin_decode_continues_prefill,
+            pin_conv_is_numpy_convolve, pin_conv_silu, pin_conv_state_rows, pin_conv_split_invariance]

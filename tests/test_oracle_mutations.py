@@ -45,6 +45,17 @@ MUTATIONS = [
     ("decode_no_bias", [("dt[s * H + hd] + (dt_bias ? dt_bias[hd] : 0.0)", "dt[s * H + hd]")]),
     ("decode_drop_D", [("(D ? D[hd] : 0.0) * xs[p]", "0.0 * xs[p]")]),
     ("decode_bad_slot_not_refused", [("            bad = 1;", "            bad = 0;")]),
+    # the varlen causal conv1d
+    ("conv_taps_reversed", [("z += weight[c * W + k] * u;", "z += weight[c * W + (W - 1 - k)] * u;")]),
+    ("conv_no_bias", [("double z = bias ? bias[c] : 0.0;", "double z = 0.0;")]),
+    ("conv_silu_sign", [("z / (1.0 + exp(-z))", "z / (1.0 + exp(z))")]),
+    ("conv_cached_rows_ignored", [("if (r >= 0 && per_slot > 0)", "if (0 && per_slot > 0)")]),
+    ("conv_leaks_previous_sequence", [(
+        "const double u = jj >= 0 ? x[(t0 + jj) * Cn + c] : ps[(W - 1 + jj) * Cn + c];",
+        "const double u = t0 + jj >= 0 ? x[(t0 + jj) * Cn + c] : ps[(W - 1 + jj) * Cn + c];")]),
+    ("conv_state_rows_reversed", [("conv_states[(int64_t)w * per_slot + i * Cn + c] =",
+                                   "conv_states[(int64_t)w * per_slot + (W - 2 - i) * Cn + c] =")]),
+    ("conv_bad_slot_not_refused", [("bad |= 1;", "bad |= 0;")]),
 ]
 
 
