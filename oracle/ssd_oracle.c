@@ -381,8 +381,8 @@ int oracle_causal_conv1d(int32_t nseqs, const int32_t *cu_seqlens, int32_t chann
             continue;
         const int64_t t0 = cu_seqlens[s], L = cu_seqlens[s + 1] - cu_seqlens[s];
         const double *ps = pre + (int64_t)s * per_slot;
-        for (int64_t c = 0; c < Cn; ++c) {
-            for (int64_t j = 0; j < L; ++j) {
+        for (int64_t j = 0; j < L; ++j) {   /* (rows outer: the memory order of x and out) */
+            for (int64_t c = 0; c < Cn; ++c) {
                 double z = bias ? bias[c] : 0.0;
                 for (int64_t k = 0; k < W; ++k) {
                     const int64_t jj = j - (W - 1) + k;   /* input position of tap k */
@@ -391,6 +391,8 @@ int oracle_causal_conv1d(int32_t nseqs, const int32_t *cu_seqlens, int32_t chann
                 }
                 out[(t0 + j) * Cn + c] = silu ? z / (1.0 + exp(-z)) : z;
             }
+        }
+        for (int64_t c = 0; c < Cn; ++c) {
             if (w >= 0) {
                 for (int64_t i = 0; i < W - 1; ++i) {
                     const int64_t jj = L - (W - 1) + i;
