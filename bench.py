@@ -28,6 +28,8 @@ DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_dual_anchor_256_counter
 KERNEL_SOURCES = ["ssd_scan.hpp", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_internal.h",
                   "ssd_scan_split.hpp", "ssd_scan_split_bf16.hip"]
 DECODE_SOURCES = ["ssd_decode.hip", "ssd_scan.hpp", "ssd_internal.h"]
+CONV_COUNTERS = os.path.join(ROOT, "profiles", "conv1d_prefix_cache_4x8894_counters.json")
+CONV_SOURCES = ["ssd_conv1d.hip", "ssd_scan.hpp", "ssd_internal.h"]
 
 
 def kernel_hash(sources=KERNEL_SOURCES):
@@ -43,9 +45,9 @@ def ingest_counters(fetch_csv, write_csv, config, calib_mib, workload="prefill",
     then WRITE_SIZE; KiB per dispatch) into the HBM traffic of one launch of the
     workload's kernel, each counter scaled by what it reads for the calibration
     kernel (one elementwise pass that reads and writes M MiB)."""
-    decode = workload == "decode"
-    out = out or (DECODE_COUNTERS if decode else COUNTERS)
-    tag = "ssd_decode" if decode else "ssd_scan"
+    decode, conv = workload == "decode", workload == "conv1d"
+    out = out or (DECODE_COUNTERS if decode else CONV_COUNTERS if conv else COUNTERS)
+    tag = "ssd_decode" if decode else "ssd_conv1d" if conv else "ssd_scan"
     import csv
 
     def read(path):
@@ -66,9 +68,9 @@ def ingest_counters(fetch_csv, write_csv, config, calib_mib, workload="prefill",
     calib_kib = calib_mib * 1024.0
     ff, fw = calib_kib / cal_f, calib_kib / cal_w
     fk, wk = sum(scan_f) / len(scan_f), sum(scan_w) / len(scan_w)
-    rec = {"kernel": "ssd_decode_kernel" if decode else scan_kernel_name(config),
-           "kernel_hash": kernel_hash(DECODE_SOURCES if decode else KERNEL_SOURCES),
-           "config": "decode" if decode else config,
+    rec = {"kernel": "ssd_decode_kernel" if decode else "ssd_conv1d_kernel" if conv else scan_kernel_name(config),
+           "kernel_hash": kernel_hash(DECODE_SOURCES if decode else CONV_SOURCES if conv else KERNEL_SOURCES),
+           "config": workload if (decode or conv) else config,
            "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": len(scan_f),
            "calibration_mib": calib_mib, "calibration_fetch_kib": cal_f, "calibration_write_kib": cal_w,
            "fetch_scale": ff, "write_scale": fw,
@@ -232,6 +234,103 @@ def cpu_baseline_decode(b, nseqs=64):
                        f"float64 widening of their {nseqs} state slots")
 
 
+def conv1d_work(b):
+    """Algorithmic bytes of one conv1d call: x read and out written once, each
+    read slot's and write slot's W-1 rows once, weights and bias once."""
+    T, C = b.x.shape
+    W = b.weight.shape[1]
+    sx = 2 if b.dtype == "bf16" else 4
+    n_read = int((b.read_slot >= 0).sum())
+    n_write = int((b.write_slot >= 0).sum())
+    return 2 * T * C * sx + (n_read + n_write) * (W - 1) * C * sx + C * W * 4 + C * 4
+
+
+def bench_conv1d(args):
+    """One JSON line for the varlen causal conv1d on the prefix-cache batch's
+    channels; a step is the chunk metadata plus the convolution."""
+    import torch
+    from selective_state_space_cu_amd import ssd
+    from selective_state_space_cu_amd.workloads import CONV_CONFIG, make_conv_config
+
+    b = make_conv_config()
+    dev = torch.device("cuda:0")
+    d = {k: getattr(b, k).to(dev).contiguous() for k in
+         ("x", "weight", "bias", "cu_seqlens", "conv_states", "read_slot", "write_slot")}
+    T = int(b.cu_seqlens[-1])
+    out = torch.empty_like(d["x"])
+    ev = []
+
+    def step(timed):
+        meta = ssd.varlen_metadata(d["cu_seqlens"], CONV_CONFIG["chunk_size"], total_tokens=T)
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        ssd.causal_conv1d_varlen(d["x"], d["weight"], meta, bias=d["bias"], silu=b.silu,
+                                 conv_states=d["conv_states"], read_slot=d["read_slot"],
+                                 write_slot=d["write_slot"], out=out)
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+        return meta
+
+    for _ in range(args.warmup):
+        meta = step(False)
+    torch.cuda.synchronize()
+    if int(meta.error_flag.item()) != 0:
+        raise RuntimeError("device error flag set")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = sum(a.elapsed_time(e) for a, e in ev) / len(ev)
+    if args.copy_calib_mib:
+        calib_copy(args.copy_calib_mib, dev)
+    alg = conv1d_work(b)
+    traffic = None
+    if os.path.exists(CONV_COUNTERS):
+        with open(CONV_COUNTERS) as f:
+            c = json.load(f)
+        if c.get("kernel_hash") == kernel_hash(CONV_SOURCES):
+            traffic = c["hbm_bytes_per_launch"]
+    ms_per_step = wall * 1e3 / args.steps
+    res = {
+        "metric": "Varlen causal conv1d tokens/s on 1 MI355X; % of HBM roofline",
+        "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype,
+        "data": "synthetic (seeded; inputs and conv-state cache resident in HBM)",
+        "config": {"workload": CONV_CONFIG["name"], "nseqs": len(CONV_CONFIG["lengths"]),
+                   "total_tokens": T, "channels": CONV_CONFIG["channels"], "width": CONV_CONFIG["width"],
+                   "activation": "silu" if b.silu else "identity", "chunk_size": CONV_CONFIG["chunk_size"],
+                   "num_slots": CONV_CONFIG["num_slots"],
+                   "step": "chunk metadata + conv1d (read slot -> window -> write slot)"},
+        "roofline": {"bound": "hbm", "kernel": "ssd_conv1d_kernel",
+                     "achieved": alg / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": alg, "kernel_ms": k_ms},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_conv1d(b)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_conv1d(b):
+    """The float64 conv1d oracle (single thread) over the whole workload."""
+    import oracle
+    t = time.perf_counter()
+    oracle.causal_conv1d(b.x, b.cu_seqlens, b.weight, b.bias, b.silu, b.conv_states, b.read_slot,
+                         b.write_slot)
+    dt_s = time.perf_counter() - t
+    T = int(b.cu_seqlens[-1])
+    return dict(value=T / dt_s, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"the whole workload ({T} tokens, all {b.x.shape[1]} channels), float64, "
+                       f"single thread (the conv oracle is not threaded); {dt_s:.2f} s wall "
+                       f"including the float64 widening of x")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,9 +341,10 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
-    ap.add_argument("--workload", choices=("prefill", "decode"), default="prefill",
+    ap.add_argument("--workload", choices=("prefill", "decode", "conv1d"), default="prefill",
                     help="prefill (default): the scan step; decode: one dual-anchor decode step "
-                         "per sequence on the 256-sequence decode batch")
+                         "per sequence on the 256-sequence decode batch; conv1d: the causal conv1d "
+                         "before the scan on the prefix-cache batch's 5120 channels")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from two rocprofv3 counter CSVs and exit "
                          "(with --copy-calib-mib giving the calibration size)")
@@ -261,6 +361,9 @@ def main():
 
     if args.workload == "decode":
         bench_decode(args)
+        return
+    if args.workload == "conv1d":
+        bench_conv1d(args)
         return
     import torch
     from selective_state_space_cu_amd import ssd

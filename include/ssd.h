@@ -223,6 +223,45 @@ ssd_status ssd_decode_step(
 /* Static, NUL-terminated description of a status code. */
 const char *ssd_status_string(ssd_status status);
 
+/*
+ * Varlen causal conv1d with a conv-state cache: the depthwise causal
+ * convolution that produces the scan's inputs (the causal_conv1d kernel named
+ * on the prefix-caching page, whose conv metadata that page builds together
+ * with the rest of the batch metadata; here the kernel walks the chunk grid of
+ * `meta`, filled by ssd_varlen_metadata on the same stream). The pages name the
+ * kernel without its formula; this is the standard Mamba2 depthwise causal
+ * convolution. For sequence s (tokens cu[s] .. cu[s+1]-1, L of them), token j
+ * and channel c, with W = width:
+ *     u_j = x[cu[s]+j, c]                               (j >= 0)
+ *     u_j = conv_states[read_slot[s], W-1+j, c]         (-(W-1) <= j < 0; zero when read_slot[s] < 0)
+ *     out[cu[s]+j, c] = act(bias[c] + sum_k weight[c,k] * u_{j-(W-1)+k})
+ *     conv_states[write_slot[s], i, c] = u_{L-(W-1)+i}  (i = 0..W-2; skipped when write_slot[s] < 0)
+ * act: activation 0 = identity, 1 = SiLU z / (1 + e^-z). Arithmetic in fp32
+ * (fmaf over the taps in order, bias first), output rounded to nearest even.
+ *
+ *  x, out        element type `in_dtype`, (T, channels) row-major, 16-byte aligned
+ *  weight        float32 (channels, width); bias float32 (channels) or NULL (= 0)
+ *  conv_states   element type `in_dtype`, (num_slots, width-1, channels), 16-byte
+ *                aligned; the last W-1 inputs of a sequence, oldest first
+ *  read_slot, write_slot  int32 (nseqs) or NULL (= all -1): dual anchors
+ *  channels      multiple of 8; width 1..4
+ * Preconditions: write slots are distinct, and none is another sequence's read
+ * slot; a sequence may read and write the same slot only if it spans at most
+ * one chunk (its reads and its write are then made by the same lanes).
+ * Empty sequences copy their read state (or zeros) to their write slot.
+ * Errors: SSD_ERR_NULL_ARG, SSD_ERR_SHAPE (channels <= 0, num_slots < 0,
+ * misaligned buffers), SSD_ERR_UNSUPPORTED (channels % 8, width outside 1..4,
+ * unknown activation), SSD_ERR_DTYPE, SSD_ERR_CHUNK_SIZE / SSD_ERR_CAPACITY
+ * (meta), SSD_ERR_HIP. Device data error: SSD_DATA_BAD_SLOT in
+ * meta->error_flag (a slot >= num_slots; that sequence is skipped: nothing of
+ * it read or written).
+ */
+ssd_status ssd_causal_conv1d_varlen(
+    const void *x, const float *weight, const float *bias, ssd_dtype in_dtype,
+    const ssd_varlen_meta *meta, int32_t channels, int32_t width, int32_t activation,
+    void *conv_states, int32_t num_slots, const int32_t *read_slot, const int32_t *write_slot,
+    void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -163,4 +163,33 @@ ssd_status ssd_decode_step(const void *x, const float *dt, const float *dt_bias,
                ? SSD_OK : SSD_ERR_HIP;
 }
 
+ssd_status ssd_causal_conv1d_varlen(const void *x, const float *weight, const float *bias,
+                                    ssd_dtype in_dtype, const ssd_varlen_meta *meta, int32_t channels,
+                                    int32_t width, int32_t activation, void *conv_states,
+                                    int32_t num_slots, const int32_t *read_slot,
+                                    const int32_t *write_slot, void *out, void *stream) {
+    ssd_status st = check_meta(meta);
+    if (st != SSD_OK) return st;
+    if (in_dtype != SSD_F32 && in_dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    if (channels <= 0 || num_slots < 0) return SSD_ERR_SHAPE;
+    if (channels % 8 != 0 || width < 1 || width > 4 || (activation != 0 && activation != 1))
+        return SSD_ERR_UNSUPPORTED;
+    if (weight == nullptr || (meta->total_tokens > 0 && (x == nullptr || out == nullptr)))
+        return SSD_ERR_NULL_ARG;
+    if (width > 1 && num_slots > 0 && (read_slot != nullptr || write_slot != nullptr) && conv_states == nullptr)
+        return SSD_ERR_NULL_ARG;
+    for (const void *p : {x, (const void *)out, (const void *)conv_states})
+        if (p != nullptr && !aligned16(p)) return SSD_ERR_SHAPE;
+    ssd::Conv1dArgs a{};
+    a.x = x; a.weight = weight; a.bias = bias; a.out = out; a.states = conv_states;
+    a.read_slot = read_slot; a.write_slot = write_slot;
+    a.chunk_offsets = meta->chunk_offsets; a.chunk_seq_idx = meta->chunk_seq_idx;
+    a.seq_chunk_start = meta->seq_chunk_start; a.error_flag = meta->error_flag;
+    a.S = meta->nseqs; a.C = channels; a.W = width; a.num_slots = (conv_states != nullptr || width == 1) ? num_slots : 0;   // (width 1 keeps no rows)
+    a.max_chunks = meta->max_chunks; a.channel_blocks = ssd::conv1d_channel_blocks(channels);
+    a.silu = activation;
+    return ssd::launch_conv1d(a, in_dtype == SSD_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SSD_OK : SSD_ERR_HIP;
+}
+
 }  // extern "C"

@@ -82,6 +82,21 @@ struct DecodeArgs {
     int32_t S, H, P, G, num_slots, pchunks;
 };
 int32_t decode_pchunks(int32_t headdim, int32_t dstate);   // workgroups per (sequence, head)
+
+// Varlen causal conv1d over the scan's chunk grid (see ssd_conv1d.hip).
+struct Conv1dArgs {
+    const void *x;            // (T, C) bf16 or f32
+    const float *weight;      // (C, W)
+    const float *bias;        // (C) or null
+    void *out;                // (T, C), element type of x
+    void *states;             // (num_slots, W-1, C), element type of x
+    const int32_t *read_slot, *write_slot;   // (S) or null (= all -1)
+    const int32_t *chunk_offsets, *chunk_seq_idx, *seq_chunk_start;   // the batch's chunk grid
+    int32_t *error_flag;
+    int32_t S, C, W, num_slots, max_chunks, channel_blocks, silu;
+};
+int32_t conv1d_channel_blocks(int32_t channels);   // workgroups per chunk
+hipError_t launch_conv1d(const Conv1dArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, int dstate, hipStream_t stream);
 
 struct MetaArgs {

@@ -21,7 +21,7 @@ DATA_BAD_CU_SEQLENS, DATA_TOO_MANY_CHUNKS, DATA_BAD_SLOT, DATA_BAD_BLOCK = 1, 2,
 
 # names exported by libssd.so (checked by the CPU tests against include/ssd.h)
 EXPORTS = ("ssd_varlen_metadata", "ssd_chunk_scan_varlen", "ssd_export_chunk_states",
-           "ssd_decode_step", "ssd_status_string")
+           "ssd_decode_step", "ssd_causal_conv1d_varlen", "ssd_status_string")
 
 
 class SSDError(RuntimeError):
@@ -67,6 +67,9 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_decode_step.restype = st
     lib.ssd_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, st, i32, i32, i32, i32, i32, vp, i32,
                                     vp, vp, vp, vp, vp]
+    lib.ssd_causal_conv1d_varlen.restype = st
+    lib.ssd_causal_conv1d_varlen.argtypes = [vp, vp, vp, st, ctypes.POINTER(_Meta), i32, i32, i32, vp, i32,
+                                             vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -272,3 +275,37 @@ def decode_step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
         S, H, P, N, G, _ptr(state_cache), state_cache.shape[0], _ptr(rs), _ptr(ws), _ptr(y),
         _ptr(error_flag), _stream(device)))
     return y
+
+
+def causal_conv1d_varlen(x: torch.Tensor, weight: torch.Tensor, meta: VarlenMeta,
+                         bias: Optional[torch.Tensor] = None, silu: bool = True,
+                         conv_states: Optional[torch.Tensor] = None,
+                         read_slot: Optional[torch.Tensor] = None,
+                         write_slot: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None):
+    """ssd_causal_conv1d_varlen: depthwise causal conv1d of x (T, C) with
+    weight (C, W) float32 over the chunk grid of `meta`; the W-1 inputs before
+    each sequence come from conv_states[read_slot[s]] (zero if < 0) and its last
+    W-1 inputs go to conv_states[write_slot[s]] (skipped if < 0); conv_states
+    (slots, W-1, C) has x's dtype. Returns out (T, C)."""
+    lib = load_library()
+    device = x.device
+    _data(x, "x", device)
+    T, C = x.shape
+    W = weight.shape[1]
+    _data(weight, "weight", device, torch.float32)
+    if bias is not None:
+        _data(bias, "bias", device, torch.float32)
+    if conv_states is not None:
+        _data(conv_states, "conv_states", device, x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    _data(out, "out", device, x.dtype)
+    rs = _index(read_slot, device) if read_slot is not None else None
+    ws = _index(write_slot, device) if write_slot is not None else None
+    m = meta.c_struct()
+    _check("ssd_causal_conv1d_varlen", lib.ssd_causal_conv1d_varlen(
+        _ptr(x), _ptr(weight), _ptr(bias), _dtype_code(x), ctypes.byref(m), C, W, int(bool(silu)),
+        _ptr(conv_states), 0 if conv_states is None else conv_states.shape[0], _ptr(rs), _ptr(ws),
+        _ptr(out), _stream(device)))
+    return out

@@ -130,3 +130,34 @@ def test_decode_rejects_bad_arguments(kw, code):
 
 def test_decode_empty_batch_launches_nothing():
     assert _decode(S=0, x=None, dt=None, B=None, C=None, y=None, cache=None, rs=None, ws=None) == 0
+
+
+def _conv(m=None, **kw):
+    args = dict(x=FAKE, w=FAKE, bias=None, dtype=1, C=64, W=4, act=1, states=FAKE, slots=8, rs=FAKE,
+                ws=FAKE, out=FAKE)
+    args.update(kw)
+    lib = ssd.load_library()
+    m = _meta() if m is None else m
+    return lib.ssd_causal_conv1d_varlen(args["x"], args["w"], args["bias"], args["dtype"], ctypes.byref(m),
+                                        args["C"], args["W"], args["act"], args["states"], args["slots"],
+                                        args["rs"], args["ws"], args["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 6), (dict(C=0), 3), (dict(C=-8), 3), (dict(slots=-1), 3), (dict(C=12), 8),
+    (dict(W=0), 8), (dict(W=5), 8), (dict(act=2), 8), (dict(x=None), 1), (dict(out=None), 1),
+    (dict(w=None), 1), (dict(states=None), 1), (dict(states=FAKE + 4), 3), (dict(x=FAKE + 8), 3),
+    (dict(out=FAKE + 2), 3),
+])
+def test_conv1d_rejects_bad_arguments(kw, code):
+    assert _conv(**kw) == code
+
+
+def test_conv1d_rejects_bad_meta():
+    assert _conv(m=_meta(null_field="chunk_seq_idx")) == 1
+    assert _conv(m=_meta(cs=48)) == 2
+    assert _conv(m=_meta(max_chunks=1)) == 5
+
+
+def test_conv1d_empty_batch_launches_nothing():
+    assert _conv(m=_meta(S=0, T=0, max_chunks=0), x=None, out=None, states=None, rs=None, ws=None) == 0

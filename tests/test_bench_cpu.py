@@ -80,3 +80,13 @@ def test_counter_ingest_counts_only_the_steps_before_the_calibration_copy(tmp_pa
     assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
     assert rec["hbm_bytes_per_launch"] == (800.0 * 2.0 + 800.0 * 1.0) * 1024.0
     assert _json.load(open(out)) == rec
+
+
+def test_conv1d_algorithmic_bytes():
+    """4 x 8894 tokens x 5120 bf16 channels read and written, 4 read and 4
+    written slots of 3 x 5120 bf16, 5120 x 4 + 5120 float32 weights and bias."""
+    from selective_state_space_cu_amd.workloads import make_conv_config
+    b = make_conv_config()
+    want = 2 * 35576 * 5120 * 2 + 8 * 3 * 5120 * 2 + 5120 * 4 * 4 + 5120 * 4
+    assert want == 728_944_640
+    assert bench.conv1d_work(b) == want
