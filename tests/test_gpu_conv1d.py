@@ -145,3 +145,13 @@ def test_conv1d_full_size_prefix_cache_channels():
     ref, st_ref, rc, mag = _ref(b)
     assert rc == 0 and flag == 0
     _compare(b, got, st, ref, st_ref, mag, b.name)
+
+
+def test_conv1d_decode_shaped_batch():
+    """One token per sequence (the conv state advanced by one step, as in decode
+    with dual anchors): 128 sequences, width 4, SiLU, mixed anchors."""
+    b = make_conv_inputs([1] * 128, 5120, 4, 300, dtype="bf16", seed=80, anchors="mixed")
+    got, st, flag = _run(b, 16)
+    ref, st_ref, rc, mag = _ref(b)
+    assert rc == 0 and flag == 0
+    _compare(b, got, st, ref, st_ref, mag, "decode-shaped conv1d")
