@@ -102,6 +102,13 @@ def _data(t: torch.Tensor, name: str, device, dtype=None):
     return t
 
 
+def _shape(t: Optional[torch.Tensor], name: str, *shape):
+    """The kernels index every buffer from the sizes passed beside it: a tensor of
+    another shape would be read or written out of its bounds, so refuse it here."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _index(t: torch.Tensor, device):
     """Index arrays are normalised to contiguous int32 on the device."""
     t = t.to(device=device, dtype=torch.int32)
@@ -184,6 +191,17 @@ def chunk_scan_varlen(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: tor
     G, N = B.shape[1], B.shape[2]
     S = meta.nseqs
     _data(x, "x", device)
+    if T != meta.total_tokens:
+        raise ValueError(f"x has {T} tokens, the metadata {meta.total_tokens}")
+    for name, t, shp in (("B", B, (T, G, N)), ("C", C, (T, G, N)), ("dt", dt, (T, H)), ("A", A, (H,)),
+                         ("dt_bias", dt_bias, (H,)), ("D", D, (H,)),
+                         ("initial_states", initial_states, (S, H, P, N)), ("y", y, (T, H, P)),
+                         ("final_states", final_states, (S, H, P, N))):
+        _shape(t, name, *shp)
+    if has_initial_state is not None:
+        _shape(has_initial_state, "has_initial_state", S)
+    if chunk_states is not None:
+        _shape(chunk_states, "chunk_states", chunk_states.shape[0], H, P, N)
     dtype = x.dtype
     for name, t in (("B", B), ("C", C)):
         _data(t, name, device, dtype)
@@ -255,6 +273,11 @@ def decode_step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
     S, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     _data(x, "x", device)
+    for name, t, shp in (("B", B, (S, G, N)), ("C", C, (S, G, N)), ("dt", dt, (S, H)), ("A", A, (H,)),
+                         ("dt_bias", dt_bias, (H,)), ("D", D, (H,)), ("y", y, (S, H, P)),
+                         ("state_cache", state_cache, (state_cache.shape[0], H, P, N)),
+                         ("read_slot", read_slot, (S,)), ("write_slot", write_slot, (S,))):
+        _shape(t, name, *shp)
     dtype = x.dtype
     for name, t in (("B", B), ("C", C)):
         _data(t, name, device, dtype)
@@ -293,6 +316,14 @@ def causal_conv1d_varlen(x: torch.Tensor, weight: torch.Tensor, meta: VarlenMeta
     _data(x, "x", device)
     T, C = x.shape
     W = weight.shape[1]
+    if T != meta.total_tokens:
+        raise ValueError(f"x has {T} tokens, the metadata {meta.total_tokens}")
+    S = meta.nseqs
+    for name, t, shp in (("weight", weight, (C, W)), ("bias", bias, (C,)), ("out", out, (T, C)),
+                         ("read_slot", read_slot, (S,)), ("write_slot", write_slot, (S,))):
+        _shape(t, name, *shp)
+    if conv_states is not None:
+        _shape(conv_states, "conv_states", conv_states.shape[0], W - 1, C)
     _data(weight, "weight", device, torch.float32)
     if bias is not None:
         _data(bias, "bias", device, torch.float32)

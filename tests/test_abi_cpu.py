@@ -161,3 +161,35 @@ def test_conv1d_rejects_bad_meta():
 
 def test_conv1d_empty_batch_launches_nothing():
     assert _conv(m=_meta(S=0, T=0, max_chunks=0), x=None, out=None, states=None, rs=None, ws=None) == 0
+
+
+def test_bindings_refuse_mismatched_shapes():
+    """The Python bindings check every tensor's shape against x, B and the
+    metadata before anything reaches the device."""
+    import torch
+    z = lambda *s, dt=torch.float32: torch.zeros(*s, dtype=dt)
+    meta = ssd.VarlenMeta(2, 10, 16, 3, *([z(1, dt=torch.int32)] * 7))
+    x = z(10, 16)
+    with pytest.raises(ValueError, match="weight"):
+        ssd.causal_conv1d_varlen(x, z(8, 4), meta)
+    with pytest.raises(ValueError, match="conv_states"):
+        ssd.causal_conv1d_varlen(x, z(16, 4), meta, conv_states=z(4, 4, 16))
+    with pytest.raises(ValueError, match="read_slot"):
+        ssd.causal_conv1d_varlen(x, z(16, 4), meta, read_slot=z(3, dt=torch.int32))
+    with pytest.raises(ValueError, match="tokens"):
+        ssd.causal_conv1d_varlen(z(11, 16), z(16, 4), meta)
+    xs = z(10, 4, 8)
+    with pytest.raises(ValueError, match="B must"):
+        ssd.chunk_scan_varlen(xs, z(10, 4), z(4), z(9, 2, 16), z(9, 2, 16), meta)
+    with pytest.raises(ValueError, match="C must"):
+        ssd.chunk_scan_varlen(xs, z(10, 4), z(4), z(10, 2, 16), z(10, 2, 8), meta)
+    with pytest.raises(ValueError, match="initial_states"):
+        ssd.chunk_scan_varlen(xs, z(10, 4), z(4), z(10, 2, 16), z(10, 2, 16), meta,
+                              initial_states=z(3, 4, 8, 16))
+    xd = z(3, 4, 8)
+    with pytest.raises(ValueError, match="write_slot"):
+        ssd.decode_step(xd, z(3, 4), z(4), z(3, 2, 16), z(3, 2, 16), z(6, 4, 8, 16),
+                        z(3, dt=torch.int32), z(2, dt=torch.int32))
+    with pytest.raises(ValueError, match="state_cache"):
+        ssd.decode_step(xd, z(3, 4), z(4), z(3, 2, 16), z(3, 2, 16), z(6, 4, 8, 32),
+                        z(3, dt=torch.int32), z(3, dt=torch.int32))
