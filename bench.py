@@ -23,7 +23,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
-COUNTERS = os.path.join(ROOT, "profiles", "scan_prefix_cache_4x8894_counters.json")
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_dual_anchor_256_counters.json")
 KERNEL_SOURCES = ["ssd_scan.hpp", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_internal.h",
                   "ssd_scan_split.hpp", "ssd_scan_split_bf16.hip"]
@@ -46,7 +45,7 @@ def ingest_counters(fetch_csv, write_csv, config, calib_mib, workload="prefill",
     workload's kernel, each counter scaled by what it reads for the calibration
     kernel (one elementwise pass that reads and writes M MiB)."""
     decode, conv = workload == "decode", workload == "conv1d"
-    out = out or (DECODE_COUNTERS if decode else CONV_COUNTERS if conv else COUNTERS)
+    out = out or (DECODE_COUNTERS if decode else CONV_COUNTERS if conv else counter_path(config))
     tag = "ssd_decode" if decode else "ssd_conv1d" if conv else "ssd_scan"
     import csv
 
@@ -339,6 +338,10 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cold-calls", type=int, default=50,
+                    help="HBM-cold timed scans per graded workload (flush write before each)")
+    ap.add_argument("--single-config", dest="all_configs", action="store_false",
+                    help="cold protocol on --config only (default: every graded prefill workload)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     ap.add_argument("--workload", choices=("prefill", "decode", "conv1d"), default="prefill",
@@ -367,69 +370,37 @@ def main():
         return
     import torch
     from selective_state_space_cu_amd import ssd
-    from selective_state_space_cu_amd.workloads import CONFIGS, make_config
+    from selective_state_space_cu_amd.workloads import CONFIGS
 
-    cfgd = CONFIGS[args.config]
-    w = make_config(args.config)
     dev = torch.device("cuda:0")
-    d = {k: getattr(w, k).to(dev).contiguous() for k in
-         ("x", "dt", "dt_bias", "A", "B", "C", "D", "initial_states", "has_initial_state", "cu_seqlens")}
+    flush = torch.empty(FLUSH_MIB << 20, dtype=torch.uint8, device=dev)
+    cfgd = CONFIGS[args.config]
+    run = PrefillRun(args.config, dev)
+    w = run.w
     S, T, H, P, N = w.nseqs, w.total_tokens, w.nheads, w.headdim, w.dstate
-    has_blocks = w.block_table is not None
-    bt = w.block_table.to(dev) if has_blocks else None
-    y = torch.empty_like(d["x"])
-    fin = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
-    cache = (torch.zeros((w.num_slots, H, P, N), dtype=torch.float32, device=dev)
-             if has_blocks else None)
-    init = d["initial_states"] if int(w.has_initial_state.sum()) else None
-    has = d["has_initial_state"] if init is not None else None
 
-    ev = []
-
-    def step(timed):
-        meta = ssd.varlen_metadata(d["cu_seqlens"], w.chunk_size, total_tokens=T)
-        dst = None
-        if has_blocks:
-            _, dst = ssd.export_chunk_states(meta, bt, w.block_size, num_slots=w.num_slots)
-        if timed:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-        ssd.chunk_scan_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], meta, dt_bias=d["dt_bias"],
-                              D=d["D"], initial_states=init, has_initial_state=has, y=y,
-                              final_states=fin, chunk_states=cache, chunk_state_dst=dst)
-        if timed:
-            e1.record()
-            ev.append((e0, e1))
-        return meta
-
+    # (1) the step loop: K steps back to back (metadata + plan + scan), wall
+    # clock for `value`, HIP events on the launch stream around each scan for
+    # the kernel's average duration (what a rocprofv3 trace of this command shows)
     for _ in range(args.warmup):
-        meta = step(False)
+        run.step(False)
     torch.cuda.synchronize()
-    if int(meta.error_flag.item()) != 0:
+    if int(run.meta.error_flag.item()) != 0:
         raise RuntimeError("device error flag set")
+    run.ev.clear()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        run.step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    scan_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    scan_ms = sum(a.elapsed_time(b) for a, b in run.ev) / len(run.ev)
+    meta_ms = sum(a.elapsed_time(b) for a, b in run.ev_meta) / len(run.ev_meta)
 
     if args.copy_calib_mib:
         calib_copy(args.copy_calib_mib, dev)
 
-    n_ckpt = 0
-    if has_blocks:
-        _, dst = ssd.export_chunk_states(meta, bt, w.block_size, num_slots=w.num_slots)
-        n_ckpt = int((dst >= 0).sum().item())
-    alg_bytes, alg_flops = algorithmic_work(w, n_ckpt)
+    alg_bytes, alg_flops = algorithmic_work(w, run.n_ckpt)
     achieved = alg_bytes / (scan_ms * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(COUNTERS):
-        with open(COUNTERS) as f:
-            c = json.load(f)
-        if c.get("kernel_hash") == kernel_hash() and c.get("config") == args.config:
-            traffic = c["hbm_bytes_per_launch"]
     ms_per_step = wall * 1e3 / args.steps
     out = {
         "metric": "SSD varlen prefill tokens/s on 1 MI355X; % of HBM/MFMA roofline",
@@ -446,30 +417,153 @@ def main():
         "data": "synthetic (seeded; inputs resident in HBM)",
         "config": {"workload": cfgd["name"], "nseqs": S, "total_tokens": T, "nheads": H,
                    "headdim": P, "dstate": N, "ngroups": w.ngroups, "chunk_size": w.chunk_size,
-                   "block_size": w.block_size, "checkpoints_per_step": n_ckpt,
+                   "block_size": w.block_size, "checkpoints_per_step": run.n_ckpt,
                    "step": "metadata + checkpoint plan + scan with at-source checkpoint export"},
         "roofline": {"bound": "hbm", "kernel": scan_kernel_name(args.config), "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes": alg_bytes,
-                     "kernel_ms": scan_ms,
+                     "traffic": counter_traffic(args.config), "algorithmic_bytes": alg_bytes,
+                     "kernel_ms": scan_ms, "metadata_and_plan_ms": meta_ms,
                      "mfma_tflops": alg_flops / (scan_ms * 1e-3) / 1e12,
                      "mfma_frac": alg_flops / (scan_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
     }
-    if has_blocks:
-        out["checkpoint_export"] = export_overhead(ssd, d, meta, bt, w, init, has, y, fin, cache)
+    # (2) the cold protocol on this workload and on the other graded prefill
+    # workloads: each timed scan preceded by a write of FLUSH_MIB outside the
+    # events (evicts L2 and the Infinity Cache), median / p10 / p90
+    graded = {}
+    for ci in ([args.config] + [c for c in GRADED if c != args.config] if args.all_configs else [args.config]):
+        r = run if ci == args.config else PrefillRun(ci, dev)
+        graded[CONFIGS[ci]["name"]] = cold_stats(r, flush, args.cold_calls)
+        if r is not run:
+            del r
+            torch.cuda.empty_cache()
+    out["cold"] = graded
+    if run.has_blocks:
+        out["checkpoint_export"] = export_overhead(ssd, run)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, H))
     print(json.dumps(out), flush=True)
 
 
-def export_overhead(ssd, d, meta, bt, w, init, has, y, fin, cache, rounds=6, per=10):
+GRADED = (4, 2, 3)   # the prefill workloads whose roofline fractions are reported
+FLUSH_MIB = 512
+
+
+class PrefillRun:
+    """Device inputs and outputs of one prefill workload, and its step."""
+
+    def __init__(self, config, dev):
+        import torch
+        from selective_state_space_cu_amd import ssd
+        from selective_state_space_cu_amd.workloads import make_config
+        self.ssd, self.config = ssd, config
+        w = self.w = make_config(config)
+        d = self.d = {k: getattr(w, k).to(dev).contiguous() for k in
+                      ("x", "dt", "dt_bias", "A", "B", "C", "D", "initial_states", "has_initial_state",
+                       "cu_seqlens")}
+        S, H, P, N = w.nseqs, w.nheads, w.headdim, w.dstate
+        self.has_blocks = w.block_table is not None
+        self.bt = w.block_table.to(dev) if self.has_blocks else None
+        self.y = torch.empty_like(d["x"])
+        self.fin = torch.empty((S, H, P, N), dtype=torch.float32, device=dev)
+        self.cache = (torch.zeros((w.num_slots, H, P, N), dtype=torch.float32, device=dev)
+                      if self.has_blocks else None)
+        self.init = d["initial_states"] if int(w.has_initial_state.sum()) else None
+        self.has = d["has_initial_state"] if self.init is not None else None
+        self.ev, self.ev_meta = [], []
+        self.meta, self.dst = None, None
+        self.prepare()
+        self.n_ckpt = int((self.dst >= 0).sum().item()) if self.has_blocks else 0
+
+    def prepare(self):
+        """Metadata and checkpoint plan (built once per batch)."""
+        self.meta = self.ssd.varlen_metadata(self.d["cu_seqlens"], self.w.chunk_size,
+                                             total_tokens=self.w.total_tokens)
+        self.dst = None
+        if self.has_blocks:
+            _, self.dst = self.ssd.export_chunk_states(self.meta, self.bt, self.w.block_size,
+                                                       num_slots=self.w.num_slots)
+
+    def scan(self, export=True):
+        d = self.d
+        self.ssd.chunk_scan_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], self.meta,
+                                   dt_bias=d["dt_bias"], D=d["D"], initial_states=self.init,
+                                   has_initial_state=self.has, y=self.y, final_states=self.fin,
+                                   chunk_states=self.cache if export else None,
+                                   chunk_state_dst=self.dst if export else None)
+
+    def step(self, timed):
+        import torch
+        if timed:
+            m0 = torch.cuda.Event(enable_timing=True)
+            m0.record()
+        self.prepare()
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        self.scan()
+        if timed:
+            e1.record()
+            self.ev.append((e0, e1))
+            self.ev_meta.append((m0, e0))
+
+
+def cold_stats(run, flush, calls, warmup=5):
+    """The scan timed alone, HBM-cold: `warmup` untimed calls, then `calls`
+    calls each preceded by a write of the flush buffer outside the events."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        run.scan()
+    ev = []
+    for i in range(calls):
+        flush.fill_(i & 0xff)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run.scan()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    if int(run.meta.error_flag.item()) != 0:
+        raise RuntimeError("device error flag set")
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    alg, flops = algorithmic_work(run.w, run.n_ckpt)
+    med = float(np.median(ms))
+    return {"kernel": scan_kernel_name(run.config), "calls": calls,
+            "kernel_ms_median": med, "kernel_ms_p10": float(np.percentile(ms, 10)),
+            "kernel_ms_p90": float(np.percentile(ms, 90)), "kernel_ms_mean": float(ms.mean()),
+            "algorithmic_bytes": alg, "hbm_frac_median": alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac_median": flops / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "tokens_per_s_median": run.w.total_tokens / (med * 1e-3),
+            "traffic": counter_traffic(run.config)}
+
+
+def counter_path(config):
+    from selective_state_space_cu_amd.workloads import CONFIGS
+    return os.path.join(ROOT, "profiles", f"scan_{CONFIGS[config]['name']}_counters.json")
+
+
+def counter_traffic(config):
+    """HBM bytes per launch from the committed counter record of this workload,
+    or None when the kernel sources changed since it was taken."""
+    path = counter_path(config)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("kernel_hash") == kernel_hash() and c.get("config") == config:
+        return c["hbm_bytes_per_launch"]
+    return None
+
+
+def export_overhead(ssd, run, rounds=6, per=10):
     """Scan time with the at-source block-checkpoint export against the same scan
     without it (interleaved rounds of HIP-event-timed launches, medians): the
     kernel-level cost of writing the checkpoints."""
     import statistics
     import torch
-    _, dst = ssd.export_chunk_states(meta, bt, w.block_size, num_slots=w.num_slots)
     t = {True: [], False: []}
     for _ in range(rounds):
         for exp in (True, False):
@@ -477,11 +571,7 @@ def export_overhead(ssd, d, meta, bt, w, init, has, y, fin, cache, rounds=6, per
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-                ssd.chunk_scan_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], meta,
-                                      dt_bias=d["dt_bias"], D=d["D"], initial_states=init,
-                                      has_initial_state=has, y=y, final_states=fin,
-                                      chunk_states=cache if exp else None,
-                                      chunk_state_dst=dst if exp else None)
+                run.scan(export=exp)
                 e1.record()
                 t[exp].append((e0, e1))
     torch.cuda.synchronize()

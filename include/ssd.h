@@ -107,7 +107,15 @@ typedef struct {
 ssd_status ssd_varlen_metadata(const ssd_varlen_meta *meta, void *stream);
 
 /*
- * The chunked scan ("Mamba2 varlen" / "initstates decay" pages): for every
+ * The chunked scan over the varlen layout of "[Model] Mamba2 varlen and
+ * metadata refactor" (Purpose: packed (total_tokens, hidden) inputs, one
+ * cu_seqlens, per-sequence initial states), with the decay indexing of
+ * "[Bugfix] Mamba2 SSD varlen bug fix initstates decay, improve test, assert
+ * chunk pwr 2" (Purpose: the entering state reaches token i through the
+ * inclusive cumsum at i, and the chunk's total decay is read at its last valid
+ * token; chunk_size a power of two) and the per-chunk state export of
+ * "[Model Runner V2] Automatic prefix caching for GDN hybrid models" (Purpose,
+ * kernels/layers item). For every
  * chunk, delta = softplus(dt + dt_bias) and the chunk-local inclusive cumsum of
  * delta*A; C.B^T with the segment-sum decay mask; the intra-chunk output
  * (L o CB) . (delta x); the inter-chunk output exp(cumsum_i) * C_i . h_in; the
@@ -141,6 +149,10 @@ ssd_status ssd_varlen_metadata(const ssd_varlen_meta *meta, void *stream);
  * SSD_ERR_CAPACITY (chunk_states_capacity < max_chunks with no dst map, or <= 0),
  * SSD_ERR_HIP. If error_flag already holds SSD_DATA_BAD_CU_SEQLENS the kernel
  * writes nothing.
+ * There is no workspace argument (and no workspace-size query): the scan is
+ * one fused walk per (sequence, head, headdim tile) that keeps the chunk
+ * cumsums, the C.B^T tiles and the carried state in LDS and registers, so no
+ * intermediate is materialised in device memory.
  */
 ssd_status ssd_chunk_scan_varlen(
     const void *x, const float *dt, const float *dt_bias, const float *A, const void *B,

@@ -146,15 +146,56 @@ __device__ __forceinline__ u32x4 dma_rsrc(const void *base, int num_records) {
 // the asm carries them itself: s_mov m0 + s_nop 4 is six wait states before the
 // load, whatever precedes the asm. Without them a load may take the previous
 // M0 (landing on the previous block's LDS address) or a stale resource word.
+// Each load carries the stage buffer it fills as an assembly comment
+// ("ssd-stage k"), and each explicit wait the stage it releases ("ssd-wait k"),
+// so that a check of the compiled code can count, on every path, the vector
+// memory instructions between a stage's last load and the wait that releases
+// it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <int STAGE>
 __device__ __forceinline__ void dma16(const u32x4 &r, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds ; ssd-stage %3"
+                 :: "v"(voff), "s"(r), "s"(lds), "i"(STAGE) : "memory", "m0");
 }
+template <int STAGE>
 __device__ __forceinline__ void dma4(const u32x4 &r, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(r), "s"(lds) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds ; ssd-stage %3"
+                 :: "v"(voff), "s"(r), "s"(lds), "i"(STAGE) : "memory", "m0");
+}
+// Wait until at most VM vector memory instructions of this wave are
+// outstanding; on gfx9 parts loads and stores count in one counter and retire
+// in issue order, so this releases every load issued VM or more instructions
+// before the wait.
+// EXCL of the VM instructions are checkpoint-export stores, issued on the
+// steps the kernel counted as exporting (tagged "ssd-export").
+template <int VM, int STAGE, int EXCL = 0>
+__device__ __forceinline__ void wait_vm_stage() {
+    static_assert(VM >= 0 && VM <= 63, "vmcnt out of range");
+    asm volatile("s_waitcnt vmcnt(%0) ; ssd-wait %1 excl %2" :: "i"(VM), "i"(STAGE), "i"(EXCL) : "memory");
+}
+// A 16-byte store of a checkpoint (exported chunk state): `off` is the byte
+// offset into the buffer resource r (offsets past its size are dropped).
+// gfx940-family parts (gfx950 included) need two wait states between a store
+// of more than 8 bytes and a VALU write of its data registers (the compiler
+// pads its own stores, not this asm, and reuses the registers at once), hence
+// the s_nop 1.
+__device__ __forceinline__ void export_store16(const u32x4 &v, const u32x4 &r, int off) {
+    asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen ; ssd-export\n\ts_nop 1" :: "v"(v), "v"(off), "s"(r) : "memory");
+}
+// The same with the non-temporal + sc1 cache policy (written once, not re-read).
+__device__ __forceinline__ void export_store16_nt(const u32x4 &v, const u32x4 &r, int off) {
+    asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen nt sc1 ; ssd-export\n\ts_nop 1" :: "v"(v), "v"(off), "s"(r) : "memory");
+}
+// Placeholder stores through a zero-sized buffer resource (dropped by the
+// hardware). Written in assembly so that the compiler can neither merge nor
+// eliminate them: they exist only to keep the number of vector memory
+// instructions per pipeline step fixed.
+__device__ __forceinline__ void null_store8(const u32x4 &r) {
+    asm volatile("buffer_store_dwordx2 %0, off, %1, 0" :: "v"(u32x2{0, 0}), "s"(r) : "memory");
+}
+__device__ __forceinline__ void null_store16(const u32x4 &r) {   // (s_nop: see export_store16)
+    asm volatile("buffer_store_dwordx4 %0, off, %1, 0\n\ts_nop 1" :: "v"(u32x4{0, 0, 0, 0}), "s"(r) : "memory");
 }
 #pragma clang diagnostic pop
 
@@ -557,12 +598,12 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #pragma unroll
             for (int i = 0; i < SH::kIC; ++i) {
                 const int j = wave + NW * i;   // 1 KB block of the tile
-                dma16(rC, lds_u(j < SH::kTileC / 1024 ? lds_c + SLOT * SH::kTileC + 1024 * j : lds_sink), go.c[i]);
+                dma16<SLOT>(rC, lds_u(j < SH::kTileC / 1024 ? lds_c + SLOT * SH::kTileC + 1024 * j : lds_sink), go.c[i]);
             }
 #pragma unroll
             for (int i = 0; i < SH::kIB; ++i) {
                 const int j = wave + NW * i;
-                dma16(rB, lds_u(j < SH::kTileB / 1024 ? lds_b + SLOT * SH::kTileB + 1024 * j : lds_sink), go.b[i]);
+                dma16<SLOT>(rB, lds_u(j < SH::kTileB / 1024 ? lds_b + SLOT * SH::kTileB + 1024 * j : lds_sink), go.b[i]);
             }
         } else {
             const u32x4 rX = dma_rsrc(xg + (t0 * H + h) * P + p0, Lt * xrow);
@@ -571,27 +612,33 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #pragma unroll
             for (int i = 0; i < SH::kIX; ++i) {
                 const int j = wave + NW * i;
-                dma16(rX, lds_u(j < SH::kTileX / 1024 ? lds_x + SLOT * SH::kTileX + 1024 * j : lds_sink), go.x[i]);
+                dma16<SLOT>(rX, lds_u(j < SH::kTileX / 1024 ? lds_x + SLOT * SH::kTileX + 1024 * j : lds_sink), go.x[i]);
             }
-            dma4(rD, lds_u(wave == 0 ? lds_dt + SLOT * 256 : lds_sink), go.d);
+            dma4<SLOT>(rD, lds_u(wave == 0 ? lds_dt + SLOT * 256 : lds_sink), go.d);
         }
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    // y stores of a step that writes no y (keeps the per-step count fixed)
-    const __amdgpu_buffer_rsrc_t r_none = __builtin_amdgcn_make_buffer_rsrc((void *)yg, 0, 0, kBufFlags);
+    // y stores of a step that writes no y (keeps the per-step count fixed):
+    // kYStores stores of y's width through a zero-sized resource
+    const u32x4 r_none = dma_rsrc(yg, 0);
     auto dummy_y_stores = [&]() {
 #pragma unroll
-        for (int i = 0; i < SH::kYStores; ++i) O::store_y(r_none, 0, f32x4{0, 0, 0, 0});
+        for (int i = 0; i < SH::kYStores; ++i) {
+            if constexpr (sizeof(T) == 2) null_store8(r_none);
+            else null_store16(r_none);
+        }
     };
-    auto wait_stage = [&](int exports) {   // exports among the last NST-1 steps
+    // wait for stage SLOT; `exports` = checkpoint exports among the last NST-1 steps
+    auto wait_stage = [&](auto slot_c, int exports) {
+        constexpr int SLOT = decltype(slot_c)::value;
         if constexpr (NST == 3) {
-            if (exports == 0) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(3, 0)>::imm);
-            else if (exports == 1) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(3, 1)>::imm);
-            else __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(3, 2)>::imm);
+            if (exports == 0) wait_vm_stage<SH::vm_wait(3, 0), SLOT>();
+            else if (exports == 1) wait_vm_stage<SH::vm_wait(3, 1), SLOT, SH::kNT>();
+            else wait_vm_stage<SH::vm_wait(3, 2), SLOT, 2 * SH::kNT>();
         } else if constexpr (NST == 2) {
-            if (exports == 0) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(2, 0)>::imm);
-            else __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(2, 1)>::imm);
+            if (exports == 0) wait_vm_stage<SH::vm_wait(2, 0), SLOT>();
+            else wait_vm_stage<SH::vm_wait(2, 1), SLOT, SH::kNT>();
         }
     };
 
@@ -644,7 +691,7 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             fetch(P1{}, slot_c, t);
             __builtin_amdgcn_s_waitcnt(WaitVm<0>::imm);
         } else {
-            wait_stage(NST == 3 ? ex1 + ex2 : ex1);
+            wait_stage(slot_c, NST == 3 ? ex1 + ex2 : ex1);
         }
         lds_barrier();   // (A) stage SLOT and this tile's scan tables are visible
 
@@ -785,13 +832,11 @@ void ssd_scan_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             ex1 = dsl >= 0;
             if (dsl >= 0) {
                 float *cbase = a.chunk_states + ((int64_t)dsl * H + h) * P * N + (int64_t)p0 * N;
-                const __amdgpu_buffer_rsrc_t re =
-                    __builtin_amdgcn_make_buffer_rsrc((void *)cbase, 0, SH::kCols * N * 4, kBufFlags);
+                const u32x4 re = dma_rsrc(cbase, SH::kCols * N * 4);
                 const int eoff = (16 * wave + q) * N * 4;
 #pragma unroll
                 for (int u = 0; u < NT; ++u)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st[u]), re,
-                                                           state_n(u) < N ? eoff + 4 * state_n(u) : kOob, 0, 0);
+                    export_store16(__builtin_bit_cast(u32x4, st[u]), re, state_n(u) < N ? eoff + 4 * state_n(u) : kOob);
             }
         }
         if constexpr (NST == 1) lds_barrier();   // the single stage is refilled next step

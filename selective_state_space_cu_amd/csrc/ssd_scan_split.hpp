@@ -69,17 +69,18 @@ __device__ __forceinline__ u32x4 sgpr4(const u32x4 &r) {
     return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)r.x), (uint32_t)__builtin_amdgcn_readfirstlane((int)r.y),
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)r.z), (uint32_t)__builtin_amdgcn_readfirstlane((int)r.w)};
 }
-template <int OFF>
+// (The "ssd-stage k" comment names the stage the load fills; see dma16.)
+template <int OFF, int STAGE>
 __device__ __forceinline__ void dma16_at(const u32x4 &r0, uint32_t lds_base, int voff) {
     const u32x4 r = sgpr4(r0);
-    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF) : "memory", "m0", "scc");
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds ; ssd-stage %4"
+                 :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF), "i"(STAGE) : "memory", "m0", "scc");
 }
-template <int OFF>
+template <int OFF, int STAGE>
 __device__ __forceinline__ void dma4_at(const u32x4 &r0, uint32_t lds_base, int voff) {
     const u32x4 r = sgpr4(r0);
-    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF) : "memory", "m0", "scc");
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds ; ssd-stage %4"
+                 :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF), "i"(STAGE) : "memory", "m0", "scc");
 }
 // A 16-byte buffer load into registers that the compiler does not track (like
 // the direct-to-LDS loads): the caller waits for it with an explicit vmcnt and
@@ -90,10 +91,11 @@ __device__ __forceinline__ void dma4_at(const u32x4 &r0, uint32_t lds_base, int 
 // registers to other values, which the late load then overwrites. The CPU
 // tests check the compiled code for this (first touch of the registers on
 // every path is their LDS store, or a vmcnt(0) wait comes first).
-template <int OFF>
+template <int OFF, int STAGE>
 __device__ __forceinline__ void load16_untracked(u32x4 &dst, const u32x4 &r0, int voff) {
     const u32x4 r = sgpr4(r0);
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3" : "=v"(dst) : "v"(voff), "s"(r), "i"(OFF) : "memory");
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:%3 ; ssd-stage %4"
+                 : "=v"(dst) : "v"(voff), "s"(r), "i"(OFF), "i"(STAGE) : "memory");
 }
 __device__ __forceinline__ void reg_fence(u32x4 &v) { asm volatile("" : "+v"(v)); }
 #pragma clang diagnostic pop
@@ -311,12 +313,10 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         for (int u = 0; u < NTH; ++u)
             dst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, state_off(k, u), 0, 0));
     };
-    auto store_final = [&](int k) {
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(uintptr_t)fin_seq, 0, k < K ? seq_bytes : 0, kBufFlags);
+    auto store_final = [&](int k) {   // (NTH stores, counted like a checkpoint export)
+        const u32x4 r = buf_rsrc(fin_seq, k < K ? seq_bytes : 0);
 #pragma unroll
-        for (int u = 0; u < NTH; ++u)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st[u]), r, state_off(k, u), 0, 0);
+        for (int u = 0; u < NTH; ++u) export_store16(__builtin_bit_cast(u32x4, st[u]), r, state_off(k, u));
     };
     if constexpr (MULTI) load_init(stn, 1);
 
@@ -436,11 +436,11 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             r_c.z = r_b.z = (uint32_t)(Lt * browg);
             static_for<SH::kIC>([&](auto i_c) {
                 constexpr int I = decltype(i_c)::value;
-                dma16_at<SLOT * SH::kTileC + 8192 * I>(r_c, lds_c, go_c[I]);
+                dma16_at<SLOT * SH::kTileC + 8192 * I, SLOT>(r_c, lds_c, go_c[I]);
             });
             static_for<SH::kIB>([&](auto i_c) {
                 constexpr int I = decltype(i_c)::value;
-                dma16_at<SLOT * SH::kTileB + 8192 * I>(r_b, lds_b, go_b[I]);
+                dma16_at<SLOT * SH::kTileB + 8192 * I, SLOT>(r_b, lds_b, go_b[I]);
             });
         } else {
             r_x.z = (uint32_t)(Lt * xrow);
@@ -448,10 +448,10 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             if constexpr (decltype(with_x)::value) {
                 static_for<SH::kIX>([&](auto i_c) {
                     constexpr int I = decltype(i_c)::value;
-                    dma16_at<SLOT * SH::kTileX + 8192 * I>(r_x, lds_x, go_x[I]);
+                    dma16_at<SLOT * SH::kTileX + 8192 * I, SLOT>(r_x, lds_x, go_x[I]);
                 });
             }
-            dma4_at<SLOT * 256>(r_d, lds_dt, go_d);
+            dma4_at<SLOT * 256, SLOT>(r_d, lds_dt, go_d);
             // next tile (past the sequence end the positions are never dereferenced)
             if constexpr (MULTI) {
                 next_pos(fi, ft);
@@ -486,7 +486,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     auto xload = [&](auto set_c) {
         constexpr int SET = decltype(set_c)::value;
         r_xg.z = (uint32_t)(clamp_len(xg_rem) * xrow);
-        load16_untracked<0>(xr[SET], r_xg, go_x[0]);
+        load16_untracked<0, SET>(xr[SET], r_xg, go_x[0]);   // waited for by the step of slot SET
         if constexpr (MULTI) {
             next_pos(xi, xt);
             set_xg();
@@ -495,12 +495,15 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             xg_rem -= TT;
         }
     };
-    auto wait_stage = [&](int exports) {   // checkpoint exports among the last two steps
-        if (exports == 0) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(0)>::imm);
-        else if (exports == 1) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(1)>::imm);
-        else if (!MULTI || exports == 2) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(2)>::imm);
-        else if (exports == 3) __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(3)>::imm);
-        else __builtin_amdgcn_s_waitcnt(WaitVm<SH::vm_wait(4)>::imm);
+    // wait for stage SLOT (and the x registers of its set); `exports` =
+    // checkpoint exports among the last two steps
+    auto wait_stage = [&](auto slot_c, int exports) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        if (exports == 0) wait_vm_stage<SH::vm_wait(0), SLOT>();
+        else if (exports == 1) wait_vm_stage<SH::vm_wait(1), SLOT, NTH>();
+        else if (!MULTI || exports == 2) wait_vm_stage<SH::vm_wait(2), SLOT, 2 * NTH>();
+        else if (exports == 3) wait_vm_stage<SH::vm_wait(3), SLOT, 3 * NTH>();
+        else wait_vm_stage<SH::vm_wait(4), SLOT, 4 * NTH>();
     };
 
     // y of the previous tile: LDS tile (row rho = token, 128 bytes, chunk k at
@@ -522,7 +525,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     fetch(P0{}, std::integral_constant<int, 0>{}, WithX{});
     fetch(P1{}, std::integral_constant<int, 0>{}, WithX{});
     xload(std::integral_constant<int, 1>{});   // x of tile 3
-    store_prev_y(u32x4{0, 0, 0, 0});   // zero-sized: keeps the per-step count of vector memory ops
+    null_store16(buf_rsrc(y_prev, 0));   // zero-sized: keeps the per-step count of vector memory ops
     fetch(P0{}, std::integral_constant<int, 1>{}, WithX{});
     fetch(P1{}, std::integral_constant<int, 1>{}, WithX{});
     xload(std::integral_constant<int, 2>{});   // x of tile 4
@@ -655,7 +658,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             ex_tile = min(ex_tile + tpc, nt - 1);
         }
 
-        wait_stage(nexp);
+        wait_stage(slot_c, nexp);
         reg_fence(xr[SLOT]);   // x of tile t + 2, loaded three steps ago
         lds_barrier();   // (A) stage SLOT, this tile's tables, the partner's state half and y of tile t-1 are visible
 
@@ -807,8 +810,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         ex1 = ex;
         if (dsl >= 0) {
             const uint64_t cbase = ck_base + (uint64_t)dsl * ck_slot;
-            const __amdgpu_buffer_rsrc_t re =
-                __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)cbase, 0, SH::kCols * N * 4, kBufFlags);
+            const u32x4 re = buf_rsrc(cbase, SH::kCols * N * 4);
 #pragma unroll
             for (int rnd = 0; rnd < 4; ++rnd) {
                 if ((q >> 2) == rnd) {
@@ -820,7 +822,7 @@ void ssd_scan_split_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 }
                 wave_lds_sync();
                 const u32x4 v = *(const lds_u32x4 *)(uintptr_t)e_get;
-                __builtin_amdgcn_raw_buffer_store_b128(v, re, ((16 * pb + 4 * rnd + (lane >> 4)) * N + nb) * 4 + 16 * (lane & 15), 0, kStoreNT);
+                export_store16_nt(v, re, ((16 * pb + 4 * rnd + (lane >> 4)) * N + nb) * 4 + 16 * (lane & 15));
                 wave_lds_sync();
             }
         }

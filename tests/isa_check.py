@@ -108,7 +108,7 @@ def m0_lds_dma_hazards(asm_text):
     each offending load and the number of LDS-DMA loads seen."""
     prev, bad, count = None, [], 0
     for i, l in enumerate(asm_text.split("\n")):
-        t = l.strip()
+        t = l.split(";")[0].strip() if not l.strip().startswith(";") else l.strip()
         if not t or t.startswith(";") or t.startswith(".") or t.endswith(":"):
             continue
         if t.startswith("buffer_load") and t.endswith(" lds"):
@@ -155,3 +155,247 @@ def valu_sgpr_vmem_hazards(asm_text, need=5):
             if ws >= need:
                 break
     return bad
+
+
+_VMEM = re.compile(r"^(buffer_(load|store|atomic)|global_(load|store|atomic)|flat_(load|store|atomic)|scratch_)")
+_INF = 64   # more than any vmcnt immediate (6 bits): "at least 64" behaves as "none outstanding"
+
+
+def _functions(asm_text):
+    """(name, [(line number, instruction text)]) per function of an assembly file."""
+    out, name, body = [], None, []
+    for i, l in enumerate(asm_text.split("\n")):
+        m = re.match(r"^(_Z\w+):", l)
+        if m:
+            name, body = m.group(1), []
+            continue
+        if name is None:
+            continue
+        if l.startswith(".Lfunc_end"):
+            out.append((name, body))
+            name = None
+            continue
+        t = l.strip()
+        m = re.match(r"^(\.LBB\d+_\d+):", t)
+        if m:
+            body.append((i + 1, m.group(1) + ":"))
+        elif t and not t.startswith(";") and not t.startswith("."):
+            body.append((i + 1, t))
+    return out
+
+
+def _vmcnt_of(t):
+    m = re.search(r"vmcnt\((\d+)\)", t)
+    if m:
+        return int(m.group(1))
+    return 0 if re.match(r"^s_waitcnt\s+0\s*$", t) else None
+
+
+def _dst_sregs(t):
+    """Scalar registers written by an instruction (its first operand), as a set."""
+    parts = t.split(None, 1)
+    if len(parts) < 2:
+        return set()
+    dst = parts[1].split(",")[0].strip()
+    return _sregs(dst)
+
+
+def _exec_step(t, st):
+    """Abstract effect of one instruction on the scalar control state
+    (exec known all-ones; SGPR pairs holding a mask saved while it was;
+    64-bit SGPR pairs known to hold 0 or -1; vcc known zero / non-zero)."""
+    full, saved, consts, vcc = st
+    parts = t.split(None, 1)
+    mn = parts[0]
+    ops = [o.strip() for o in parts[1].split(";")[0].split(",")] if len(parts) > 1 else []
+    dst = ops[0] if ops else ""
+    written = _dst_sregs(t) if dst not in ("exec", "vcc") else set()
+    if written:
+        saved = frozenset(x for x in saved if not (_sregs(x) & written))
+        consts = {k: v for k, v in consts.items() if not (_sregs(k) & written)}
+    if dst == "exec":
+        if mn == "s_mov_b64" and len(ops) > 1 and ops[1] == "-1":
+            full = True
+        elif mn == "s_or_b64" and len(ops) == 3 and "exec" in ops[1:]:
+            other = ops[2] if ops[1] == "exec" else ops[1]
+            full = True if other in saved else full
+        else:
+            full = False
+        return full, saved, consts, vcc
+    if mn == "s_mov_b64" and len(ops) == 2 and ops[1] == "exec":
+        # a copy of exec, restored later with s_or_b64 exec, exec, <copy>
+        return full, (saved | {dst}) if full else saved, consts, vcc
+    if mn.startswith("s_") and "saveexec" in mn and ops:
+        # saves the current exec into ops[0], then changes exec
+        return False, (saved | {dst}) if full else saved, consts, vcc
+    if mn == "s_mov_b64" and len(ops) == 2 and ops[1] in ("0", "-1") and dst.startswith("s["):
+        consts = dict(consts)
+        consts[dst] = int(ops[1])
+    if dst == "vcc":
+        vcc = None
+        if mn in ("s_and_b64", "s_andn2_b64") and len(ops) == 3 and ops[1] == "exec" and ops[2] in consts:
+            c = consts[ops[2]]
+            if mn == "s_andn2_b64":
+                c = ~c
+            if c == 0:
+                vcc = "zero"
+            elif c == -1 and full:
+                vcc = "nonzero"
+    elif mn.startswith("v_") and ("vcc" in ops or mn.endswith("_e32") and ("cmp" in mn or "_co_" in mn
+                                                                            or "addc" in mn or "subb" in mn)):
+        vcc = None
+    return full, saved, consts, vcc
+
+
+def _edges(last, bi, nblocks, label_of, st):
+    """Feasible successors of a block ending in `last` under control state st."""
+    full, _, _, vcc = st
+    if last.startswith("s_branch"):
+        return [label_of[last.split()[-1]]]
+    if last.startswith("s_endpgm"):
+        return []
+    fall = [bi + 1] if bi + 1 < nblocks else []
+    if not last.startswith("s_cbranch"):
+        return fall
+    mn, tgt = last.split()[0], [label_of[last.split()[-1]]]
+    if mn == "s_cbranch_execz" and full:
+        return fall
+    if mn == "s_cbranch_execnz" and full:
+        return tgt
+    if mn == "s_cbranch_vccnz" and vcc is not None:
+        return tgt if vcc == "nonzero" else fall
+    if mn == "s_cbranch_vccz" and vcc is not None:
+        return tgt if vcc == "zero" else fall
+    return tgt + fall
+
+
+def vmcnt_stage_violations(asm_text):
+    """Tagged waits that may release a stage before its loads have landed.
+
+    The kernels' pipelined loads carry the stage they fill ("; ssd-stage k")
+    and their explicit waits the stage they release ("; ssd-wait k" on an
+    `s_waitcnt vmcnt(n)`). Loads and stores share the vmcnt counter and retire
+    in issue order, so `vmcnt(n)` releases stage k only if at least n vector
+    memory instructions were issued after stage k's last load. A forward
+    dataflow over the control-flow graph keeps, per stage, the minimum of that
+    count over all paths (every wait, the compiler's too, retires what it
+    covers).
+
+    Paths that need an all-zero exec mask where exec is known to be all ones
+    (the fall-through of `s_cbranch_execnz`, the target of `s_cbranch_execz`)
+    are not taken: the control-flow structurizer emits such edges for loop
+    exits, and no wave runs them. Exec is known full at entry (whole waves)
+    and after restoring a mask that was saved while it was full.
+
+    Returns (violations, per-function (tagged loads, tagged waits)); a
+    violation is (function, line, stage, n, count)."""
+    bad, counts = [], {}
+    for fname, body in _functions(asm_text):
+        blocks, cur, label_of = [], [], {}
+        for ln, t in body:
+            if t.endswith(":"):
+                if cur:
+                    blocks.append(cur)
+                cur = []
+                label_of[t[:-1]] = len(blocks)
+                continue
+            cur.append((ln, t))
+            if t.startswith("s_branch") or t.startswith("s_cbranch") or t.startswith("s_endpgm"):
+                blocks.append(cur)
+                cur = []
+        if cur:
+            blocks.append(cur)
+        n_loads = sum(1 for blk in blocks for _, t in blk if "ssd-stage" in t)
+        n_waits = sum(1 for blk in blocks for _, t in blk if "ssd-wait" in t)
+        counts[fname] = (n_loads, n_waits)
+        if not blocks:
+            continue
+        stages = sorted({int(m) for blk in blocks for _, t in blk for m in re.findall(r"ssd-stage (\d+)", t)})
+
+        def key(st):
+            f, sv, c, v = st
+            return (f, sv, tuple(sorted(c.items())), v)
+
+        # per block: control state -> per-stage minimum counts (paths are kept
+        # apart by control state, merged only when it is the same)
+        state_in = [dict() for _ in blocks]
+        st0 = (True, frozenset(), {}, None)
+        state_in[0][key(st0)] = (st0, {k: _INF for k in stages})
+        work, found = [(0, key(st0))], {}
+        while work:
+            bi, ck = work.pop()
+            st, d0 = state_in[bi][ck]
+            d = dict(d0)
+            for ln, t in blocks[bi]:
+                if t.startswith("s_waitcnt"):
+                    n = _vmcnt_of(t)
+                    m = re.search(r"ssd-wait (\d+)(?: excl (\d+))?", t)
+                    if m and n is not None:
+                        k, excl = int(m.group(1)), int(m.group(2) or 0)
+                        if d.get(k, _INF) < n - excl:
+                            old = found.get((ln, k))
+                            if old is None or d[k] < old[4]:
+                                found[(ln, k)] = (fname, ln, k, n - excl, d[k])
+                    if n is not None:
+                        for k in d:
+                            if d[k] >= n:
+                                d[k] = _INF
+                    continue
+                if _VMEM.match(t.split()[0]):
+                    m = re.search(r"ssd-stage (\d+)", t)
+                    if "ssd-export" not in t:
+                        for k in d:
+                            d[k] = min(_INF, d[k] + 1)
+                    if m:
+                        d[int(m.group(1))] = 0
+                st = _exec_step(t, st)
+            nk = key(st)
+            for sb in _edges(blocks[bi][-1][1], bi, len(blocks), label_of, st):
+                prev = state_in[sb].get(nk)
+                if prev is None:
+                    state_in[sb][nk] = (st, dict(d))
+                    work.append((sb, nk))
+                else:
+                    merged = {k: min(prev[1][k], d[k]) for k in d}
+                    if merged != prev[1]:
+                        state_in[sb][nk] = (st, merged)
+                        work.append((sb, nk))
+        bad.extend(found.values())
+    return bad, counts
+
+
+def store_data_hazards(asm_text, need=2):
+    """Stores of more than 8 bytes (dwordx3 / dwordx4) whose data registers a
+    VALU instruction overwrites fewer than `need` wait states later (gfx940-
+    family parts, gfx950 included, need two: the store may still be reading
+    them; each instruction in between is one wait state, s_nop N is N + 1).
+    Straight-line view; returns (line, store, writer) per hazard and the
+    number of such stores seen."""
+    ins = []
+    for i, l in enumerate(asm_text.split("\n")):
+        t = l.split(";")[0].strip() if not l.strip().startswith(";") else ""
+        if t and not t.startswith(".") and not t.endswith(":"):
+            ins.append((i + 1, t))
+    bad, count = [], 0
+    for k, (ln, t) in enumerate(ins):
+        mn = t.split()[0]
+        if not re.match(r"^(buffer|global|flat|scratch)_store_dwordx[34]$", mn):
+            continue
+        count += 1
+        ops = t.split(None, 1)[1].split(",")
+        m = re.search(r"v\[(\d+):(\d+)\]", ops[0] if mn.startswith("buffer") else ops[1])
+        if not m:
+            continue
+        data = set(range(int(m.group(1)), int(m.group(2)) + 1))
+        ws = 0
+        for j in range(k + 1, len(ins)):
+            if ws >= need:
+                break
+            nt = ins[j][1]
+            if nt.startswith("v_") and " " in nt:
+                dst = nt.split(None, 1)[1].split(",")[0]
+                if _vregs(dst) & data:
+                    bad.append((ln, t, nt))
+                    break
+            ws += int(nt.split()[1]) + 1 if nt.startswith("s_nop") else 1
+    return bad, count

@@ -1,15 +1,17 @@
-"""Checks of the compiled gfx950 kernels (CPU): the split-state scan's untracked
-register loads of x are never overwritten or reused before their wait, on any
-path; no direct-to-LDS load directly follows a write of M0; and no vector
-memory instruction reads an SGPR that a VALU instruction wrote fewer than five
-wait states before (inline assembly is not padded by the compiler)."""
+"""Checks of the compiled gfx950 kernels (CPU): every explicit stage wait of the
+scan pipelines has, on every path, at least as many vector memory instructions
+after the stage's last load as its vmcnt assumes; the split-state scan's
+untracked register loads of x are never overwritten or reused before their
+wait, on any path; no direct-to-LDS load directly follows a write of M0; and no
+vector memory instruction reads an SGPR that a VALU instruction wrote fewer
+than five wait states before (inline assembly is not padded by the compiler)."""
 import os
 import shutil
 
 import pytest
 
 from isa_check import (HIPCC, kernel_asm, m0_lds_dma_hazards, untracked_load_violations,
-                       valu_sgpr_vmem_hazards)
+                       store_data_hazards, valu_sgpr_vmem_hazards, vmcnt_stage_violations)
 
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None,
                                 reason="hipcc not available")
@@ -76,3 +78,89 @@ def test_valu_sgpr_checker_flags_a_planted_hazard():
                       "\tbuffer_load_dwordx4 v66, s[68:71], 0 offen lds"])
     bad = valu_sgpr_vmem_hazards(text)
     assert [b[0] for b in bad] == [5]
+
+
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip"])
+def test_stage_waits_cover_their_loads(src):
+    """Each `s_waitcnt vmcnt(n)` that releases a pipeline stage sees at least
+    n vector memory instructions after that stage's last load, on every path,
+    in every compiled instance (placeholder stores the compiler merged or
+    dropped would leave fewer)."""
+    bad, counts = vmcnt_stage_violations(kernel_asm(src))
+    pipelined = [f for f, (nl, nw) in counts.items() if nw > 0]
+    assert pipelined, "no tagged stage waits found"
+    assert all(counts[f][0] > 0 for f in pipelined), "tagged waits without tagged loads"
+    assert not bad, f"{len(bad)} stage waits with too few instructions after the stage's loads, e.g. " + \
+        "; ".join(f"{f[:48]}.. line {ln}: stage {k} waits vmcnt({n}) after {d}" for f, ln, k, n, d in bad[:3])
+
+
+def _kernel(lines):
+    return "\n".join(["_Z4testv:"] + ["\t" + l if not l.endswith(":") else l for l in lines] +
+                     [".Lfunc_end0:"])
+
+
+def test_vmcnt_checker_flags_merged_placeholder_stores():
+    """Planted: two placeholder stores were expected after the stage's load,
+    the compiler left one, and the wait still assumes two."""
+    load = "buffer_load_dwordx4 v1, s[0:3], 0 offen lds ; ssd-stage 0"
+    bad, _ = vmcnt_stage_violations(_kernel([
+        load, "buffer_store_dwordx2 v[2:3], off, s[4:7], 0",
+        "s_waitcnt vmcnt(2) ; ssd-wait 0 excl 0", "s_endpgm"]))
+    assert [(b[2], b[3], b[4]) for b in bad] == [(0, 2, 1)]
+    ok, _ = vmcnt_stage_violations(_kernel([
+        load, "buffer_store_dwordx2 v[2:3], off, s[4:7], 0", "buffer_store_dwordx2 v[2:3], off, s[4:7], 0",
+        "s_waitcnt vmcnt(2) ; ssd-wait 0 excl 0", "s_endpgm"]))
+    assert ok == []
+
+
+def test_vmcnt_checker_paths_exports_and_structurizer_edges():
+    """A path that skips an instruction fails; export stores only count as
+    the wait declares; a loop exit through s_cbranch_execnz with a full exec
+    mask never falls through; a flag set to -1 selects its branch."""
+    load = "buffer_load_dwordx4 v1, s[0:3], 0 offen lds ; ssd-stage 1"
+    store = "buffer_store_dwordx2 v[2:3], off, s[4:7], 0"
+    bad, _ = vmcnt_stage_violations(_kernel([
+        load, "s_cbranch_scc1 .LBB0_2", store, ".LBB0_2:",
+        "s_waitcnt vmcnt(1) ; ssd-wait 1 excl 0", "s_endpgm"]))
+    assert len(bad) == 1
+    export = "buffer_store_dwordx4 v[2:5], v6, s[4:7], 0 offen ; ssd-export"
+    ok, _ = vmcnt_stage_violations(_kernel([load, store, export, "s_waitcnt vmcnt(2) ; ssd-wait 1 excl 1", "s_endpgm"]))
+    assert ok == []
+    bad, _ = vmcnt_stage_violations(_kernel([load, export, export, "s_waitcnt vmcnt(2) ; ssd-wait 1 excl 0", "s_endpgm"]))
+    assert len(bad) == 1
+    ok, _ = vmcnt_stage_violations(_kernel([
+        load, "s_cbranch_execnz .LBB0_9",
+        "s_waitcnt vmcnt(1) ; ssd-wait 1 excl 0", ".LBB0_9:", "s_endpgm"]))
+    assert ok == []
+    ok, _ = vmcnt_stage_violations(_kernel([
+        load, "s_mov_b64 s[44:45], -1", "s_and_b64 vcc, exec, s[44:45]", "s_cbranch_vccnz .LBB0_9",
+        "s_waitcnt vmcnt(1) ; ssd-wait 1 excl 0", ".LBB0_9:", "s_endpgm"]))
+    assert ok == []
+    bad, _ = vmcnt_stage_violations(_kernel([
+        load, "s_and_saveexec_b64 s[2:3], vcc", "s_cbranch_execnz .LBB0_9",
+        "s_waitcnt vmcnt(1) ; ssd-wait 1 excl 0", ".LBB0_9:", "s_endpgm"]))
+    assert len(bad) == 1
+
+
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip",
+                                 "ssd_decode.hip", "ssd_meta.hip", "ssd_conv1d.hip"])
+def test_wide_store_data_not_overwritten_at_once(src):
+    bad, count = store_data_hazards(kernel_asm(src))
+    assert not bad, (f"{len(bad)} of {count} wide stores have their data registers overwritten by the "
+                     f"next instruction, e.g. line {bad[0][0]}: {bad[0][1]} then {bad[0][2]}")
+
+
+def test_store_data_checker_flags_a_planted_hazard():
+    text = "\n".join(["\tbuffer_store_dwordx4 v[2:5], v193, s[44:47], 0 offen",
+                      "\tv_accvgpr_read_b32 v2, a20",
+                      "\tbuffer_store_dwordx4 v[6:9], v193, s[44:47], 0 offen",
+                      "\ts_nop 0",
+                      "\tv_accvgpr_read_b32 v6, a20",
+                      "\tbuffer_store_dwordx4 v[14:17], v193, s[44:47], 0 offen",
+                      "\ts_nop 1",
+                      "\tv_accvgpr_read_b32 v14, a20",
+                      "\tglobal_store_dwordx4 v[0:1], v[10:13], off",
+                      "\ts_add_u32 s0, s0, 1",
+                      "\tv_mov_b32_e32 v11, 0"])
+    bad, count = store_data_hazards(text)
+    assert count == 4 and [b[0] for b in bad] == [1, 3, 9]
