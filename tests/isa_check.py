@@ -22,8 +22,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 def compile_asm(src, out, defines=()):
+    from selective_state_space_cu_amd.build import SOURCE_FLAGS
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", f"-I{os.path.join(ROOT, 'include')}",
+           "-Xclang", "-packed-fp32-ops", *SOURCE_FLAGS.get(os.path.basename(src), []),
+           f"-I{os.path.join(ROOT, 'include')}",
            *[f"-D{d}" for d in defines], "--cuda-device-only", "-S", src, "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
     return out
@@ -306,7 +308,7 @@ def vmcnt_stage_violations(asm_text):
         if cur:
             blocks.append(cur)
         n_loads = sum(1 for blk in blocks for _, t in blk if "ssd-stage" in t)
-        n_waits = sum(1 for blk in blocks for _, t in blk if "ssd-wait" in t)
+        n_waits = sum(len(re.findall("ssd-wait", t)) for blk in blocks for _, t in blk)
         counts[fname] = (n_loads, n_waits)
         if not blocks:
             continue
@@ -329,9 +331,8 @@ def vmcnt_stage_violations(asm_text):
             for ln, t in blocks[bi]:
                 if t.startswith("s_waitcnt"):
                     n = _vmcnt_of(t)
-                    m = re.search(r"ssd-wait (\d+)(?: excl (\d+))?", t)
-                    if m and n is not None:
-                        k, excl = int(m.group(1)), int(m.group(2) or 0)
+                    for ks_, ex_ in re.findall(r"ssd-wait (\d+)(?: excl (\d+))?", t) if n is not None else []:
+                        k, excl = int(ks_), int(ex_ or 0)
                         if d.get(k, _INF) < n - excl:
                             old = found.get((ln, k))
                             if old is None or d[k] < old[4]:

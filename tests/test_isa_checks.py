@@ -47,7 +47,8 @@ def test_checker_flags_a_reused_register():
     assert untracked_load_violations(ok) == ([], 1)
 
 
-@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip"])
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip",
+                                 "ssd_scan_f32.hip"])
 def test_m0_written_a_wait_state_before_lds_dma(src):
     bad, count = m0_lds_dma_hazards(kernel_asm(src))
     assert count > 0, "no direct-to-LDS loads found"
@@ -62,8 +63,8 @@ def test_m0_checker_flags_a_planted_hazard():
     assert count == 2 and [b[0] for b in bad] == [2]
 
 
-@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip",
-                                 "ssd_decode.hip", "ssd_meta.hip"])
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip",
+                                 "ssd_scan_f32.hip", "ssd_decode.hip", "ssd_meta.hip"])
 def test_valu_sgpr_write_five_wait_states_before_vmem(src):
     bad = valu_sgpr_vmem_hazards(kernel_asm(src))
     assert not bad, (f"{len(bad)} vector memory reads of a VALU-written SGPR too soon, e.g. line "
@@ -80,7 +81,8 @@ def test_valu_sgpr_checker_flags_a_planted_hazard():
     assert [b[0] for b in bad] == [5]
 
 
-@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip"])
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip",
+                                 "ssd_scan_f32.hip"])
 def test_stage_waits_cover_their_loads(src):
     """Each `s_waitcnt vmcnt(n)` that releases a pipeline stage sees at least
     n vector memory instructions after that stage's last load, on every path,
@@ -128,6 +130,14 @@ def test_vmcnt_checker_paths_exports_and_structurizer_edges():
     assert ok == []
     bad, _ = vmcnt_stage_violations(_kernel([load, export, export, "s_waitcnt vmcnt(2) ; ssd-wait 1 excl 0", "s_endpgm"]))
     assert len(bad) == 1
+    # a wait that releases two stages is checked for both
+    load5 = "buffer_load_dwordx4 v1, s[0:3], 0 offen lds ; ssd-stage 5"
+    bad, _ = vmcnt_stage_violations(_kernel([load5, store, load, store, "s_waitcnt vmcnt(1) ; ssd-wait 1 excl 0 ; ssd-wait 5 excl 0",
+                                             "s_endpgm"]))
+    assert bad == []
+    bad, _ = vmcnt_stage_violations(_kernel([load, store, load5, "s_waitcnt vmcnt(1) ; ssd-wait 1 excl 0 ; ssd-wait 5 excl 0",
+                                             "s_endpgm"]))
+    assert [b[2] for b in bad] == [5]
     ok, _ = vmcnt_stage_violations(_kernel([
         load, "s_cbranch_execnz .LBB0_9",
         "s_waitcnt vmcnt(1) ; ssd-wait 1 excl 0", ".LBB0_9:", "s_endpgm"]))
@@ -142,8 +152,8 @@ def test_vmcnt_checker_paths_exports_and_structurizer_edges():
     assert len(bad) == 1
 
 
-@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip",
-                                 "ssd_decode.hip", "ssd_meta.hip", "ssd_conv1d.hip"])
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip",
+                                 "ssd_scan_f32.hip", "ssd_decode.hip", "ssd_meta.hip", "ssd_conv1d.hip"])
 def test_wide_store_data_not_overwritten_at_once(src):
     bad, count = store_data_hazards(kernel_asm(src))
     assert not bad, (f"{len(bad)} of {count} wide stores have their data registers overwritten by the "
