@@ -43,6 +43,8 @@ def load(path=LIB):
     lib.oracle_causal_conv1d.argtypes = [
         ctypes.c_int32, _I32P, ctypes.c_int32, ctypes.c_int32, _F64P, _F64P, _F64P, ctypes.c_int32,
         _F64P, ctypes.c_int32, _I32P, _I32P, _F64P]
+    lib.oracle_prefill_bites.restype = ctypes.c_int
+    lib.oracle_prefill_bites.argtypes = [ctypes.c_int32, _I32P, _I32P, _I32P, ctypes.c_int32, _I32P]
     lib.oracle_num_threads.restype = ctypes.c_int
     _cache[path] = lib
     return lib
@@ -129,6 +131,32 @@ def checkpoint_plan(cu_seqlens, seq_chunk_start, max_chunks, block_table, block_
     if rc != 0:
         raise ValueError(f"oracle_checkpoint_plan failed ({rc})")
     return src, dst
+
+
+def prefill_bites(num_computed_tokens, prompt_len, budget, align, lib=None):
+    """Tokens the scheduler gives each sequence this step (the re-alignment rule)."""
+    lib = lib or load()
+    nc = _np(num_computed_tokens, np.int32)
+    pl = _np(prompt_len, np.int32)
+    bu = _np(np.broadcast_to(np.asarray(budget, np.int32), nc.shape), np.int32)
+    out = np.empty(nc.shape, np.int32)
+    rc = lib.oracle_prefill_bites(nc.size, _p(nc, _I32P), _p(pl, _I32P), _p(bu, _I32P), int(align),
+                                  _p(out, _I32P))
+    if rc != 0:
+        raise ValueError(f"oracle_prefill_bites failed ({rc})")
+    return out
+
+
+def prefill_schedule(start, prompt_len, budget, align, lib=None):
+    """The whole bite sequence of one prompt from `start`: [(first, last + 1), ...]."""
+    bites = []
+    while start < prompt_len:
+        n = int(prefill_bites([start], [prompt_len], budget, align, lib=lib)[0])
+        if n <= 0:
+            raise ValueError("no progress")
+        bites.append((start, start + n))
+        start += n
+    return bites
 
 
 def ssd_decode(x, dt, dt_bias, A, B, C, D, state_cache, read_slot, write_slot, lib=None):

@@ -253,6 +253,49 @@ int oracle_checkpoint_plan(int32_t nseqs, const int32_t *cu_seqlens, const int32
 }
 
 /*
+ * Prefill bites of the scheduler, one step (the prefix-caching page: the
+ * scheduler diff fragment, which re-aligns a misaligned start at the next
+ * boundary and otherwise clips the end down to a boundary, and the review
+ * note under it, which re-aligns a misaligned start even on the final bite and
+ * lets the final bite from an aligned start end anywhere).
+ * Sequence s has prompt_len[s] tokens, num_computed_tokens[s] of them done,
+ * and at most budget[s] tokens this step:
+ *     last_aligned = floor(prompt_len / align) * align
+ *     next         = (floor(start / align) + 1) * align     (start = num_computed_tokens)
+ *     end          = min(start + budget, prompt_len)
+ *     if start is not a multiple of align and next <= last_aligned:  end = min(end, next)
+ *     else if end < last_aligned:                                    end = floor(end / align) * align
+ *     num_scheduled[s] = end - start
+ * So every bite ends on a multiple of align except the one that ends the
+ * prompt, and only a misaligned starting position (state loaded from
+ * elsewhere) can start a bite off the grid: it ends at the next boundary.
+ * Returns 0, or -1 when align <= 0, a budget is below align, or a start lies
+ * outside [0, prompt_len].
+ */
+int oracle_prefill_bites(int32_t nseqs, const int32_t *num_computed_tokens, const int32_t *prompt_len,
+                         const int32_t *budget, int32_t align, int32_t *num_scheduled)
+{
+    if (align <= 0)
+        return -1;
+    for (int32_t s = 0; s < nseqs; ++s) {
+        const int64_t start = num_computed_tokens[s], len = prompt_len[s];
+        if (start < 0 || start > len || budget[s] < align)
+            return -1;
+        const int64_t last_aligned = len / align * align;
+        const int64_t next = (start / align + 1) * align;
+        int64_t end = start + budget[s] < len ? start + budget[s] : len;
+        if (start % align != 0 && next <= last_aligned) {
+            if (next < end)
+                end = next;
+        } else if (end < last_aligned) {
+            end = end / align * align;
+        }
+        num_scheduled[s] = (int32_t)(end - start);
+    }
+    return 0;
+}
+
+/*
  * One decode step with dual state anchors. The prefix-caching page's decode
  * kernels read a request's running state from one cache slot (the previous
  * step's write anchor) and write the advanced state to another (the current

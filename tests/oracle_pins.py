@@ -343,6 +343,101 @@ def pin_plan_scatter_equals_gather(lib):
         assert list(dst) == list(ref), f"trial {trial}"
 
 
+# ---- continuation: the scheduler's prefill bites ------------------------------
+
+def pin_bites_golden(lib):
+    """Bites worked out by hand from the scheduler rule (tests/golden/prefill_bites.json)."""
+    with open(os.path.join(GOLDEN, "prefill_bites.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        got = oracle.prefill_bites([c["start"]], [c["prompt_len"]], [c["budget"]], g["align"], lib=lib)
+        assert int(got[0]) == c["num_scheduled"], (c, int(got[0]))
+
+
+def pin_bites_invariants(lib):
+    """On random prompts the bites tile [start, prompt_len) with at most `budget`
+    tokens each; a bite that ends at or before the last boundary ends on the
+    grid; only the first bite, or one past the last boundary, starts off it, and
+    then it ends at the next boundary when that is <= the last boundary; a bite
+    from the grid ends at the last boundary it can reach."""
+    rng = np.random.default_rng(31)
+    for trial in range(300):
+        align = int(2 ** rng.integers(4, 10))
+        budget = align * int(rng.integers(1, 9)) + int(rng.integers(0, align))
+        plen = int(rng.integers(0, 20 * align))
+        start = int(rng.integers(0, plen + 1)) if trial % 2 else int(rng.integers(0, plen // align + 1)) * align
+        start = min(start, plen)
+        bites = oracle.prefill_schedule(start, plen, budget, align, lib=lib)
+        last_aligned = plen // align * align
+        pos = start
+        for i, (a, b) in enumerate(bites):
+            assert a == pos and 0 < b - a <= budget, (trial, bites)
+            if b <= last_aligned:
+                assert b % align == 0, (trial, bites)
+            if i > 0 and a < last_aligned:
+                assert a % align == 0, (trial, bites)
+            if a % align != 0 and (a // align + 1) * align <= last_aligned:
+                assert b == (a // align + 1) * align, (trial, a, b)
+            elif a % align == 0 and a + budget < last_aligned:
+                assert b == (a + budget) // align * align, (trial, a, b)
+            pos = b
+        assert pos == plen
+
+
+def pin_bites_checkpoints_exact(lib):
+    """A prompt computed in scheduler bites (each bite's initial state = the previous
+    bite's final state, the plan at num_computed_tokens = the bite's start) gives
+    the same outputs as one pass, and every block whose end lies in the computed
+    range gets a checkpoint equal to the one-pass state at that block end --
+    also when the computation resumes from a start off the grid."""
+    cs, bs, budget = 16, 64, 160
+    L = 530
+    w = make_inputs([L], 2, 3, 2, 1, cs, dtype="f32", init_seqs=[0], seed=41)
+    y_full, _, cst_full = _run(lib, w, chunk_size=cs)
+    nblocks = (L + bs - 1) // bs
+    for start in (0, 64, 37, 515):
+        # state after `start` tokens, from a one-pass run of the prefix
+        if start > 0:
+            wp = make_inputs([start], 2, 3, 2, 1, cs, dtype="f32", init_seqs=[0], seed=41)
+            for k in ("x", "dt", "B", "C"):
+                setattr(wp, k, getattr(w, k)[:start])
+            for k in ("dt_bias", "A", "D", "initial_states"):
+                setattr(wp, k, getattr(w, k))
+            _, h, _ = _run(lib, wp)
+        else:
+            h = w.initial_states.double().numpy()
+        got = {}
+        for a, b in oracle.prefill_schedule(start, L, budget, bs, lib=lib):
+            n = b - a
+            wb = make_inputs([n], 2, 3, 2, 1, cs, dtype="f32", init_seqs=[0], seed=41)
+            for k in ("x", "dt", "B", "C"):
+                setattr(wb, k, getattr(w, k)[a:b])
+            for k in ("dt_bias", "A", "D"):
+                setattr(wb, k, getattr(w, k))
+            wb.initial_states = torch_from(h)
+            yb, h, cstb = _run(lib, wb, chunk_size=cs)
+            _close(yb, y_full[a:b], 1e-12, f"bite [{a},{b}) y")
+            cu = np.array([0, n], np.int32)
+            meta = oracle.varlen_metadata(cu, cs, n // cs + 1, lib=lib)
+            bt = np.arange(nblocks, dtype=np.int32)[None, :]
+            src, _ = oracle.checkpoint_plan(cu, meta["seq_chunk_start"], n // cs + 1, bt, bs, cs,
+                                            num_computed_tokens=np.array([a], np.int32), lib=lib)
+            for k in range(nblocks):
+                if src[0, k] >= 0:
+                    got[k] = (cstb[src[0, k]], min((k + 1) * bs, b))
+        # every block ending inside [start, L) (or ending the prompt) is covered, exactly
+        want = [k for k in range(nblocks) if min((k + 1) * bs, L) > start]
+        assert sorted(got) == want, (start, sorted(got), want)
+        for k, (state, end) in got.items():
+            assert end == min((k + 1) * bs, L), (start, k, end)
+            _close(state, cst_full[(end + cs - 1) // cs - 1], 1e-12, f"start {start} block {k}")
+
+
+def torch_from(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float64)))
+
+
 # ---- decode step with dual state anchors -------------------------------------
 
 def _decode(lib, b, cache=None, rs=None, ws=None, dt_bias=None, A=None):
@@ -600,6 +695,7 @@ ALL_PINS = [pin_brute_force_semiseparable, pin_scalar_closed_form, pin_linear_at
             pin_chunked_decomposition, pin_initial_state_decay, pin_768_token_chunk128,
             pin_metadata_enumeration, pin_metadata_golden_tiny,
             pin_plan_prefix_cache_closed_form, pin_plan_misaligned_and_resume,
-            pin_plan_scatter_equals_gather, pin_decode_is_one_recurrence_token,
+            pin_plan_scatter_equals_gather, pin_bites_golden, pin_bites_invariants,
+            pin_bites_checkpoints_exact, pin_decode_is_one_recurrence_token,
             pin_decode_limits, pin_decode_anchor_rules, pin_decode_continues_prefill,
             pin_conv_is_numpy_convolve, pin_conv_silu, pin_conv_state_rows, pin_conv_split_invariance]

@@ -32,6 +32,14 @@ MUTATIONS = [
     ("plan_no_alignment_skip", [("if (ncomp % chunk_size == 0) {", "if (1) {")]),
     ("plan_no_final_block", [("ckpt_src[s * max_blocks + last] = (int32_t)hi;", "")]),
     ("order_tie_break", [("(lu == lv && u < v)", "(lu == lv && u > v)")]),
+    # the scheduler's prefill bites
+    ("bites_no_realign_on_final_bite", [("if (start % align != 0 && next <= last_aligned) {",
+                                         "if (start % align != 0 && end < last_aligned) {")]),
+    ("bites_clip_up", [("end = end / align * align;", "end = (end + align - 1) / align * align;")]),
+    ("bites_realign_one_boundary_late", [("if (next < end)\n                end = next;",
+                                          "if (next + align < end)\n                end = next + align;")]),
+    ("bites_ignore_budget", [("int64_t end = start + budget[s] < len ? start + budget[s] : len;",
+                              "int64_t end = len;")]),
     # the decode step with dual state anchors
     ("decode_drop_decay", [("hs[p * N + n] = decay * hs[p * N + n] + delta * xs[p] * Bs[n];",
                             "hs[p * N + n] = hs[p * N + n] + delta * xs[p] * Bs[n];")]),
