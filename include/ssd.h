@@ -232,6 +232,38 @@ ssd_status ssd_decode_step(
     const int32_t *read_slot, const int32_t *write_slot, void *y, int32_t *error_flag,
     void *stream);
 
+/*
+ * Continuation: how many tokens the scheduler gives each prefilling sequence
+ * this step (the scheduler diff fragment of the prefix-caching page, "re-align
+ * a misaligned start at the next boundary, otherwise clip the end down", with
+ * the review note under it: re-align a misaligned start even on the final
+ * bite, and let the final bite from an aligned start end anywhere). HOST code:
+ * every pointer is a [host] array of nseqs entries; nothing is launched.
+ * For sequence s with start = num_computed_tokens[s] tokens already computed
+ * (e.g. a prefix whose state was loaded from the cache), prompt_len[s] tokens
+ * in all and a budget of budget[s] tokens this step:
+ *     last_aligned = floor(prompt_len / align) * align
+ *     end = min(start + budget, prompt_len)
+ *     if start % align != 0 and the next multiple of align is <= last_aligned:
+ *         end = min(end, that multiple)            (re-align)
+ *     else if end < last_aligned:
+ *         end = floor(end / align) * align         (clip down)
+ *     num_scheduled[s] = end - start
+ * With align the cache block size (a multiple of chunk_size), every bite after
+ * a misaligned first one starts on a block boundary, so the chunk grid of each
+ * bite (anchored at its first token) falls on absolute multiples of
+ * chunk_size and every block end inside the bite is a chunk end: the plan of
+ * ssd_export_chunk_states (called with num_computed_tokens = the bite starts)
+ * then writes an exact checkpoint for every block that ends in the computed
+ * range; the misaligned first bite ends at a block end, whose checkpoint is
+ * its final state.
+ * Errors: SSD_ERR_NULL_ARG (a NULL array with nseqs > 0), SSD_ERR_SHAPE
+ * (nseqs < 0, align <= 0, a budget below align, a start outside
+ * [0, prompt_len]); num_scheduled is left unspecified on error.
+ */
+ssd_status ssd_prefill_bites(int32_t nseqs, const int32_t *num_computed_tokens, const int32_t *prompt_len,
+                             const int32_t *budget, int32_t align, int32_t *num_scheduled);
+
 /* Static, NUL-terminated description of a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -192,4 +192,29 @@ ssd_status ssd_causal_conv1d_varlen(const void *x, const float *weight, const fl
                ? SSD_OK : SSD_ERR_HIP;
 }
 
+ssd_status ssd_prefill_bites(int32_t nseqs, const int32_t *num_computed_tokens, const int32_t *prompt_len,
+                             const int32_t *budget, int32_t align, int32_t *num_scheduled) {
+    if (nseqs < 0 || align <= 0) return SSD_ERR_SHAPE;
+    if (nseqs > 0 && (num_computed_tokens == nullptr || prompt_len == nullptr || budget == nullptr ||
+                      num_scheduled == nullptr))
+        return SSD_ERR_NULL_ARG;
+    for (int32_t s = 0; s < nseqs; ++s)
+        if (num_computed_tokens[s] < 0 || num_computed_tokens[s] > prompt_len[s] || budget[s] < align)
+            return SSD_ERR_SHAPE;
+    for (int32_t s = 0; s < nseqs; ++s) {
+        const int64_t pos = num_computed_tokens[s], total = prompt_len[s];
+        const int64_t grid_end = total - total % align;            // last block boundary of the prompt
+        const int64_t boundary = pos - pos % align + align;        // first boundary after pos
+        const int64_t want = pos + budget[s];
+        int64_t stop = want < total ? want : total;
+        if (pos % align != 0) {
+            if (boundary <= grid_end && boundary < stop) stop = boundary;   // back onto the grid
+        } else if (stop < grid_end) {
+            stop -= stop % align;                                           // end on the grid
+        }
+        num_scheduled[s] = (int32_t)(stop - pos);
+    }
+    return SSD_OK;
+}
+
 }  // extern "C"

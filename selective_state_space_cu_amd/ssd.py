@@ -21,7 +21,7 @@ DATA_BAD_CU_SEQLENS, DATA_TOO_MANY_CHUNKS, DATA_BAD_SLOT, DATA_BAD_BLOCK = 1, 2,
 
 # names exported by libssd.so (checked by the CPU tests against include/ssd.h)
 EXPORTS = ("ssd_varlen_metadata", "ssd_chunk_scan_varlen", "ssd_export_chunk_states",
-           "ssd_decode_step", "ssd_causal_conv1d_varlen", "ssd_status_string")
+           "ssd_decode_step", "ssd_causal_conv1d_varlen", "ssd_prefill_bites", "ssd_status_string")
 
 
 class SSDError(RuntimeError):
@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_causal_conv1d_varlen.restype = st
     lib.ssd_causal_conv1d_varlen.argtypes = [vp, vp, vp, st, ctypes.POINTER(_Meta), i32, i32, i32, vp, i32,
                                              vp, vp, vp, vp]
+    lib.ssd_prefill_bites.restype = st
+    lib.ssd_prefill_bites.argtypes = [i32, vp, vp, vp, i32, vp]
     _lib = lib
     return lib
 
@@ -257,6 +259,22 @@ def export_chunk_states(meta: VarlenMeta, block_table: torch.Tensor, block_size:
         ctypes.byref(m), _ptr(ncomp), _ptr(bt), maxb, int(block_size), _ptr(ckpt_src), _ptr(dst),
         _ptr(chunk_states), state_elems, _ptr(state_cache), int(num_slots or 0), _stream(device)))
     return ckpt_src, dst[: meta.max_chunks]
+
+
+def prefill_bites(num_computed_tokens, prompt_len, budget, align: int):
+    """ssd_prefill_bites (host): tokens each prefilling sequence gets this step.
+    Arguments are host sequences, arrays or CPU tensors of nseqs entries (budget may
+    be a single int); returns a host int32 tensor of nseqs entries."""
+    lib = load_library()
+    nc = torch.as_tensor(num_computed_tokens, dtype=torch.int32).reshape(-1).contiguous()
+    pl = torch.as_tensor(prompt_len, dtype=torch.int32).reshape(-1).contiguous()
+    bu = torch.as_tensor(budget, dtype=torch.int32).reshape(-1).expand(nc.numel()).contiguous()
+    if pl.numel() != nc.numel():
+        raise ValueError("prompt_len and num_computed_tokens differ in length")
+    out = torch.empty_like(nc)
+    _check("ssd_prefill_bites", lib.ssd_prefill_bites(nc.numel(), nc.data_ptr(), pl.data_ptr(), bu.data_ptr(),
+                                                     int(align), out.data_ptr()))
+    return out
 
 
 def decode_step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
