@@ -5,4 +5,4 @@ benchmark's CPU-baseline leg, never by the product path. It shares no code with
 the HIP library.
 """
 from .oracle import (load, ssd_varlen, ssd_decode, causal_conv1d, varlen_metadata,  # noqa: F401
-                     checkpoint_plan, num_threads, prefill_bites, prefill_schedule)
+                     checkpoint_plan, num_threads, prefill_bites, prefill_schedule, gated_delta)

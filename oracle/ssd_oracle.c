@@ -253,6 +253,86 @@ int oracle_checkpoint_plan(int32_t nseqs, const int32_t *cu_seqlens, const int32
 }
 
 /*
+ * Gated delta rule (the recurrent state of the GDN layers whose chunk kernel
+ * the prefix-caching page extends with a per-chunk intermediate-state export,
+ * chunk size 64). The pages print no formula; this is the plainest reading of
+ * the gated delta rule, token by token, per sequence s and value head h (key
+ * head g = h / (H/G)), with the state h (dk x dv) in key-major layout:
+ *     h      <- exp(gate[t,h]) * h                   (gated decay; gate <= 0)
+ *     u      =  beta[t,h] * (v[t,h] - h^T k[t,g])     (delta-rule write value)
+ *     h      <- h + k[t,g] (outer) u
+ *     o[t,h] =  scale * h^T q[t,g]
+ * starting from initial_states[s,h] (if flagged) or zero. States are recorded
+ * after the last token of each chunk (chunk grid per sequence from its first
+ * token, like the scan's) when chunk_states is given, and after the last token
+ * of the sequence in final_states. Layouts (row-major): q, k (T,G,dk);
+ * v, o (T,H,dv); gate, beta (T,H); states (.,H,dk,dv).
+ * OpenMP over (sequence, head) pairs. Returns 0, or -1 on bad shapes.
+ */
+int oracle_gated_delta(int32_t nseqs, const int32_t *cu_seqlens, int32_t H, int32_t G, int32_t dk,
+                       int32_t dv, const double *q, const double *k, const double *v, const double *gate,
+                       const double *beta, double scale, const double *init, const int32_t *has_init,
+                       int32_t chunk_size, double *o, double *final_states, double *chunk_states)
+{
+    if (nseqs < 0 || H <= 0 || G <= 0 || H % G != 0 || dk <= 0 || dv <= 0)
+        return -1;
+    const int64_t per_state = (int64_t)dk * dv;
+    int64_t *chunk_base = (int64_t *)calloc((size_t)nseqs + 1, sizeof(int64_t));
+    if (!chunk_base)
+        return -1;
+    for (int32_t s = 0; s < nseqs; ++s) {
+        const int64_t L = (int64_t)cu_seqlens[s + 1] - cu_seqlens[s];
+        chunk_base[s + 1] = chunk_base[s] + (chunk_size > 0 ? (L + chunk_size - 1) / chunk_size : 0);
+    }
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int32_t s = 0; s < nseqs; ++s) {
+        for (int32_t hd = 0; hd < H; ++hd) {
+            const int64_t g = hd / (H / G);
+            double *S = (double *)malloc((size_t)per_state * sizeof(double));
+            double *u = (double *)malloc((size_t)dv * sizeof(double));
+            if (init && (has_init == NULL || has_init[s] != 0))
+                memcpy(S, init + ((int64_t)s * H + hd) * per_state, (size_t)per_state * sizeof(double));
+            else
+                memset(S, 0, (size_t)per_state * sizeof(double));
+            const int64_t t0 = cu_seqlens[s], t1 = cu_seqlens[s + 1];
+            for (int64_t t = t0; t < t1; ++t) {
+                const double a = exp(gate[t * H + hd]), b = beta[t * H + hd];
+                const double *kt = k + (t * G + g) * dk, *qt = q + (t * G + g) * dk;
+                const double *vt = v + (t * H + hd) * dv;
+                for (int64_t i = 0; i < per_state; ++i)
+                    S[i] *= a;
+                for (int64_t c = 0; c < dv; ++c) {
+                    double hk = 0.0;
+                    for (int64_t r = 0; r < dk; ++r)
+                        hk += S[r * dv + c] * kt[r];
+                    u[c] = b * (vt[c] - hk);
+                }
+                for (int64_t r = 0; r < dk; ++r)
+                    for (int64_t c = 0; c < dv; ++c)
+                        S[r * dv + c] += kt[r] * u[c];
+                double *ot = o + (t * H + hd) * dv;
+                for (int64_t c = 0; c < dv; ++c) {
+                    double acc = 0.0;
+                    for (int64_t r = 0; r < dk; ++r)
+                        acc += S[r * dv + c] * qt[r];
+                    ot[c] = scale * acc;
+                }
+                const int64_t local = t - t0;
+                if (chunk_states && chunk_size > 0 && ((local + 1) % chunk_size == 0 || t == t1 - 1)) {
+                    const int64_t c = chunk_base[s] + local / chunk_size;
+                    memcpy(chunk_states + (c * H + hd) * per_state, S, (size_t)per_state * sizeof(double));
+                }
+            }
+            memcpy(final_states + ((int64_t)s * H + hd) * per_state, S, (size_t)per_state * sizeof(double));
+            free(S);
+            free(u);
+        }
+    }
+    free(chunk_base);
+    return 0;
+}
+
+/*
  * Prefill bites of the scheduler, one step (the prefix-caching page: the
  * scheduler diff fragment, which re-aligns a misaligned start at the next
  * boundary and otherwise clips the end down to a boundary, and the review

@@ -11,7 +11,7 @@ import os
 import numpy as np
 
 import oracle
-from ssd_brute import chunked, semiseparable
+from ssd_brute import chunked, gdn_chunked, semiseparable
 from selective_state_space_cu_amd.workloads import (make_config, make_conv_inputs, make_decode_inputs,
                                                      make_inputs)
 
@@ -438,6 +438,109 @@ def torch_from(a):
     return torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float64)))
 
 
+# ---- gated delta rule (GDN) ------------------------------------------------------
+
+def gdn_inputs(lengths, H, G, dk, dv, seed, unit_keys=True, gate_scale=1.0, init=True):
+    """Small float64 inputs: unit-norm keys, gates in (-gate_scale, 0], beta in (0, 1)."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(lengths))
+    q = rng.normal(size=(T, G, dk)) / math.sqrt(dk)
+    k = rng.normal(size=(T, G, dk))
+    if unit_keys:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.normal(size=(T, H, dv))
+    gate = -gate_scale * rng.uniform(0.0, 1.0, size=(T, H))
+    beta = rng.uniform(0.05, 1.0, size=(T, H))
+    h0 = rng.normal(0.0, 0.5, size=(len(lengths), H, dk, dv)) if init else None
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return q, k, v, gate, beta, cu, h0
+
+
+def _gdn(lib, q, k, v, gate, beta, cu, scale, h0, cs=0, has=None):
+    return oracle.gated_delta(q, k, v, gate, beta, cu, scale, initial_states=h0, has_initial_state=has,
+                              chunk_size=cs, lib=lib)
+
+
+def pin_gdn_chunked_wy_form(lib):
+    """The token loop equals an independent chunked (WY) evaluation -- a triangular
+    solve per chunk -- at several chunk sizes, with partial chunks and states."""
+    for lengths, H, G, dk, dv, seed in [([13, 0, 40, 7], 4, 2, 6, 5, 1), ([64, 33], 2, 1, 8, 8, 2),
+                                        ([100], 3, 3, 4, 7, 3)]:
+        q, k, v, gate, beta, cu, h0 = gdn_inputs(lengths, H, G, dk, dv, seed)
+        for cs in (1, 3, 8, 16, 64):
+            o, fin, cst = _gdn(lib, q, k, v, gate, beta, cu, 0.7, h0, cs)
+            ob, fb, cb = gdn_chunked(q, k, v, gate, beta, cu, 0.7, h0, cs)
+            _close(o, ob, 1e-10, f"gdn o cs={cs}")
+            _close(fin, fb, 1e-10, f"gdn final cs={cs}")
+            _close(cst, cb, 1e-10, f"gdn chunk states cs={cs}")
+
+
+def pin_gdn_delta_write(lib):
+    """With no decay and beta = 1, a write stores v_t under the unit key k_t exactly:
+    the output read with q_t = k_t (scale 1) is v_t, whatever came before."""
+    q, k, v, gate, beta, cu, h0 = gdn_inputs([30], 2, 1, 8, 3, 4)
+    gate[:] = 0.0
+    beta[:] = 1.0
+    o, _, _ = _gdn(lib, k, k, v, gate, beta, cu, 1.0, h0)
+    _close(o, v, 1e-12, "gdn delta write")
+
+
+def pin_gdn_orthogonal_keys(lib):
+    """Mutually orthogonal unit keys, no decay, zero initial state: the delta term
+    vanishes and the layer is beta-weighted causal linear attention,
+    o_t = scale sum_{j <= t} beta_j (q_t . k_j) v_j, h_T = sum_j beta_j k_j v_j^T."""
+    T, dk, dv, H = 6, 8, 3, 2
+    q, _, v, gate, beta, cu, _ = gdn_inputs([T], H, 1, dk, dv, 5, init=False)
+    k = np.eye(dk)[:T][:, None, :]   # k_t = e_t
+    gate[:] = 0.0
+    o, fin, _ = _gdn(lib, q, k, v, gate, beta, cu, 0.5, None)
+    for h in range(H):
+        qk = q[:, 0] @ k[:, 0].T
+        want = 0.5 * np.tril(qk) @ (beta[:, h, None] * v[:, h])
+        _close(o[:, h], want, 1e-12, "gdn linear attention o")
+        _close(fin[0, h], k[:, 0].T @ (beta[:, h, None] * v[:, h]), 1e-12, "gdn linear attention h")
+
+
+def pin_gdn_no_write(lib):
+    """beta = 0: the state only decays, h_t = e^(sum of gates) h0, and
+    o_t = scale e^(G_t) h0^T q_t."""
+    q, k, v, gate, beta, cu, h0 = gdn_inputs([25, 9], 2, 2, 5, 4, 6)
+    beta[:] = 0.0
+    o, fin, _ = _gdn(lib, q, k, v, gate, beta, cu, 0.3, h0)
+    for s in range(2):
+        a, b = cu[s], cu[s + 1]
+        for h in range(2):
+            G = np.cumsum(gate[a:b, h])
+            want = 0.3 * np.exp(G)[:, None] * (q[a:b, h] @ h0[s, h])
+            _close(o[a:b, h], want, 1e-12, "gdn beta=0 o")
+            _close(fin[s, h], np.exp(G[-1]) * h0[s, h], 1e-12, "gdn beta=0 h")
+
+
+def pin_gdn_linear_in_values_and_state(lib):
+    """For fixed q, k, gates and beta the layer is linear in (v, h0):
+    o(v, h0) = o(v, 0) + o(0, h0), and likewise the final state."""
+    q, k, v, gate, beta, cu, h0 = gdn_inputs([20, 31], 3, 1, 6, 4, 7)
+    o, fin, _ = _gdn(lib, q, k, v, gate, beta, cu, 1.0, h0)
+    o1, f1, _ = _gdn(lib, q, k, v, gate, beta, cu, 1.0, np.zeros_like(h0))
+    o2, f2, _ = _gdn(lib, q, k, np.zeros_like(v), gate, beta, cu, 1.0, h0)
+    _close(o, o1 + o2, 1e-12, "gdn superposition o")
+    _close(fin, f1 + f2, 1e-12, "gdn superposition h")
+
+
+def pin_gdn_no_leakage_and_init_flag(lib):
+    """Packed sequences equal separate runs; a sequence without its flag starts from zero."""
+    q, k, v, gate, beta, cu, h0 = gdn_inputs([11, 23, 5], 2, 1, 4, 3, 8)
+    has = np.array([1, 0, 1], np.int32)
+    o, fin, _ = _gdn(lib, q, k, v, gate, beta, cu, 1.0, h0, has=has)
+    for s in range(3):
+        a, b = cu[s], cu[s + 1]
+        hs = h0[s:s + 1] if has[s] else np.zeros_like(h0[s:s + 1])
+        os_, fs, _ = _gdn(lib, q[a:b], k[a:b], v[a:b], gate[a:b], beta[a:b], np.array([0, b - a], np.int32),
+                          1.0, hs)
+        _close(o[a:b], os_, 1e-14, f"gdn sequence {s} o")
+        _close(fin[s:s + 1], fs, 1e-14, f"gdn sequence {s} h")
+
+
 # ---- decode step with dual state anchors -------------------------------------
 
 def _decode(lib, b, cache=None, rs=None, ws=None, dt_bias=None, A=None):
@@ -696,6 +799,8 @@ ALL_PINS = [pin_brute_force_semiseparable, pin_scalar_closed_form, pin_linear_at
             pin_metadata_enumeration, pin_metadata_golden_tiny,
             pin_plan_prefix_cache_closed_form, pin_plan_misaligned_and_resume,
             pin_plan_scatter_equals_gather, pin_bites_golden, pin_bites_invariants,
-            pin_bites_checkpoints_exact, pin_decode_is_one_recurrence_token,
+            pin_bites_checkpoints_exact, pin_gdn_chunked_wy_form, pin_gdn_delta_write,
+            pin_gdn_orthogonal_keys, pin_gdn_no_write, pin_gdn_linear_in_values_and_state,
+            pin_gdn_no_leakage_and_init_flag, pin_decode_is_one_recurrence_token,
             pin_decode_limits, pin_decode_anchor_rules, pin_decode_continues_prefill,
             pin_conv_is_numpy_convolve, pin_conv_silu, pin_conv_state_rows, pin_conv_split_invariance]

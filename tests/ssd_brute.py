@@ -103,3 +103,47 @@ def chunked(x, dt, dt_bias, A, B, C, D, cu, chunk_size, init=None, has_init=None
         final[s] = hst
     cs = np.stack(states) if states else np.zeros((0, H, P, N))
     return y, final, cs
+
+
+def gdn_chunked(q, k, v, gate, beta, cu, scale, h0, chunk):
+    """Independent float64 chunked (WY) form of the gated delta rule, per sequence
+    and value head: within a chunk with entering state H0 and inclusive log-gate
+    cumsum G (gamma = e^G),
+        (I + A) U = diag(beta) V - diag(beta gamma) K H0,  A_ij = beta_i e^(G_i - G_j) k_i.k_j (j < i)
+        O = scale (diag(gamma) Q H0 + (e^(G_i - G_j) q_i.k_j)_{j <= i} U)
+        H_next = gamma_last H0 + K^T diag(e^(G_last - G)) U
+    Returns (o, final_states, chunk_states) like the oracle."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    gate, beta = np.asarray(gate, np.float64), np.asarray(beta, np.float64)
+    T, G, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
+    S = len(cu) - 1
+    o = np.zeros((T, H, dv))
+    fin = np.zeros((S, H, dk, dv))
+    cst = []
+    for s in range(S):
+        a0, a1 = int(cu[s]), int(cu[s + 1])
+        per = []
+        for h in range(H):
+            g = h // (H // G)
+            Hs = np.array(h0[s, h], np.float64) if h0 is not None else np.zeros((dk, dv))
+            states = []
+            for c0 in range(a0, a1, chunk):
+                c1 = min(c0 + chunk, a1)
+                K, Q, V = k[c0:c1, g], q[c0:c1, g], v[c0:c1, h]
+                Gc = np.cumsum(gate[c0:c1, h])
+                bt = beta[c0:c1, h]
+                gam = np.exp(Gc)
+                D = np.exp(Gc[:, None] - Gc[None, :])
+                n = c1 - c0
+                A = np.tril(bt[:, None] * D * (K @ K.T), -1)
+                U = np.linalg.solve(np.eye(n) + A, bt[:, None] * V - (bt * gam)[:, None] * (K @ Hs))
+                Mq = np.tril(D * (Q @ K.T))
+                o[c0:c1, h] = scale * (gam[:, None] * (Q @ Hs) + Mq @ U)
+                Hs = gam[-1] * Hs + K.T @ (np.exp(Gc[-1] - Gc)[:, None] * U)
+                states.append(Hs.copy())
+            fin[s, h] = Hs
+            per.append(states)
+        for c in range(len(per[0]) if per else 0):
+            cst.append(np.stack([per[h][c] for h in range(H)]))
+    return o, fin, (np.stack(cst) if cst else np.zeros((0, H, dk, dv)))

@@ -32,6 +32,19 @@ MUTATIONS = [
     ("plan_no_alignment_skip", [("if (ncomp % chunk_size == 0) {", "if (1) {")]),
     ("plan_no_final_block", [("ckpt_src[s * max_blocks + last] = (int32_t)hi;", "")]),
     ("order_tie_break", [("(lu == lv && u < v)", "(lu == lv && u > v)")]),
+    # the gated delta rule
+    ("gdn_drop_decay", [("                    S[i] *= a;", "                    S[i] *= 1.0;")]),
+    ("gdn_write_from_undecayed_state", [("u[c] = b * (vt[c] - hk);", "u[c] = b * (vt[c] - hk / a);")]),
+    ("gdn_write_without_beta", [("u[c] = b * (vt[c] - hk);", "u[c] = (vt[c] - hk);")]),
+    ("gdn_beta_on_value_only", [("u[c] = b * (vt[c] - hk);", "u[c] = b * vt[c] - hk;")]),
+    ("gdn_output_before_write", [("acc += S[r * dv + c] * qt[r];", "acc += (S[r * dv + c] - kt[r] * u[c]) * qt[r];")]),
+    ("gdn_wrong_key_group", [("const int64_t g = hd / (H / G);\n            double *S",
+                              "const int64_t g = hd % G;\n            double *S")]),
+    ("gdn_read_with_key", [("acc += S[r * dv + c] * qt[r];", "acc += S[r * dv + c] * kt[r];")]),
+    ("gdn_no_scale", [("ot[c] = scale * acc;", "ot[c] = acc;")]),
+    ("gdn_chunk_state_off_by_one", [(
+        "((local + 1) % chunk_size == 0 || t == t1 - 1)) {\n                    const int64_t c = chunk_base[s]",
+        "(local % chunk_size == 0 || t == t1 - 1)) {\n                    const int64_t c = chunk_base[s]")]),
     # the scheduler's prefill bites
     ("bites_no_realign_on_final_bite", [("if (start % align != 0 && next <= last_aligned) {",
                                          "if (start % align != 0 && end < last_aligned) {")]),
