@@ -24,8 +24,8 @@ MUTATIONS = [
     ("transposed_input", [("+ delta * xt[p] * Bt[n]", "+ delta * xt[n % P] * Bt[p % N]")]),
     ("output_uses_previous_C", [("const double *Ct = C + (t * G + g) * N;",
                                  "const double *Ct = C + ((t > t0 ? t - 1 : t) * G + g) * N;")]),
-    ("chunk_state_off_by_one", [("(local + 1) % chunk_size == 0", "local % chunk_size == 0")]),
-    ("ignore_has_init", [("(has_init == NULL || has_init[s] != 0)", "(has_init == NULL)")]),
+    ("chunk_state_off_by_one", [("if ((local + 1) % chunk_size == 0 || t == t1 - 1) {", "if (local % chunk_size == 0 || t == t1 - 1) {")]),
+    ("ignore_has_init", [("init != NULL && (has_init == NULL || has_init[s] != 0);", "init != NULL && (has_init == NULL);")]),
     ("global_chunk_grid", [("t < cu_seqlens[s + 1]; t += chunk_size)",
                             "t < cu_seqlens[s + 1]; t = (t / chunk_size + 1) * chunk_size)")]),
     ("plan_missing_minus_one", [("ncomp) / chunk_size - 1;", "ncomp) / chunk_size;")]),
@@ -62,7 +62,7 @@ MUTATIONS = [
     ("decode_read_slot_ignored", [("if (r >= 0)\n            memcpy(h_in", "if (0)\n            memcpy(h_in")]),
     ("decode_writes_read_anchor", [("memcpy(state_cache + (int64_t)w * per_state",
                                     "memcpy(state_cache + (int64_t)(r >= 0 ? r : w) * per_state")]),
-    ("decode_wrong_group", [("const int64_t g = hd / (H / G);", "const int64_t g = hd % G;")]),
+    ("decode_wrong_group", [("const int64_t g = hd / (H / G);\n            const double delta", "const int64_t g = hd % G;\n            const double delta")]),
     ("decode_no_bias", [("dt[s * H + hd] + (dt_bias ? dt_bias[hd] : 0.0)", "dt[s * H + hd]")]),
     ("decode_drop_D", [("(D ? D[hd] : 0.0) * xs[p]", "0.0 * xs[p]")]),
     ("decode_bad_slot_not_refused", [("            bad = 1;", "            bad = 0;")]),
