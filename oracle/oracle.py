@@ -140,7 +140,7 @@ def checkpoint_plan(cu_seqlens, seq_chunk_start, max_chunks, block_table, block_
 def gated_delta(q, k, v, gate, beta, cu_seqlens, scale, initial_states=None, has_initial_state=None,
                 chunk_size=0, lib=None):
     """Token-by-token float64 gated delta rule. q, k (T,G,dk); v (T,H,dv); gate, beta (T,H);
-    states (S,H,dk,dv). Returns (o, final_states, chunk_states|None)."""
+    states value-major (S,H,dv,dk). Returns (o, final_states, chunk_states|None)."""
     lib = lib or load()
     q, k, v = _np(q, np.float64), _np(k, np.float64), _np(v, np.float64)
     gate, beta = _np(gate, np.float64), _np(beta, np.float64)
@@ -151,9 +151,9 @@ def gated_delta(q, k, v, gate, beta, cu_seqlens, scale, initial_states=None, has
     init = _np(initial_states, np.float64)
     has = _np(has_initial_state, np.int32)
     o = np.zeros((T, H, dv))
-    fin = np.zeros((S, H, dk, dv))
+    fin = np.zeros((S, H, dv, dk))
     nch = sum((int(cu[i + 1] - cu[i]) + chunk_size - 1) // chunk_size for i in range(S)) if chunk_size else 0
-    cst = np.zeros((nch, H, dk, dv)) if chunk_size else None
+    cst = np.zeros((nch, H, dv, dk)) if chunk_size else None
     rc = lib.oracle_gated_delta(S, _p(cu, _I32P), H, G, dk, dv, _p(q, _F64P), _p(k, _F64P), _p(v, _F64P),
                                 _p(gate, _F64P), _p(beta, _F64P), float(scale), _p(init, _F64P), _p(has, _I32P),
                                 int(chunk_size), _p(o, _F64P), _p(fin, _F64P), _p(cst, _F64P))

@@ -257,16 +257,17 @@ int oracle_checkpoint_plan(int32_t nseqs, const int32_t *cu_seqlens, const int32
  * the prefix-caching page extends with a per-chunk intermediate-state export,
  * chunk size 64). The pages print no formula; this is the plainest reading of
  * the gated delta rule, token by token, per sequence s and value head h (key
- * head g = h / (H/G)), with the state h (dk x dv) in key-major layout:
- *     h      <- exp(gate[t,h]) * h                   (gated decay; gate <= 0)
- *     u      =  beta[t,h] * (v[t,h] - h^T k[t,g])     (delta-rule write value)
- *     h      <- h + k[t,g] (outer) u
- *     o[t,h] =  scale * h^T q[t,g]
+ * head g = h / (H/G)), with the state S (dv x dk, value-major):
+ *     S      <- exp(gate[t,h]) * S                   (gated decay; gate <= 0)
+ *     u      =  beta[t,h] * (v[t,h] - S k[t,g])       (delta-rule write value)
+ *     S      <- S + u (outer) k[t,g]
+ *     o[t,h] =  scale * S q[t,g]
+ * i.e. S_t = e^(gate) S_{t-1} (I - beta k k^T) + beta v k^T, o_t = scale S_t q_t,
  * starting from initial_states[s,h] (if flagged) or zero. States are recorded
  * after the last token of each chunk (chunk grid per sequence from its first
  * token, like the scan's) when chunk_states is given, and after the last token
  * of the sequence in final_states. Layouts (row-major): q, k (T,G,dk);
- * v, o (T,H,dv); gate, beta (T,H); states (.,H,dk,dv).
+ * v, o (T,H,dv); gate, beta (T,H); states (.,H,dv,dk).
  * OpenMP over (sequence, head) pairs. Returns 0, or -1 on bad shapes.
  */
 int oracle_gated_delta(int32_t nseqs, const int32_t *cu_seqlens, int32_t H, int32_t G, int32_t dk,
@@ -304,17 +305,17 @@ int oracle_gated_delta(int32_t nseqs, const int32_t *cu_seqlens, int32_t H, int3
                 for (int64_t c = 0; c < dv; ++c) {
                     double hk = 0.0;
                     for (int64_t r = 0; r < dk; ++r)
-                        hk += S[r * dv + c] * kt[r];
+                        hk += S[c * dk + r] * kt[r];
                     u[c] = b * (vt[c] - hk);
                 }
-                for (int64_t r = 0; r < dk; ++r)
-                    for (int64_t c = 0; c < dv; ++c)
-                        S[r * dv + c] += kt[r] * u[c];
+                for (int64_t c = 0; c < dv; ++c)
+                    for (int64_t r = 0; r < dk; ++r)
+                        S[c * dk + r] += u[c] * kt[r];
                 double *ot = o + (t * H + hd) * dv;
                 for (int64_t c = 0; c < dv; ++c) {
                     double acc = 0.0;
                     for (int64_t r = 0; r < dk; ++r)
-                        acc += S[r * dv + c] * qt[r];
+                        acc += S[c * dk + r] * qt[r];
                     ot[c] = scale * acc;
                 }
                 const int64_t local = t - t0;

@@ -451,7 +451,7 @@ def gdn_inputs(lengths, H, G, dk, dv, seed, unit_keys=True, gate_scale=1.0, init
     v = rng.normal(size=(T, H, dv))
     gate = -gate_scale * rng.uniform(0.0, 1.0, size=(T, H))
     beta = rng.uniform(0.05, 1.0, size=(T, H))
-    h0 = rng.normal(0.0, 0.5, size=(len(lengths), H, dk, dv)) if init else None
+    h0 = rng.normal(0.0, 0.5, size=(len(lengths), H, dv, dk)) if init else None
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     return q, k, v, gate, beta, cu, h0
 
@@ -498,7 +498,7 @@ def pin_gdn_orthogonal_keys(lib):
         qk = q[:, 0] @ k[:, 0].T
         want = 0.5 * np.tril(qk) @ (beta[:, h, None] * v[:, h])
         _close(o[:, h], want, 1e-12, "gdn linear attention o")
-        _close(fin[0, h], k[:, 0].T @ (beta[:, h, None] * v[:, h]), 1e-12, "gdn linear attention h")
+        _close(fin[0, h], (k[:, 0].T @ (beta[:, h, None] * v[:, h])).T, 1e-12, "gdn linear attention S")
 
 
 def pin_gdn_no_write(lib):
@@ -511,13 +511,13 @@ def pin_gdn_no_write(lib):
         a, b = cu[s], cu[s + 1]
         for h in range(2):
             G = np.cumsum(gate[a:b, h])
-            want = 0.3 * np.exp(G)[:, None] * (q[a:b, h] @ h0[s, h])
+            want = 0.3 * np.exp(G)[:, None] * (q[a:b, h] @ h0[s, h].T)
             _close(o[a:b, h], want, 1e-12, "gdn beta=0 o")
             _close(fin[s, h], np.exp(G[-1]) * h0[s, h], 1e-12, "gdn beta=0 h")
 
 
 def pin_gdn_linear_in_values_and_state(lib):
-    """For fixed q, k, gates and beta the layer is linear in (v, h0):
+    """For fixed q, k, gates and beta the layer is linear in (v, S0):
     o(v, h0) = o(v, 0) + o(0, h0), and likewise the final state."""
     q, k, v, gate, beta, cu, h0 = gdn_inputs([20, 31], 3, 1, 6, 4, 7)
     o, fin, _ = _gdn(lib, q, k, v, gate, beta, cu, 1.0, h0)

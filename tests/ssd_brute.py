@@ -112,21 +112,22 @@ def gdn_chunked(q, k, v, gate, beta, cu, scale, h0, chunk):
         (I + A) U = diag(beta) V - diag(beta gamma) K H0,  A_ij = beta_i e^(G_i - G_j) k_i.k_j (j < i)
         O = scale (diag(gamma) Q H0 + (e^(G_i - G_j) q_i.k_j)_{j <= i} U)
         H_next = gamma_last H0 + K^T diag(e^(G_last - G)) U
-    Returns (o, final_states, chunk_states) like the oracle."""
+    (H0 here is key-major, dk x dv; states in and out are value-major like the
+    oracle's, dv x dk.) Returns (o, final_states, chunk_states) like the oracle."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     gate, beta = np.asarray(gate, np.float64), np.asarray(beta, np.float64)
     T, G, dk = q.shape
     H, dv = v.shape[1], v.shape[2]
     S = len(cu) - 1
     o = np.zeros((T, H, dv))
-    fin = np.zeros((S, H, dk, dv))
+    fin = np.zeros((S, H, dv, dk))
     cst = []
     for s in range(S):
         a0, a1 = int(cu[s]), int(cu[s + 1])
         per = []
         for h in range(H):
             g = h // (H // G)
-            Hs = np.array(h0[s, h], np.float64) if h0 is not None else np.zeros((dk, dv))
+            Hs = np.array(h0[s, h], np.float64).T if h0 is not None else np.zeros((dk, dv))
             states = []
             for c0 in range(a0, a1, chunk):
                 c1 = min(c0 + chunk, a1)
@@ -141,9 +142,9 @@ def gdn_chunked(q, k, v, gate, beta, cu, scale, h0, chunk):
                 Mq = np.tril(D * (Q @ K.T))
                 o[c0:c1, h] = scale * (gam[:, None] * (Q @ Hs) + Mq @ U)
                 Hs = gam[-1] * Hs + K.T @ (np.exp(Gc[-1] - Gc)[:, None] * U)
-                states.append(Hs.copy())
-            fin[s, h] = Hs
+                states.append(Hs.T.copy())
+            fin[s, h] = Hs.T
             per.append(states)
         for c in range(len(per[0]) if per else 0):
             cst.append(np.stack([per[h][c] for h in range(H)]))
-    return o, fin, (np.stack(cst) if cst else np.zeros((0, H, dk, dv)))
+    return o, fin, (np.stack(cst) if cst else np.zeros((0, H, dv, dk)))

@@ -37,10 +37,10 @@ MUTATIONS = [
     ("gdn_write_from_undecayed_state", [("u[c] = b * (vt[c] - hk);", "u[c] = b * (vt[c] - hk / a);")]),
     ("gdn_write_without_beta", [("u[c] = b * (vt[c] - hk);", "u[c] = (vt[c] - hk);")]),
     ("gdn_beta_on_value_only", [("u[c] = b * (vt[c] - hk);", "u[c] = b * vt[c] - hk;")]),
-    ("gdn_output_before_write", [("acc += S[r * dv + c] * qt[r];", "acc += (S[r * dv + c] - kt[r] * u[c]) * qt[r];")]),
+    ("gdn_output_before_write", [("acc += S[c * dk + r] * qt[r];", "acc += (S[c * dk + r] - kt[r] * u[c]) * qt[r];")]),
     ("gdn_wrong_key_group", [("const int64_t g = hd / (H / G);\n            double *S",
                               "const int64_t g = hd % G;\n            double *S")]),
-    ("gdn_read_with_key", [("acc += S[r * dv + c] * qt[r];", "acc += S[r * dv + c] * kt[r];")]),
+    ("gdn_read_with_key", [("acc += S[c * dk + r] * qt[r];", "acc += S[c * dk + r] * kt[r];")]),
     ("gdn_no_scale", [("ot[c] = scale * acc;", "ot[c] = acc;")]),
     ("gdn_chunk_state_off_by_one", [(
         "((local + 1) % chunk_size == 0 || t == t1 - 1)) {\n                    const int64_t c = chunk_base[s]",
