@@ -264,6 +264,39 @@ ssd_status ssd_decode_step(
 ssd_status ssd_prefill_bites(int32_t nseqs, const int32_t *num_computed_tokens, const int32_t *prompt_len,
                              const int32_t *budget, int32_t align, int32_t *num_scheduled);
 
+/*
+ * Chunked gated delta rule with per-chunk state export: the recurrent state of
+ * the GDN layers of the prefix-caching page (Purpose, kernels/layers item:
+ * "per-chunk intermediate-state export from the FLA chunk kernel"; chunk size
+ * 64 in its per-file table). The pages print no formula; the gated delta rule
+ * read here is, per sequence s and value head h (key head g = h / (H/G)), with
+ * the state S (dv x dk) value-major:
+ *     S_t = e^(gate[t,h]) S_{t-1} (I - beta[t,h] k_t k_t^T) + beta[t,h] v_t k_t^T
+ *     o_t = scale S_t q_t
+ * from initial_states[s,h] (if flagged; all if has_initial_state is NULL) or
+ * zero, evaluated 64 tokens at a time in the chunked (WY) form.
+ *  q, k            bf16 (T, G, dk); the layer normalises them before the call
+ *  v, o            bf16 (T, H, dv)
+ *  gate, beta      float32 (T, H): log-decay (<= 0) and write strength
+ *  initial_states  float32 (S, H, dv, dk) or NULL; final_states (S, H, dv, dk)
+ *  chunk_states    optional state export after each chunk, as for the scan:
+ *                  chunk_states[chunk_state_dst[c]] (or [c] when
+ *                  chunk_state_dst is NULL); slots >= capacity raise
+ *                  SSD_DATA_BAD_SLOT and are skipped.
+ * meta is the chunk metadata of ssd_varlen_metadata with chunk_size 64; the
+ * block-checkpoint plan of ssd_export_chunk_states (state_elems = H dv dk)
+ * feeds chunk_state_dst. Supported: in_dtype SSD_BF16, dk 128, dv a multiple
+ * of 64, nheads % nkheads == 0.
+ * Errors: SSD_ERR_NULL_ARG, SSD_ERR_SHAPE, SSD_ERR_DTYPE, SSD_ERR_UNSUPPORTED
+ * (another dtype, dk, dv or chunk size), SSD_ERR_CAPACITY, SSD_ERR_HIP.
+ * Asynchronous on `stream`; the caller owns every buffer; no workspace.
+ */
+ssd_status ssd_gated_delta_chunk_varlen(
+    const void *q, const void *k, const void *v, const float *gate, const float *beta, float scale,
+    ssd_dtype in_dtype, const ssd_varlen_meta *meta, int32_t nheads, int32_t nkheads, int32_t dk, int32_t dv,
+    const float *initial_states, const int32_t *has_initial_state, void *o, float *final_states,
+    float *chunk_states, const int32_t *chunk_state_dst, int32_t chunk_states_capacity, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *ssd_status_string(ssd_status status);
 

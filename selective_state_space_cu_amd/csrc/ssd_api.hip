@@ -37,7 +37,7 @@ const char *ssd_status_string(ssd_status status) {
     case SSD_ERR_CAPACITY: return "capacity below the required bound (max_chunks or chunk_states)";
     case SSD_ERR_DTYPE: return "unknown dtype";
     case SSD_ERR_HIP: return "a HIP call failed";
-    case SSD_ERR_UNSUPPORTED: return "unsupported headdim/dstate for this dtype";
+    case SSD_ERR_UNSUPPORTED: return "unsupported dtype/shape combination (headdim, dstate, dk, dv or chunk size)";
     }
     return "unknown status";
 }
@@ -190,6 +190,45 @@ ssd_status ssd_causal_conv1d_varlen(const void *x, const float *weight, const fl
     a.silu = activation;
     return ssd::launch_conv1d(a, in_dtype == SSD_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
                ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_gated_delta_chunk_varlen(const void *q, const void *k, const void *v, const float *gate,
+                                        const float *beta, float scale, ssd_dtype in_dtype,
+                                        const ssd_varlen_meta *meta, int32_t nheads, int32_t nkheads, int32_t dk,
+                                        int32_t dv, const float *initial_states, const int32_t *has_initial_state,
+                                        void *o, float *final_states, float *chunk_states,
+                                        const int32_t *chunk_state_dst, int32_t chunk_states_capacity,
+                                        void *stream) {
+    ssd_status st = check_meta(meta);
+    if (st != SSD_OK) return st;
+    if (in_dtype != SSD_F32 && in_dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    const bool empty = meta->total_tokens == 0;
+    if ((!empty && (q == nullptr || k == nullptr || v == nullptr || gate == nullptr || beta == nullptr ||
+                    o == nullptr)) ||
+        (meta->nseqs > 0 && final_states == nullptr))
+        return SSD_ERR_NULL_ARG;
+    if (nheads <= 0 || nkheads <= 0 || dk <= 0 || dv <= 0 || nheads % nkheads != 0) return SSD_ERR_SHAPE;
+    if (in_dtype != SSD_BF16 || dk != 128 || dv % 64 != 0 || meta->chunk_size != 64) return SSD_ERR_UNSUPPORTED;
+    if (chunk_states != nullptr) {
+        if (chunk_states_capacity <= 0) return SSD_ERR_CAPACITY;
+        if (chunk_state_dst == nullptr && chunk_states_capacity < meta->max_chunks) return SSD_ERR_CAPACITY;
+    }
+    for (const void *p : {q, k, v, (const void *)o, (const void *)final_states, (const void *)initial_states,
+                          (const void *)chunk_states})
+        if (p != nullptr && !aligned16(p)) return SSD_ERR_SHAPE;
+    ssd::GdnArgs a{};
+    a.q = static_cast<const uint16_t *>(q); a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v); a.gate = gate; a.beta = beta;
+    a.init = initial_states; a.has_init = has_initial_state;
+    a.o = static_cast<uint16_t *>(o); a.final_states = final_states;
+    a.chunk_states = chunk_states; a.chunk_state_dst = chunk_state_dst;
+    a.cu_seqlens = meta->cu_seqlens; a.seq_chunk_start = meta->seq_chunk_start; a.seq_order = meta->seq_order;
+    a.error_flag = meta->error_flag; a.scale = scale;
+    a.T = meta->total_tokens; a.S = meta->nseqs; a.H = nheads; a.G = nkheads; a.dv = dv;
+    a.max_chunks = meta->max_chunks; a.capacity = chunk_states ? chunk_states_capacity : 0;
+    a.nptiles = dv / 64;
+    if (meta->nseqs == 0) return SSD_OK;
+    return ssd::launch_gdn(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
 ssd_status ssd_prefill_bites(int32_t nseqs, const int32_t *num_computed_tokens, const int32_t *prompt_len,

@@ -99,6 +99,23 @@ int32_t conv1d_channel_blocks(int32_t channels);   // workgroups per chunk
 hipError_t launch_conv1d(const Conv1dArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, int dstate, hipStream_t stream);
 
+// Chunked gated delta rule (see ssd_gdn.hip).
+struct GdnArgs {
+    const uint16_t *q, *k, *v;          // (T,G,dk), (T,G,dk), (T,H,dv) bf16
+    const float *gate, *beta;           // (T,H)
+    const float *init;                  // (S,H,dv,dk) or null
+    const int32_t *has_init;            // (S) or null
+    uint16_t *o;                        // (T,H,dv) bf16
+    float *final_states;                // (S,H,dv,dk)
+    float *chunk_states;                // checkpoint cache or null
+    const int32_t *chunk_state_dst;     // slot per chunk or null (-> chunk index)
+    const int32_t *cu_seqlens, *seq_chunk_start, *seq_order;
+    int32_t *error_flag;
+    float scale;
+    int32_t T, S, H, G, dv, max_chunks, capacity, nptiles;
+};
+hipError_t launch_gdn(const GdnArgs &a, hipStream_t stream);
+
 struct MetaArgs {
     const int32_t *cu_seqlens;
     int32_t *chunk_offsets, *chunk_seq_idx, *seq_chunk_start, *nchunks, *seq_order, *error_flag;

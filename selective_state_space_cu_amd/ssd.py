@@ -21,7 +21,8 @@ DATA_BAD_CU_SEQLENS, DATA_TOO_MANY_CHUNKS, DATA_BAD_SLOT, DATA_BAD_BLOCK = 1, 2,
 
 # names exported by libssd.so (checked by the CPU tests against include/ssd.h)
 EXPORTS = ("ssd_varlen_metadata", "ssd_chunk_scan_varlen", "ssd_export_chunk_states",
-           "ssd_decode_step", "ssd_causal_conv1d_varlen", "ssd_prefill_bites", "ssd_status_string")
+           "ssd_decode_step", "ssd_causal_conv1d_varlen", "ssd_gated_delta_chunk_varlen", "ssd_prefill_bites",
+           "ssd_status_string")
 
 
 class SSDError(RuntimeError):
@@ -70,6 +71,9 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_causal_conv1d_varlen.restype = st
     lib.ssd_causal_conv1d_varlen.argtypes = [vp, vp, vp, st, ctypes.POINTER(_Meta), i32, i32, i32, vp, i32,
                                              vp, vp, vp, vp]
+    lib.ssd_gated_delta_chunk_varlen.restype = st
+    lib.ssd_gated_delta_chunk_varlen.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, st, ctypes.POINTER(_Meta),
+                                                 i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]
     lib.ssd_prefill_bites.restype = st
     lib.ssd_prefill_bites.argtypes = [i32, vp, vp, vp, i32, vp]
     _lib = lib
@@ -109,6 +113,12 @@ def _shape(t: Optional[torch.Tensor], name: str, *shape):
     another shape would be read or written out of its bounds, so refuse it here."""
     if t is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _dst_len(dst: Optional[torch.Tensor], meta):
+    """The kernels read one checkpoint slot per chunk of the batch's chunk grid."""
+    if dst is not None and dst.numel() < meta.max_chunks:
+        raise ValueError(f"chunk_state_dst needs {meta.max_chunks} entries (one per chunk), got {dst.numel()}")
 
 
 def _index(t: torch.Tensor, device):
@@ -204,6 +214,7 @@ def chunk_scan_varlen(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: tor
         _shape(has_initial_state, "has_initial_state", S)
     if chunk_states is not None:
         _shape(chunk_states, "chunk_states", chunk_states.shape[0], H, P, N)
+    _dst_len(chunk_state_dst, meta)
     dtype = x.dtype
     for name, t in (("B", B), ("C", C)):
         _data(t, name, device, dtype)
@@ -259,6 +270,57 @@ def export_chunk_states(meta: VarlenMeta, block_table: torch.Tensor, block_size:
         ctypes.byref(m), _ptr(ncomp), _ptr(bt), maxb, int(block_size), _ptr(ckpt_src), _ptr(dst),
         _ptr(chunk_states), state_elems, _ptr(state_cache), int(num_slots or 0), _stream(device)))
     return ckpt_src, dst[: meta.max_chunks]
+
+
+def gated_delta_chunk_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor,
+                             beta: torch.Tensor, meta: VarlenMeta, scale: Optional[float] = None,
+                             initial_states: Optional[torch.Tensor] = None,
+                             has_initial_state: Optional[torch.Tensor] = None,
+                             o: Optional[torch.Tensor] = None, final_states: Optional[torch.Tensor] = None,
+                             chunk_states: Optional[torch.Tensor] = None,
+                             chunk_state_dst: Optional[torch.Tensor] = None):
+    """ssd_gated_delta_chunk_varlen: q, k (T,G,dk), v (T,H,dv) bf16; gate, beta (T,H) float32;
+    states (S,H,dv,dk) float32. Returns (o, final_states)."""
+    lib = load_library()
+    device = v.device
+    T, H, DV = v.shape
+    G, DK = k.shape[1], k.shape[2]
+    S = meta.nseqs
+    for name, t, shp in (("q", q, (T, G, DK)), ("k", k, (T, G, DK)), ("gate", gate, (T, H)), ("beta", beta, (T, H)),
+                         ("o", o, (T, H, DV)), ("initial_states", initial_states, (S, H, DV, DK)),
+                         ("final_states", final_states, (S, H, DV, DK)), ("has_initial_state", has_initial_state, (S,))):
+        _shape(t, name, *shp)
+    if chunk_states is not None:
+        _shape(chunk_states, "chunk_states", chunk_states.shape[0], H, DV, DK)
+    _dst_len(chunk_state_dst, meta)
+    if T != meta.total_tokens:
+        raise ValueError(f"v has {T} tokens, the metadata {meta.total_tokens}")
+    dtype = v.dtype
+    _data(v, "v", device)
+    for name, t in (("q", q), ("k", k)):
+        _data(t, name, device, dtype)
+    for name, t in (("gate", gate), ("beta", beta)):
+        _data(t, name, device, torch.float32)
+    if o is None:
+        o = torch.empty_like(v)
+    _data(o, "o", device, dtype)
+    if final_states is None:
+        final_states = torch.empty((S, H, DV, DK), dtype=torch.float32, device=device)
+    _data(final_states, "final_states", device, torch.float32)
+    if initial_states is not None:
+        _data(initial_states, "initial_states", device, torch.float32)
+    has = _index(has_initial_state, device) if has_initial_state is not None else None
+    cap = 0
+    if chunk_states is not None:
+        _data(chunk_states, "chunk_states", device, torch.float32)
+        cap = chunk_states.shape[0]
+    dst = _index(chunk_state_dst, device) if chunk_state_dst is not None else None
+    m = meta.c_struct()
+    _check("ssd_gated_delta_chunk_varlen", lib.ssd_gated_delta_chunk_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), float(scale if scale is not None else DK ** -0.5),
+        _dtype_code(v), ctypes.byref(m), H, G, DK, DV, _ptr(initial_states), _ptr(has), _ptr(o), _ptr(final_states),
+        _ptr(chunk_states), _ptr(dst), cap, _stream(device)))
+    return o, final_states
 
 
 def prefill_bites(num_computed_tokens, prompt_len, budget, align: int):

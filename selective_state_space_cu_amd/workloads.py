@@ -284,3 +284,81 @@ def make_conv_config() -> ConvBatch:
     c = CONV_CONFIG
     return make_conv_inputs(c["lengths"], c["channels"], c["width"], c["num_slots"], dtype=c["dtype"],
                             seed=c["seed"], silu=c["silu"], name=c["name"])
+
+
+@dataclasses.dataclass
+class GdnBatch:
+    """Packed varlen inputs of one gated-delta-rule (GDN) chunk call."""
+    lengths: list
+    cu_seqlens: torch.Tensor       # (S+1,) int32
+    q: torch.Tensor                # (T, G, dk) in dtype, unit rows
+    k: torch.Tensor                # (T, G, dk) in dtype, unit rows
+    v: torch.Tensor                # (T, H, dv) in dtype
+    gate: torch.Tensor             # (T, H) float32 log-decay (<= 0)
+    beta: torch.Tensor             # (T, H) float32 in (0, 1)
+    scale: float
+    initial_states: torch.Tensor   # (S, H, dv, dk) float32
+    has_initial_state: torch.Tensor  # (S,) int32
+    chunk_size: int
+    dtype: str
+    block_table: Optional[torch.Tensor] = None
+    block_size: Optional[int] = None
+    num_slots: Optional[int] = None
+    name: str = ""
+
+    @property
+    def nseqs(self):
+        return len(self.lengths)
+
+    @property
+    def total_tokens(self):
+        return int(sum(self.lengths))
+
+
+# GDN workload timed next to the scan: the prefix-caching page's ~8.9k-token
+# prompt, four sequences, 32 value heads on 16 key heads, key and value head
+# dimensions 128, chunk 64, 256-token cache blocks.
+GDN_CONFIG = dict(name="gdn_prefix_cache_4x8894_h32g16", lengths=[8894] * 4, nheads=32, nkheads=16,
+                  dk=128, dv=128, chunk_size=64, block_size=256, num_slots=140, dtype="bf16", seed=7)
+
+
+def make_gdn_inputs(lengths, nheads, nkheads, dk, dv, chunk_size=64, dtype="bf16", init_seqs=(), seed=0,
+                    block_size=None, num_slots=None, name=""):
+    """Draw one GDN batch. Draw order: q, k ~ N(0,1) rows scaled to unit length
+    (the layer normalises them before the kernel) -> v ~ N(0,1) -> gate =
+    -e^U(ln 1e-3, ln 0.2) (log-decay per token and value head: per-token decay
+    factors between 0.82 and 0.999, about 0.09 over a chunk) -> beta ~ U(0.05, 0.95)
+    -> initial states ~ N(0, 0.5^2) -> block table (a slot permutation).
+    scale = 1/sqrt(dk)."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(v) for v in lengths]
+    S, T = len(lengths), int(sum(lengths))
+    cu = np.zeros(S + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    q = rng.standard_normal((T, nkheads, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((T, nkheads, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, nheads, dv))
+    gate = -np.exp(rng.uniform(np.log(1e-3), np.log(0.2), size=(T, nheads)))
+    beta = rng.uniform(0.05, 0.95, size=(T, nheads))
+    init = rng.standard_normal((S, nheads, dv, dk)) * 0.5
+    has = np.zeros(S, np.int32)
+    has[list(init_seqs)] = 1
+    block_table = None
+    if block_size is not None:
+        nblk = -(-max(lengths) // block_size) if lengths else 0
+        slots = num_slots if num_slots is not None else S * nblk
+        block_table = torch.from_numpy(rng.permutation(slots)[: S * nblk].reshape(S, nblk).astype(np.int32))
+    return GdnBatch(lengths=lengths, cu_seqlens=torch.from_numpy(cu), q=_cast(q, dtype), k=_cast(k, dtype),
+                    v=_cast(v, dtype), gate=_cast(gate, "f32"), beta=_cast(beta, "f32"),
+                    scale=float(1.0 / np.sqrt(dk)), initial_states=_cast(init, "f32"),
+                    has_initial_state=torch.from_numpy(has), chunk_size=chunk_size, dtype=dtype,
+                    block_table=block_table, block_size=block_size, num_slots=num_slots, name=name)
+
+
+def make_gdn_config() -> GdnBatch:
+    c = GDN_CONFIG
+    return make_gdn_inputs(c["lengths"], c["nheads"], c["nkheads"], c["dk"], c["dv"], c["chunk_size"],
+                           dtype=c["dtype"], seed=c["seed"], block_size=c["block_size"], num_slots=c["num_slots"],
+                           name=c["name"])

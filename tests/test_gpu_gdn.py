@@ -1,0 +1,192 @@
+"""GPU parity of the chunked gated delta rule (GDN) kernel through the C ABI
+against the float64 token-by-token oracle on the same seeded inputs.
+
+Inputs are bf16 q, k, v (the oracle reads the same rounded values in float64),
+float32 gates and betas, float32 states; tolerance 2e-2 (bf16 operands with
+float32 accumulation and state). Covered: varlen batches with empty, one-token,
+ragged and exact-multiple sequences, initial-state flags, value widths of one to
+three 64-column slices, grouped and ungrouped key heads, the per-chunk state
+export (dense and through the block-checkpoint plan), bit determinism, the
+argument checks, and the full 4 x 8894-token, 32-head workload on sampled heads
+with its block checkpoints.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, check_close, log
+from selective_state_space_cu_amd import ssd
+from selective_state_space_cu_amd.workloads import make_gdn_config, make_gdn_inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+CS = 64
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _oracle(w, chunk_size=0, seqs=None, heads=None):
+    """Oracle on the whole batch (seqs / heads None) or on one (sequence, head)."""
+    if seqs is None:
+        return oracle.gated_delta(_f64(w.q), _f64(w.k), _f64(w.v), _f64(w.gate), _f64(w.beta), w.cu_seqlens.numpy(),
+                                  w.scale, _f64(w.initial_states), w.has_initial_state.numpy(),
+                                  chunk_size=chunk_size)
+    s, h = seqs, heads
+    cu = w.cu_seqlens.numpy()
+    t0, t1 = int(cu[s]), int(cu[s + 1])
+    g = h // (w.v.shape[1] // w.q.shape[1])
+    return oracle.gated_delta(_f64(w.q[t0:t1, g:g + 1]), _f64(w.k[t0:t1, g:g + 1]), _f64(w.v[t0:t1, h:h + 1]),
+                              _f64(w.gate[t0:t1, h:h + 1]), _f64(w.beta[t0:t1, h:h + 1]),
+                              np.array([0, t1 - t0], np.int32), w.scale, _f64(w.initial_states[s:s + 1, h:h + 1]),
+                              w.has_initial_state[s:s + 1].numpy(), chunk_size=chunk_size)
+
+
+def _dev(w):
+    return {k: getattr(w, k).cuda().contiguous() for k in ("q", "k", "v", "gate", "beta", "initial_states",
+                                                           "has_initial_state", "cu_seqlens")}
+
+
+def _run(w, d=None, export=None, dst=None, init=True):
+    d = d or _dev(w)
+    meta = ssd.varlen_metadata(d["cu_seqlens"], CS, total_tokens=w.total_tokens)
+    cst = None
+    if export == "dense":
+        cst = torch.full((max(meta.max_chunks, 1),) + tuple(w.initial_states.shape[1:]), float("nan"),
+                         device="cuda")
+    elif export is not None:
+        cst = export
+    o, fin = ssd.gated_delta_chunk_varlen(d["q"], d["k"], d["v"], d["gate"], d["beta"], meta, scale=w.scale,
+                                          initial_states=d["initial_states"] if init else None,
+                                          has_initial_state=d["has_initial_state"] if init else None,
+                                          chunk_states=cst, chunk_state_dst=dst)
+    torch.cuda.synchronize()
+    assert int(meta.error_flag.item()) == 0
+    return meta, o, fin, cst
+
+
+SHAPES = [
+    # lengths, H, G, dv, init seqs
+    ([1, 63, 64, 65, 200, 0, 130], 4, 2, 128, (1, 4, 5)),
+    ([300, 17], 2, 2, 64, (0,)),
+    ([129, 5, 256], 3, 1, 192, (2,)),
+    ([64] * 6, 8, 4, 128, (0, 1, 2, 3, 4, 5)),
+]
+
+
+@pytest.mark.parametrize("shape", range(len(SHAPES)))
+def test_gdn_small_varlen(shape):
+    lengths, H, G, dv, init = SHAPES[shape]
+    w = make_gdn_inputs(lengths, H, G, 128, dv, init_seqs=init, seed=100 + shape)
+    log(f"gdn small: lengths={lengths} H={H} G={G} dv={dv}")
+    meta, o, fin, cst = _run(w, export="dense")
+    o_ref, fin_ref, cst_ref = _oracle(w, chunk_size=CS)
+    check_close(o, o_ref, TOL["bf16"], "o")
+    check_close(fin, fin_ref, TOL["bf16"], "final states")
+    check_close(cst[: cst_ref.shape[0]], cst_ref, TOL["bf16"], "chunk states")
+
+
+def test_gdn_no_initial_states():
+    w = make_gdn_inputs([90, 1, 200], 4, 4, 128, 128, init_seqs=(0, 1, 2), seed=5)
+    _, o, fin, _ = _run(w, init=False)
+    w.has_initial_state.zero_()
+    o_ref, fin_ref, _ = _oracle(w)
+    check_close(o, o_ref, TOL["bf16"], "o")
+    check_close(fin, fin_ref, TOL["bf16"], "final states")
+
+
+def test_gdn_all_empty_sequences():
+    w = make_gdn_inputs([0, 0, 0], 2, 1, 128, 64, init_seqs=(1,), seed=6)
+    _, o, fin, _ = _run(w)
+    assert o.numel() == 0
+    ref = w.initial_states.clone()
+    ref[0].zero_()
+    ref[2].zero_()
+    assert torch.equal(fin.cpu(), ref)
+
+
+def test_gdn_slow_decay_long_sequence():
+    """Gates near zero and betas near one: the state carries across many chunks."""
+    w = make_gdn_inputs([1000, 333], 2, 1, 128, 128, init_seqs=(1,), seed=8)
+    w.gate.mul_(0.05)
+    w.beta.copy_(0.5 + 0.5 * w.beta)
+    _, o, fin, _ = _run(w)
+    o_ref, fin_ref, _ = _oracle(w)
+    check_close(o, o_ref, TOL["bf16"], "o")
+    check_close(fin, fin_ref, TOL["bf16"], "final states")
+
+
+def test_gdn_bit_deterministic():
+    w = make_gdn_inputs([500, 77, 128], 4, 2, 128, 128, init_seqs=(0,), seed=9)
+    d = _dev(w)
+    _, o1, f1, c1 = _run(w, d, export="dense")
+    _, o2, f2, c2 = _run(w, d, export="dense")
+    # rows past the batch's chunks stay NaN in both exports
+    same = [torch.equal(o1, o2), torch.equal(f1, f2), torch.equal(c1.nan_to_num(7.0), c2.nan_to_num(7.0))]
+    assert same == [True, True, True], same
+
+
+def test_gdn_argument_checks():
+    w = make_gdn_inputs([70, 10], 2, 1, 128, 64, seed=10)
+    d = _dev(w)
+    meta = ssd.varlen_metadata(d["cu_seqlens"], 32, total_tokens=w.total_tokens)
+    with pytest.raises(ssd.SSDError, match="unsupported"):
+        ssd.gated_delta_chunk_varlen(d["q"], d["k"], d["v"], d["gate"], d["beta"], meta)   # chunk size 32
+    meta = ssd.varlen_metadata(d["cu_seqlens"], CS, total_tokens=w.total_tokens)
+    with pytest.raises(ssd.SSDError, match="unsupported"):
+        ssd.gated_delta_chunk_varlen(d["q"][:, :, :64].contiguous(), d["k"][:, :, :64].contiguous(), d["v"],
+                                     d["gate"], d["beta"], meta)   # dk 64
+    small = torch.zeros((1, 2, 64, 128), device="cuda")
+    with pytest.raises(ssd.SSDError, match="capacity"):
+        ssd.gated_delta_chunk_varlen(d["q"], d["k"], d["v"], d["gate"], d["beta"], meta, chunk_states=small)
+    torch.cuda.synchronize()
+
+
+def test_gdn_bad_slot_sets_error_flag():
+    w = make_gdn_inputs([130], 2, 1, 128, 64, seed=11)
+    d = _dev(w)
+    meta = ssd.varlen_metadata(d["cu_seqlens"], CS, total_tokens=w.total_tokens)
+    cache = torch.full((2, 2, 64, 128), float("nan"), device="cuda")
+    dst = torch.tensor([-1, 5, 1], dtype=torch.int32, device="cuda")   # 5 >= capacity 2
+    ssd.gated_delta_chunk_varlen(d["q"], d["k"], d["v"], d["gate"], d["beta"], meta, scale=w.scale,
+                                 chunk_states=cache, chunk_state_dst=dst)
+    torch.cuda.synchronize()
+    assert int(meta.error_flag.item()) & ssd.DATA_BAD_SLOT
+    _, _, cst_ref = _oracle(w, chunk_size=CS)
+    assert torch.isnan(cache[0]).all()
+    check_close(cache[1], cst_ref[2], TOL["bf16"], "slot 1")
+
+
+def test_gdn_full_size_sampled_with_block_checkpoints():
+    """4 x 8894 tokens, 32 value heads on 16 key heads, dk = dv = 128: every output
+    and final state of sampled (sequence, head) pairs, and the 256-token block
+    checkpoints written at the source through the plan."""
+    w = make_gdn_config()
+    S, H = w.nseqs, w.v.shape[1]
+    d = _dev(w)
+    meta = ssd.varlen_metadata(d["cu_seqlens"], CS, total_tokens=w.total_tokens)
+    cache = torch.full((w.num_slots, H, 128, 128), float("nan"), device="cuda")
+    _, dst = ssd.export_chunk_states(meta, w.block_table, w.block_size, state_cache=cache, num_slots=w.num_slots)
+    _, o, fin, _ = _run(w, d, export=cache, dst=dst)
+    bt = w.block_table.numpy()
+    L = w.lengths[0]
+    nblocks = -(-L // w.block_size)
+    rng = np.random.default_rng(0)
+    pairs = [(s, int(rng.integers(H))) for s in range(S)] + [(int(rng.integers(S)), H - 1)]
+    cu = w.cu_seqlens.numpy()
+    for s, h in pairs:
+        log(f"gdn full size: sequence {s} head {h}")
+        o_ref, fin_ref, cst_ref = _oracle(w, CS, seqs=s, heads=h)
+        check_close(o[cu[s]:cu[s + 1], h], o_ref[:, 0], TOL["bf16"], f"o s={s} h={h}")
+        check_close(fin[s, h], fin_ref[0, 0], TOL["bf16"], f"final s={s} h={h}")
+        for kb in range(nblocks):
+            end = min((kb + 1) * w.block_size, L)
+            check_close(cache[int(bt[s, kb]), h], cst_ref[(end + CS - 1) // CS - 1, 0], TOL["bf16"],
+                        f"block {kb} s={s} h={h}")
+    used = set(int(v) for v in bt[:, :nblocks].ravel())
+    unused = [sl for sl in range(w.num_slots) if sl not in used]
+    assert all(torch.isnan(cache[sl]).all() for sl in unused)
+    assert torch.isfinite(o).all() and torch.isfinite(fin).all()
