@@ -44,33 +44,45 @@ def ingest_counters(fetch_csv, write_csv, config, calib_mib, workload="prefill",
     then WRITE_SIZE; KiB per dispatch) into the HBM traffic of one launch of the
     workload's kernel, each counter scaled by what it reads for the calibration
     kernel (one elementwise pass that reads and writes M MiB)."""
-    decode, conv = workload == "decode", workload == "conv1d"
-    out = out or (DECODE_COUNTERS if decode else CONV_COUNTERS if conv else counter_path(config))
-    tag = "ssd_decode" if decode else "ssd_conv1d" if conv else "ssd_scan"
+    other = {"decode": (DECODE_COUNTERS, "ssd_decode_kernel", DECODE_SOURCES),
+             "conv1d": (CONV_COUNTERS, "ssd_conv1d_kernel", CONV_SOURCES),
+             "gdn": (GDN_COUNTERS, "ssd_gdn_kernel", GDN_SOURCES)}.get(workload)
+    out = out or (other[0] if other else counter_path(config))
+    kname = other[1] if other else scan_kernel_name(config)
+    tag = kname[: -len("_kernel")] if other else "ssd_scan"
     import csv
 
     def read(path):
-        """(scan readings, calibration reading) of one pass: the calibration
-        dispatch is the elementwise kernel with the largest reading (the add);
-        only the scan dispatches issued before it count, which are the warm-up
-        and timed steps (the export-overhead runs after it include launches
-        that write no checkpoints)."""
+        """(readings per kernel name, calibration reading) of one pass: the
+        calibration dispatch is the elementwise kernel with the largest reading
+        (the add); only the workload's dispatches issued before it count, which
+        are the warm-up and timed steps (the export-overhead runs after it
+        include launches that write no checkpoints)."""
         rows = [(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
                 for r in csv.DictReader(open(path))]
         cal_id, cal = max(((i, v) for i, k, v in rows if "elementwise" in k), key=lambda t: t[1])
-        scan = [v for i, k, v in rows if tag in k and i < cal_id]
-        if not scan:
+        per = {}
+        for i, k, v in rows:
+            if tag in k and i < cal_id:
+                per.setdefault(k, []).append(v)
+        if not per:
             raise ValueError(f"{path}: no {tag} dispatch before the calibration copy")
-        return scan, cal
+        return per, cal
 
-    (scan_f, cal_f), (scan_w, cal_w) = read(fetch_csv), read(write_csv)
+    (per_f, cal_f), (per_w, cal_w) = read(fetch_csv), read(write_csv)
     calib_kib = calib_mib * 1024.0
     ff, fw = calib_kib / cal_f, calib_kib / cal_w
-    fk, wk = sum(scan_f) / len(scan_f), sum(scan_w) / len(scan_w)
-    rec = {"kernel": "ssd_decode_kernel" if decode else "ssd_conv1d_kernel" if conv else scan_kernel_name(config),
-           "kernel_hash": kernel_hash(DECODE_SOURCES if decode else CONV_SOURCES if conv else KERNEL_SOURCES),
-           "config": workload if (decode or conv) else config,
-           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": len(scan_f),
+    # one launch of each matching kernel per call: sum of the per-kernel averages
+    fk = sum(sum(v) / len(v) for v in per_f.values())
+    wk = sum(sum(v) / len(v) for v in per_w.values())
+    rec = {"kernel": kname if len(per_f) == 1 else " + ".join(sorted(per_f)),
+           "kernel_hash": kernel_hash(other[2] if other else KERNEL_SOURCES),
+           "config": workload if other else config,
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+           "dispatches": min(len(v) for v in per_f.values()),
+           "per_kernel_kib": {k: {"fetch": sum(per_f[k]) / len(per_f[k]),
+                                  "write": sum(per_w.get(k, [0.0])) / max(len(per_w.get(k, [])), 1)}
+                              for k in per_f},
            "calibration_mib": calib_mib, "calibration_fetch_kib": cal_f, "calibration_write_kib": cal_w,
            "fetch_scale": ff, "write_scale": fw,
            "hbm_bytes_per_launch": (fk * ff + wk * fw) * 1024.0}
@@ -330,6 +342,167 @@ def cpu_baseline_conv1d(b):
                        f"including the float64 widening of x")
 
 
+GDN_COUNTERS = os.path.join(ROOT, "profiles", "gdn_prefix_cache_4x8894_h32g16_counters.json")
+GDN_SOURCES = ["ssd_gdn.hip", "ssd_scan.hpp", "ssd_internal.h"]
+
+
+def gdn_work(w, n_ckpt):
+    """Algorithmic bytes and flops of one GDN chunk call. Bytes: q, k read once
+    per key head, v read and o written once, gate and beta read once, each
+    flagged initial state read, each final state and checkpoint written once.
+    Flops: per chunk of Lc tokens and value head, the chunked form's products
+    (K K^T and Q K^T lower triangles, W and T beta V, W H0, Q H0, the causal
+    Mq U and the state update K^T U), counted once per value head."""
+    T, G, dk = w.q.shape
+    H, dv = w.v.shape[1], w.v.shape[2]
+    state = H * dv * dk * 4
+    n_init = int(w.has_initial_state.sum())
+    bytes_ = T * (2 * G * dk * 2 + 2 * H * dv * 2 + 2 * H * 4) + (n_init + w.nseqs) * state + n_ckpt * state
+    flops = 0
+    for L in w.lengths:
+        for c0 in range(0, L, w.chunk_size):
+            Lc = min(w.chunk_size, L - c0)
+            tri = Lc * (Lc + 1) // 2
+            flops += 2 * H * (2 * tri * dk + tri * dk + tri * dv + 3 * Lc * dk * dv + tri * dv + Lc * dk * dv)
+    return bytes_, flops
+
+
+class GdnRun:
+    """Device inputs and outputs of the GDN workload, and its step."""
+
+    def __init__(self, dev):
+        import torch
+        from selective_state_space_cu_amd import ssd
+        from selective_state_space_cu_amd.workloads import make_gdn_config
+        self.ssd = ssd
+        w = self.w = make_gdn_config()
+        self.d = {k: getattr(w, k).to(dev).contiguous() for k in
+                  ("q", "k", "v", "gate", "beta", "initial_states", "has_initial_state", "cu_seqlens")}
+        S, H, dv, dk = w.nseqs, w.v.shape[1], w.v.shape[2], w.q.shape[2]
+        self.bt = w.block_table.to(dev)
+        self.o = torch.empty_like(self.d["v"])
+        self.fin = torch.empty((S, H, dv, dk), dtype=torch.float32, device=dev)
+        self.cache = torch.zeros((w.num_slots, H, dv, dk), dtype=torch.float32, device=dev)
+        self.init = self.d["initial_states"] if int(w.has_initial_state.sum()) else None
+        self.has = self.d["has_initial_state"] if self.init is not None else None
+        self.ev, self.ev_meta = [], []
+        self.prepare()
+        self.n_ckpt = int((self.dst >= 0).sum().item())
+        self.ws = torch.empty(ssd.gated_delta_workspace_size(self.meta, H), dtype=torch.uint8, device=dev)
+
+    def prepare(self):
+        self.meta = self.ssd.varlen_metadata(self.d["cu_seqlens"], self.w.chunk_size,
+                                             total_tokens=self.w.total_tokens)
+        _, self.dst = self.ssd.export_chunk_states(self.meta, self.bt, self.w.block_size, num_slots=self.w.num_slots)
+
+    def scan(self, export=True):
+        d = self.d
+        self.ssd.gated_delta_chunk_varlen(d["q"], d["k"], d["v"], d["gate"], d["beta"], self.meta,
+                                          scale=self.w.scale, initial_states=self.init,
+                                          has_initial_state=self.has, o=self.o, final_states=self.fin,
+                                          chunk_states=self.cache if export else None,
+                                          chunk_state_dst=self.dst if export else None, workspace=self.ws)
+
+
+
+def bench_gdn(args):
+    """One JSON line for the chunked gated delta rule with per-chunk state export
+    on the prefix-cache batch (4 x 8894 tokens, 32 value heads on 16 key heads,
+    dk = dv = 128, chunk 64, 256-token blocks); a step is the chunk metadata, the
+    checkpoint plan and the GDN chunk kernel writing the block checkpoints."""
+    import numpy as np
+    import torch
+    from selective_state_space_cu_amd.workloads import GDN_CONFIG
+
+    dev = torch.device("cuda:0")
+    run = GdnRun(dev)
+    w = run.w
+    for _ in range(args.warmup):
+        run.step(False)
+    torch.cuda.synchronize()
+    if int(run.meta.error_flag.item()) != 0:
+        raise RuntimeError("device error flag set")
+    run.ev.clear()
+    run.ev_meta.clear()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run.step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = sum(a.elapsed_time(b) for a, b in run.ev) / len(run.ev)
+    meta_ms = sum(a.elapsed_time(b) for a, b in run.ev_meta) / len(run.ev_meta)
+    if args.copy_calib_mib:
+        calib_copy(args.copy_calib_mib, dev)
+    flush = torch.empty(FLUSH_MIB << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(args.cold_calls):
+        flush.fill_(i & 0xff)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run.scan()
+        e1.record()
+        cold.append((e0, e1))
+    torch.cuda.synchronize()
+    cold_ms = np.array([a.elapsed_time(b) for a, b in cold]) if cold else np.array([k_ms])
+    alg, flops = gdn_work(w, run.n_ckpt)
+    traffic = None
+    if os.path.exists(GDN_COUNTERS):
+        with open(GDN_COUNTERS) as f:
+            c = json.load(f)
+        if c.get("kernel_hash") == kernel_hash(GDN_SOURCES):
+            traffic = c["hbm_bytes_per_launch"]
+    ms_per_step = wall * 1e3 / args.steps
+    T = w.total_tokens
+    H, G, dk, dv = w.v.shape[1], w.q.shape[1], w.q.shape[2], w.v.shape[2]
+    med = float(np.median(cold_ms))
+    res = {
+        "metric": "Gated delta rule (GDN) chunked prefill tokens/s on 1 MI355X; % of HBM roofline",
+        "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded; inputs and checkpoint cache resident in HBM)",
+        "config": {"workload": GDN_CONFIG["name"], "nseqs": w.nseqs, "total_tokens": T, "nheads": H,
+                   "nkheads": G, "dk": dk, "dv": dv, "chunk_size": w.chunk_size, "block_size": w.block_size,
+                   "checkpoints_per_step": run.n_ckpt,
+                   "step": "metadata + checkpoint plan + GDN chunk kernel with at-source checkpoint export"},
+        "roofline": {"bound": "hbm", "kernel": "ssd_gdn_prep_kernel + ssd_gdn_scan_kernel (one call)",
+                     "achieved": alg / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": alg / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": alg, "kernel_ms": k_ms, "metadata_and_plan_ms": meta_ms,
+                     "mfma_tflops": flops / (k_ms * 1e-3) / 1e12,
+                     "mfma_frac": flops / (k_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "cold": {"calls": len(cold), "kernel_ms_median": med, "kernel_ms_p10": float(np.percentile(cold_ms, 10)),
+                 "kernel_ms_p90": float(np.percentile(cold_ms, 90)),
+                 "hbm_frac_median": alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_gdn(w)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_gdn(w):
+    """The float64 GDN oracle over the whole workload, one key head (its value
+    heads) per call so that the float64 copies stay small."""
+    import numpy as np
+    import oracle
+    H, G = w.v.shape[1], w.q.shape[1]
+    per = H // G
+    f = lambda t: t.float().numpy().astype(np.float64)   # noqa: E731
+    t = time.perf_counter()
+    for g in range(G):
+        hs = slice(g * per, (g + 1) * per)
+        oracle.gated_delta(f(w.q[:, g:g + 1]), f(w.k[:, g:g + 1]), f(w.v[:, hs]), f(w.gate[:, hs]),
+                           f(w.beta[:, hs]), w.cu_seqlens.numpy(), w.scale, f(w.initial_states[:, hs]),
+                           w.has_initial_state.numpy(), chunk_size=w.chunk_size)
+    dt_s = time.perf_counter() - t
+    return dict(value=w.total_tokens / dt_s, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"the whole workload ({w.total_tokens} tokens, all {H} value heads), float64, "
+                       f"chunk-state recording on, one key head per call; {dt_s:.2f} s wall including "
+                       f"the float64 widening of the inputs")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,10 +517,11 @@ def main():
                     help="cold protocol on --config only (default: every graded prefill workload)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
-    ap.add_argument("--workload", choices=("prefill", "decode", "conv1d"), default="prefill",
+    ap.add_argument("--workload", choices=("prefill", "decode", "conv1d", "gdn"), default="prefill",
                     help="prefill (default): the scan step; decode: one dual-anchor decode step "
                          "per sequence on the 256-sequence decode batch; conv1d: the causal conv1d "
-                         "before the scan on the prefix-cache batch's 5120 channels")
+                         "before the scan on the prefix-cache batch's 5120 channels; gdn: the chunked "
+                         "gated delta rule with per-chunk state export on the same batch")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic record from two rocprofv3 counter CSVs and exit "
                          "(with --copy-calib-mib giving the calibration size)")
@@ -367,6 +541,9 @@ def main():
         return
     if args.workload == "conv1d":
         bench_conv1d(args)
+        return
+    if args.workload == "gdn":
+        bench_gdn(args)
         return
     import torch
     from selective_state_space_cu_amd import ssd
@@ -579,6 +756,9 @@ def export_overhead(ssd, run, rounds=6, per=10):
     return {"scan_ms_with": med[True], "scan_ms_without": med[False],
             "overhead_frac": med[True] / med[False] - 1.0,
             "note": "kernel-level: the same scan with and without writing the block checkpoints"}
+
+
+GdnRun.step = PrefillRun.step   # same step shape: metadata + plan, then the timed kernel
 
 
 if __name__ == "__main__":

@@ -287,15 +287,26 @@ ssd_status ssd_prefill_bites(int32_t nseqs, const int32_t *num_computed_tokens, 
  * block-checkpoint plan of ssd_export_chunk_states (state_elems = H dv dk)
  * feeds chunk_state_dst. Supported: in_dtype SSD_BF16, dk 128, dv a multiple
  * of 64, nheads % nkheads == 0.
+ * workspace: device memory of at least
+ * ssd_gated_delta_workspace_size(meta->max_chunks, nheads) bytes, 16-byte
+ * aligned, owned by the caller; it holds (I + A)^-1 of every chunk and head
+ * between the call's two kernels and is free again when the call's work on
+ * `stream` has finished. Calls that overlap in time need separate workspaces.
  * Errors: SSD_ERR_NULL_ARG, SSD_ERR_SHAPE, SSD_ERR_DTYPE, SSD_ERR_UNSUPPORTED
- * (another dtype, dk, dv or chunk size), SSD_ERR_CAPACITY, SSD_ERR_HIP.
- * Asynchronous on `stream`; the caller owns every buffer; no workspace.
+ * (another dtype, dk, dv or chunk size), SSD_ERR_CAPACITY (chunk_states or
+ * workspace too small), SSD_ERR_HIP.
+ * Asynchronous on `stream`; the caller owns every buffer.
  */
 ssd_status ssd_gated_delta_chunk_varlen(
     const void *q, const void *k, const void *v, const float *gate, const float *beta, float scale,
     ssd_dtype in_dtype, const ssd_varlen_meta *meta, int32_t nheads, int32_t nkheads, int32_t dk, int32_t dv,
     const float *initial_states, const int32_t *has_initial_state, void *o, float *final_states,
-    float *chunk_states, const int32_t *chunk_state_dst, int32_t chunk_states_capacity, void *stream);
+    float *chunk_states, const int32_t *chunk_state_dst, int32_t chunk_states_capacity,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes ssd_gated_delta_chunk_varlen needs for a batch whose
+ * metadata has `max_chunks` and for `nheads` value heads (0 for no chunks). */
+size_t ssd_gated_delta_workspace_size(int32_t max_chunks, int32_t nheads);
 
 /* Static, NUL-terminated description of a status code. */
 const char *ssd_status_string(ssd_status status);

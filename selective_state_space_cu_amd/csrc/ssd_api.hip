@@ -192,13 +192,18 @@ ssd_status ssd_causal_conv1d_varlen(const void *x, const float *weight, const fl
                ? SSD_OK : SSD_ERR_HIP;
 }
 
+size_t ssd_gated_delta_workspace_size(int32_t max_chunks, int32_t nheads) {
+    if (max_chunks <= 0 || nheads <= 0) return 0;
+    return (size_t)max_chunks * (size_t)nheads * ssd::kGdnWsBytes;
+}
+
 ssd_status ssd_gated_delta_chunk_varlen(const void *q, const void *k, const void *v, const float *gate,
                                         const float *beta, float scale, ssd_dtype in_dtype,
                                         const ssd_varlen_meta *meta, int32_t nheads, int32_t nkheads, int32_t dk,
                                         int32_t dv, const float *initial_states, const int32_t *has_initial_state,
                                         void *o, float *final_states, float *chunk_states,
                                         const int32_t *chunk_state_dst, int32_t chunk_states_capacity,
-                                        void *stream) {
+                                        void *workspace, size_t workspace_bytes, void *stream) {
     ssd_status st = check_meta(meta);
     if (st != SSD_OK) return st;
     if (in_dtype != SSD_F32 && in_dtype != SSD_BF16) return SSD_ERR_DTYPE;
@@ -213,8 +218,10 @@ ssd_status ssd_gated_delta_chunk_varlen(const void *q, const void *k, const void
         if (chunk_states_capacity <= 0) return SSD_ERR_CAPACITY;
         if (chunk_state_dst == nullptr && chunk_states_capacity < meta->max_chunks) return SSD_ERR_CAPACITY;
     }
+    if (!empty && (workspace == nullptr || workspace_bytes < ssd_gated_delta_workspace_size(meta->max_chunks, nheads)))
+        return SSD_ERR_CAPACITY;
     for (const void *p : {q, k, v, (const void *)o, (const void *)final_states, (const void *)initial_states,
-                          (const void *)chunk_states})
+                          (const void *)chunk_states, (const void *)workspace})
         if (p != nullptr && !aligned16(p)) return SSD_ERR_SHAPE;
     ssd::GdnArgs a{};
     a.q = static_cast<const uint16_t *>(q); a.k = static_cast<const uint16_t *>(k);
@@ -222,7 +229,9 @@ ssd_status ssd_gated_delta_chunk_varlen(const void *q, const void *k, const void
     a.init = initial_states; a.has_init = has_initial_state;
     a.o = static_cast<uint16_t *>(o); a.final_states = final_states;
     a.chunk_states = chunk_states; a.chunk_state_dst = chunk_state_dst;
+    a.workspace = static_cast<uint16_t *>(workspace);
     a.cu_seqlens = meta->cu_seqlens; a.seq_chunk_start = meta->seq_chunk_start; a.seq_order = meta->seq_order;
+    a.chunk_offsets = meta->chunk_offsets; a.chunk_seq_idx = meta->chunk_seq_idx;
     a.error_flag = meta->error_flag; a.scale = scale;
     a.T = meta->total_tokens; a.S = meta->nseqs; a.H = nheads; a.G = nkheads; a.dv = dv;
     a.max_chunks = meta->max_chunks; a.capacity = chunk_states ? chunk_states_capacity : 0;

@@ -16,23 +16,21 @@
 // (U_i is the delta-rule write value of token i; the token loop computes the
 // same map one token at a time.)
 //
-// One workgroup per (sequence, value head, 64 value columns), four waves, one
-// per SIMD: wave w owns value columns 16 w .. 16 w + 15 and carries their
-// state rows S[v][0..dk) (float32, in the accumulator layout of the state
-// update: register u, element r = S[16 w + q][16 u + 4 g + r] for lane
-// (g, q)) from chunk to chunk. Per chunk, in order (barrier between phases):
-//   load K, Q (64 x 128) and this slice of V (64 x 64) into LDS (zero rows past
-//   the sequence: gate 0 and beta 0 make them neutral) and the gate / beta rows;
-//   tables (cumsum, gamma, decay factors);
-//   K K^T and Q K^T sub-tiles on the matrix cores, masked by the decay, into A
-//   (float32) and the causal matrix Mq (bf16);
-//   T: 16 x 16 diagonal blocks by forward substitution, then block rows below
-//   (float32 VALU; exact to float32);
-//   W^T = (beta gamma K)^T T^T, U^T = (beta V)^T T^T - H0^T W^T (bf16 matrix products,
-//   float32 accumulation);
-//   O^T = (H0^T Q^T) diag(gamma) + U^T Mq^T, scaled; the state update
-//   H = gamma_last H + K^T (rho U), rho_j = e^(G_last - G_j); the state after
-//   the chunk goes to its checkpoint slot when the plan names one.
+// Two kernels on one stream:
+//  ssd_gdn_prep_kernel, one workgroup per (chunk, value head), all in parallel
+//    (four workgroups per CU):
+//    A on the matrix cores (bf16 K K^T, masked by the decay, float32), T by
+//    forward substitution on the four 16 x 16 diagonal blocks and block merges
+//    on the float32 matrix cores
+//        T_IJ = -T_II (sum_K A_IK T_KJ)   (first the blocks next to the diagonal,
+//                                         then the 32 x 32 corner),
+//    written to the workspace as bf16 (64 x 64 per chunk and head). T depends
+//    on neither the state nor the values, so no chunk waits for another here.
+//  ssd_gdn_scan_kernel, one workgroup per (sequence, value head, 64 value
+//    columns), walks the chunks in order with the state in registers; per chunk
+//    only matrix-core products: W, T beta V, Q H0, the causal Q K^T (masked), then
+//    U = T beta V - W H0, O and the state update. The next chunk's K, Q, V and T
+//    are loaded into registers while the current chunk computes.
 #include <hip/hip_runtime.h>
 
 #include "ssd_scan.hpp"
@@ -42,47 +40,280 @@ namespace ssd {
 namespace {
 
 constexpr int kGdnDk = 128;            // key dimension
-constexpr int kGdnCols = 64;           // value columns per workgroup
+constexpr int kGdnCols = 64;           // value columns per scan workgroup
 constexpr int kGdnChunk = 64;          // tokens per chunk
-// LDS layouts (bytes), those of the scan's general kernel: K rows in the B
-// layout (pitch 288 + 128 per 8 rows: conflict-free row-fragment and
-// transposed reads), Q and W rows in the C layout (pitch 272), V and U rows in
-// the x layout (pitch 144), T and Mq rows in the decay-matrix layout (160).
-constexpr int kPB = kGdnDk * 2 + 32, kGB = 8 * kPB + 128, kTileK = 8 * kGB;
-constexpr int kPC = kGdnDk * 2 + 16, kTileQ = kGdnChunk * kPC;
-constexpr int kPX = kGdnCols * 2 + 16, kTileV = kGdnChunk * kPX;
-constexpr int kMPB = (kGdnChunk + 16) * 2, kTileM = kGdnChunk * kMPB;
-constexpr int kPF = kGdnChunk + 1;     // float32 64 x 64 matrices: row pitch (floats)
+// Row tiles (K, Q, W: 64 rows of 128 bf16): rows in groups of 8 (pitch kPB, 128
+// extra bytes per group), and within every 32-column k step the columns
+// interleaved in groups of 4 -- c = 32 kc + 16 hh + 4 gg + x sits at
+// 32 kc + 8 gg + 4 hh + x -- so that the eight elements lane group gg feeds the
+// matrix cores in one k step (columns 4 gg.. and 16 + 4 gg..) are one 16-byte read,
+// and any 4 consecutive columns from a multiple of 4 stay 8 contiguous bytes
+// (the transposed reads).
+constexpr int kPB = kGdnDk * 2 + 32, kGB = 8 * kPB + 128, kTileR = 8 * kGB;
+// V and U rows (64 value columns): pitch 144; T and Mq rows: pitch 160
+[[maybe_unused]] constexpr int kPX = kGdnCols * 2 + 16, kTileV = kGdnChunk * kPX;
+[[maybe_unused]] constexpr int kMPB = (kGdnChunk + 16) * 2, kTileM = kGdnChunk * kMPB;
+// float32 16 x 16 blocks of the lower triangle of a 64 x 64 matrix, stored
+// compactly: block (I, J), I >= J, at (I (I + 1) / 2 + J) * kBlk floats, rows of
+// kBP floats (16-byte aligned)
+constexpr int kBP = 20, kBlk = 16 * kBP, kTri = 10 * kBlk;
+static_assert(2 * kTri * 4 >= kTileR, "T and T^T blocks reuse the K tile");
+static_assert(kGdnWsBytes == kGdnChunk * kGdnChunk * 2, "workspace: one bf16 T per (chunk, head)");
 
-__device__ __forceinline__ int gbrow(int r) { return (r >> 3) * kGB + (r & 7) * kPB; }
+[[maybe_unused]] __device__ __forceinline__ int rt_row(int r) { return (r >> 3) * kGB + (r & 7) * kPB; }
+[[maybe_unused]] __device__ __forceinline__ int rt_col(int c) {   // byte offset of column c in a row
+    return (32 * (c >> 5) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3)) * 2;
+}
+// row fragment of k step kc for lane group g (the permuted k order of the state fragments)
+[[maybe_unused]] __device__ __forceinline__ Ops<uint16_t>::Frag rt_frag(const unsigned char *tile, int row, int kc,
+                                                                        int g) {
+    return Ops<uint16_t>::Frag{*reinterpret_cast<const u32x4 *>(tile + rt_row(row) + 64 * kc + 16 * g)};
+}
+// transposed fragment: column c0 + q of rows kb .. kb + 7 (kb a multiple of 8)
+[[maybe_unused]] __device__ __forceinline__ Ops<uint16_t>::Frag rt_tr(const unsigned char *tile, int kb, int c0,
+                                                                      int q) {
+    using O = Ops<uint16_t>;
+    return O::tr(tile + rt_row(kb) + O::tr_row(q) * kPB + rt_col(c0 + O::tr_col(q)), 4 * kPB);
+}
+// one staged 16-byte piece (columns 8 cpos .. 8 cpos + 7 of row r) into a row tile
+[[maybe_unused]] __device__ __forceinline__ void rt_store(unsigned char *tile, int r, int cpos, const u32x4 &v) {
+    unsigned char *row = tile + rt_row(r);
+    *reinterpret_cast<u32x2 *>(row + rt_col(8 * cpos)) = u32x2{v[0], v[1]};
+    *reinterpret_cast<u32x2 *>(row + rt_col(8 * cpos + 4)) = u32x2{v[2], v[3]};
+}
+[[maybe_unused]] __device__ __forceinline__ int tri_blk(int I, int J) { return (I * (I + 1) / 2 + J) * kBlk; }
+
+[[maybe_unused]] __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// 16 x 16 x 16 float32 product on the matrix cores. Lane (g, q) supplies
+// a[r] = X[q][4 g + r] and b[r] = Y[4 g + r][q] (step r sums k = 4 g + r over
+// the four lane groups); the result holds (X Y)[4 g + r][q] in element r, which
+// is the b operand layout of the next product.
+[[maybe_unused]] __device__ __forceinline__ f32x4 mm16(const f32x4 &a, const f32x4 &b, f32x4 c) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) c = mfma4(a[r], b[r], c);
+    return c;
+}
+
+// Buffer resource over `bytes` bytes from p (loads past them read zero)
+[[maybe_unused]] __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, kBufFlags);
+}
+// 16-byte pieces of a chunk's q or k rows (64 rows x 16 pieces, 4 per thread;
+// rows past the chunk's Lc >= 1 tokens read zero)
+[[maybe_unused]] __device__ __forceinline__ void load_rows(u32x4 (&kv)[4], const uint16_t *base, int64_t t0, int Lc,
+                                                           int G, int grp, int tid) {
+    const int rowb = G * kGdnDk * 2;
+    const __amdgpu_buffer_rsrc_t r = rsrc(base + (t0 * G + grp) * kGdnDk, (int64_t)(Lc - 1) * rowb + 256);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int piece = tid + 256 * i;
+        kv[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (piece >> 4) * rowb + 16 * (piece & 15), 0, 0);
+    }
+}
+// one lane per token of a chunk: x[(t0 + lane) H + h] (zero past the chunk's Lc >= 1 tokens)
+[[maybe_unused]] __device__ __forceinline__ float load_token(const float *x, int64_t t0, int Lc, int H, int h,
+                                                             int lane) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(x + t0 * H + h, (int64_t)(Lc - 1) * H * 4 + 4);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, lane * H * 4, 0, 0));
+}
+
+// The three A (or Mq) sub-tiles (I, J), I >= J, of wave w: ten over four waves,
+// the last two waves repeat their last sub-tile (identical writes)
+[[maybe_unused]] __device__ __forceinline__ int sub_tile(int wave, int n) {
+    const uint32_t codes = wave == 0 ? 0x333000u : wave == 1 ? 0x311110u : wave == 2 ? 0x212120u : 0x333222u;
+    return (codes >> (8 * n)) & 0xff;   // I in the high nibble, J in the low
+}
 
 }  // namespace
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void ssd_gdn_chunk_kernel(GdnArgs a)
+// ---------------------------------------------------------------------------
+// T = (I + A)^-1 for one (chunk, value head)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ssd_gdn_prep_kernel(GdnArgs a)
 #if !defined(__HIP_DEVICE_COMPILE__)
-{   // the host pass only needs the signature (for the launch stub)
+{
+}
+#else
+{
+    using O = Ops<uint16_t>;
+    constexpr int CH = kGdnChunk;
+    __shared__ __align__(16) float fTT[2 * kTri];   // K rows (row tile) first; then T and T^T blocks
+    __shared__ __align__(16) float fA[kTri];        // A blocks (float32, strictly lower)
+    __shared__ __align__(16) float tab[2 * 64];     // G (log2), beta
+    unsigned char *const sK = reinterpret_cast<unsigned char *>(fTT);
+    float *const fT = fTT, *const fTt = fTT + kTri;   // T_IJ blocks; (T_IJ)^T blocks
+    float *const tG = tab, *const tBeta = tab + 64;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = lane & 15, g = lane >> 4;
+
+    if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
+    const int H = a.H, G = a.G;
+    const int gc = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    if (gc >= a.max_chunks) return;
+    const int s = a.chunk_seq_idx[gc];
+    if (s < 0 || s >= a.S) return;
+    const int t0 = a.chunk_offsets[gc], t1 = a.chunk_offsets[gc + 1];
+    if (t0 < 0 || t1 > a.T || t1 <= t0 || t1 - t0 > CH) return;
+    const int Lc = t1 - t0;
+    const int grp = h / (H / G);
+
+    {
+        u32x4 kv[4];
+        load_rows(kv, a.k, t0, Lc, G, grp, tid);
+        float gt = 0.0f, bt = 0.0f;
+        if (wave == 0) {
+            gt = load_token(a.gate, t0, Lc, H, h, lane);
+            bt = load_token(a.beta, t0, Lc, H, h, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rt_store(sK, (tid + 256 * i) >> 4, (tid + 256 * i) & 15, kv[i]);
+        if (wave == 0) {   // inclusive cumsum of the log2-decay (zero past the chunk: neutral)
+            tG[lane] = wave_scan(gt * kLog2e);
+            tBeta[lane] = bt;
+        }
+    }
+    lds_barrier();
+
+    // ---- A sub-tiles: A[i][j] = beta_i e^(G_i - G_j) k_i . k_j (j < i); lane (g, q): i = 16 I + q,
+    //      j = 16 J + 4 g + r
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        const int code = sub_tile(wave, n), I = code >> 4, J = code & 15;
+        f32x4 kk = {0, 0, 0, 0};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) kk = O::mma(kk, rt_frag(sK, 16 * J + q, kc, g), rt_frag(sK, 16 * I + q, kc, g));
+        const int i = 16 * I + q;
+        const float gi = tG[i], bi = tBeta[i];
+        const f32x4 gj = *reinterpret_cast<const f32x4 *>(tG + 16 * J + 4 * g);
+        f32x4 fa;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(fminf(gi - gj[r], 0.0f));
+            fa[r] = (16 * J + 4 * g + r < i) ? bi * kk[r] * e : 0.0f;
+        }
+        *reinterpret_cast<f32x4 *>(fA + tri_blk(I, J) + q * kBP + 4 * g) = fa;
+    }
+    lds_barrier();
+
+    // ---- diagonal blocks by forward substitution (wave w: block w; lane column j = q;
+    //      the four lane groups compute the same column): T[i][j] = [i == j] - sum_{m < i} A[i][m] T[m][j]
+    {
+        const float *ab = fA + tri_blk(wave, wave);
+        float tc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tc[i] = i == q ? 1.0f : 0.0f;
+#pragma unroll
+        for (int m = 0; m < 15; ++m)
+#pragma unroll
+            for (int i = m + 1; i < 16; ++i) tc[i] = fmaf(-ab[i * kBP + m], tc[m], tc[i]);
+        if (g == 0) {
+            float *tb = fT + tri_blk(wave, wave), *tt = fTt + tri_blk(wave, wave);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tb[i * kBP + q] = tc[i];
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                *reinterpret_cast<f32x4 *>(tt + q * kBP + 4 * i4) =
+                    f32x4{tc[4 * i4], tc[4 * i4 + 1], tc[4 * i4 + 2], tc[4 * i4 + 3]};
+        }
+    }
+    lds_barrier();
+
+    // ---- blocks next to the diagonal: T_10 (wave 0), T_32 (wave 1): T_{J+1,J} = -T_{J+1,J+1} A_{J+1,J} T_JJ
+    if (wave < 2) {
+        const int J = 2 * wave, I = J + 1;
+        const f32x4 p = mm16(*reinterpret_cast<const f32x4 *>(fA + tri_blk(I, J) + q * kBP + 4 * g),
+                             *reinterpret_cast<const f32x4 *>(fTt + tri_blk(J, J) + q * kBP + 4 * g),
+                             f32x4{0, 0, 0, 0});
+        const f32x4 t = -mm16(*reinterpret_cast<const f32x4 *>(fT + tri_blk(I, I) + q * kBP + 4 * g), p,
+                              f32x4{0, 0, 0, 0});
+        // t[r] = T[16 I + 4 g + r][16 J + q]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fT[tri_blk(I, J) + (4 * g + r) * kBP + q] = t[r];
+        *reinterpret_cast<f32x4 *>(fTt + tri_blk(I, J) + q * kBP + 4 * g) = t;
+    }
+    lds_barrier();
+
+    // ---- the 32 x 32 corner, one block per wave ((2,0), (2,1), (3,0), (3,1)):
+    //      Y_KJ = sum_{J <= L <= 1} A_KL T_LJ,  T_IJ = -sum_{2 <= K <= I} T_IK Y_KJ
+    {
+        const int I = 2 + (wave >> 1), J = wave & 1;
+        f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int K = 2; K < 4; ++K) {
+            if (K > I) continue;
+            f32x4 y = {0, 0, 0, 0};
+#pragma unroll
+            for (int L = 0; L < 2; ++L) {
+                if (L < J) continue;
+                y = mm16(*reinterpret_cast<const f32x4 *>(fA + tri_blk(K, L) + q * kBP + 4 * g),
+                         *reinterpret_cast<const f32x4 *>(fTt + tri_blk(L, J) + q * kBP + 4 * g), y);
+            }
+            acc = mm16(*reinterpret_cast<const f32x4 *>(fT + tri_blk(I, K) + q * kBP + 4 * g), y, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fT[tri_blk(I, J) + (4 * g + r) * kBP + q] = -acc[r];
+    }
+    lds_barrier();
+
+    // ---- T (unit lower triangular) -> bf16, row-major 64 x 64, into the workspace
+    {
+        uint16_t *ws = a.workspace + ((int64_t)gc * H + h) * (CH * CH);
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int e = 8 * (tid + 256 * it), i = e >> 6, j0 = e & 63, I = i >> 4, J = j0 >> 4;
+            const float *src = fT + tri_blk(I, J <= I ? J : I) + (i & 15) * kBP + (j0 & 15);
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(src), hi = *reinterpret_cast<const f32x4 *>(src + 4);
+            float v8[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v8[x] = j0 + x <= i ? (x < 4 ? lo[x] : hi[x - 4]) : 0.0f;
+            *reinterpret_cast<u32x4 *>(ws + e) = u32x4{pack_bf16(v8[0], v8[1]), pack_bf16(v8[2], v8[3]),
+                                                       pack_bf16(v8[4], v8[5]), pack_bf16(v8[6], v8[7])};
+        }
+    }
+}
+#endif
+
+// ---------------------------------------------------------------------------
+// The chunk walk of one (sequence, value head, 64 value columns)
+// ---------------------------------------------------------------------------
+//
+// Four waves, one per SIMD: wave w owns value columns 16 w .. 16 w + 15 of the
+// slice and carries their state rows S[v][0..dk) (float32, in the accumulator
+// layout of the state update: register u, element r = S[16 w + q][16 u + 4 g + r]
+// for lane (g, q)) from chunk to chunk. Per chunk:
+//   (1) Mq = (e^(G_i - G_j) q_i . k_j)_{j <= i} (bf16, sub-tiles over the waves),
+//       W^T = (beta gamma K)^T T^T (wave w: keys 32 w ..), and in registers this
+//       wave's (beta V)^T T^T and H0^T Q^T; the next chunk's loads in flight;
+//   (2) U^T = (beta V)^T T^T - H0^T W^T -> this wave's columns of the U tile;
+//       O^T = scale ((H0^T Q^T) diag(gamma) + U^T Mq^T); H = gamma_last H + K^T (rho U),
+//       rho_j = e^(G_last - G_j); the state after the chunk to its checkpoint slot;
+//   (3) the next chunk's tiles into LDS and its tables.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ssd_gdn_scan_kernel(GdnArgs a)
+#if !defined(__HIP_DEVICE_COMPILE__)
+{
 }
 #else
 {
     using O = Ops<uint16_t>;
     using Frag = O::Frag;
-    typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
     constexpr int DK = kGdnDk, CH = kGdnChunk;
 
-    __shared__ __align__(16) unsigned char sK[kTileK];
-    __shared__ __align__(16) unsigned char sQ[kTileQ];
+    __shared__ __align__(16) unsigned char sK[kTileR];
+    __shared__ __align__(16) unsigned char sQ[kTileR];
+    __shared__ __align__(16) unsigned char sW[kTileR];
     __shared__ __align__(16) unsigned char sV[kTileV];
-    __shared__ __align__(16) unsigned char sW[kTileQ];
     __shared__ __align__(16) unsigned char sU[kTileV];
     __shared__ __align__(16) unsigned char sT[kTileM];
     __shared__ __align__(16) unsigned char sMq[kTileM];
-    __shared__ __align__(16) float fA[CH * kPF];   // A (float32), then the state staging area (with fT)
-    __shared__ __align__(16) float fT[CH * kPF];   // T (float32)
-    // tables of the chunk: G (log2), gamma, beta, beta gamma, rho, V, Bf (64 each) and P (16)
-    __shared__ __align__(16) float tab[7 * 64 + 16];
+    // tables of the chunk: G (log2), gamma, beta, beta gamma, rho (64 each)
+    __shared__ __align__(16) float tab[5 * 64];
     float *const tG = tab, *const tGam = tab + 64, *const tBeta = tab + 128, *const tBG = tab + 192,
-                 *const tRho = tab + 256, *const tVf = tab + 320, *const tBf = tab + 384, *const tP = tab + 448;
+                 *const tRho = tab + 256;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -116,275 +347,181 @@ void ssd_gdn_chunk_kernel(GdnArgs a)
         for (int u = 0; u < 8; ++u) st[u] = *reinterpret_cast<const f32x4 *>(src + 16 * u + 4 * g);
     }
 
-    // zero the strictly-upper sub-tiles that the causal products read
-    // (row block 0 x column block 1, row block 2 x column block 3) in T and Mq
+    // the strictly-upper sub-tiles that the causal products read (row block 0 x
+    // column block 1, row block 2 x column block 3) stay zero in Mq
     {
         const int t2 = tid & 127, r = t2 >> 3, part = t2 & 7;   // 16 rows x 8 pieces of 4 bytes per sub-tile
-        const int which = tid >> 7;                             // 0: sub-tile (0,1); 1: (2,3)
-        const int I = which ? 2 : 0, row = 16 * I + r, col = 16 * (I + 1) + 2 * part;
-        *reinterpret_cast<uint32_t *>(sT + row * kMPB + col * 2) = 0u;
+        const int I = (tid >> 7) ? 2 : 0, row = 16 * I + r, col = 16 * (I + 1) + 2 * part;
         *reinterpret_cast<uint32_t *>(sMq + row * kMPB + col * 2) = 0u;
     }
+
+    // ---- staging of one chunk: global loads into registers, then LDS
+    u32x4 rk[4], rq[4], rv[2], rt[2];
+    float rgate = 0.0f, rbeta = 0.0f;
+    const int vrow = H * DV * 2;
+    auto stage_load = [&](int c) {
+        const int64_t t0 = tb + (int64_t)c * CH;
+        const int Lc = min(CH, L - c * CH);
+        load_rows(rk, a.k, t0, Lc, G, grp, tid);
+        load_rows(rq, a.q, t0, Lc, G, grp, tid);
+        const __amdgpu_buffer_rsrc_t r = rsrc(a.v + (t0 * H + h) * DV + v0, (int64_t)(Lc - 1) * vrow + 128);
+        const uint16_t *tsrc = a.workspace + ((int64_t)(c0 + c) * H + h) * (CH * CH);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int piece = tid + 256 * i;
+            rv[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (piece >> 3) * vrow + 16 * (piece & 7), 0, 0);
+            rt[i] = *reinterpret_cast<const u32x4 *>(tsrc + 8 * piece);
+        }
+        if (wave == 0) {
+            rgate = load_token(a.gate, t0, Lc, H, h, lane);
+            rbeta = load_token(a.beta, t0, Lc, H, h, lane);
+        }
+    };
+    auto stage_store = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int piece = tid + 256 * i;
+            rt_store(sK, piece >> 4, piece & 15, rk[i]);
+            rt_store(sQ, piece >> 4, piece & 15, rq[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int piece = tid + 256 * i, r = piece >> 3, cpos = piece & 7;
+            *reinterpret_cast<u32x4 *>(sV + r * kPX + 16 * cpos) = rv[i];
+            *reinterpret_cast<u32x4 *>(sT + r * kMPB + 16 * cpos) = rt[i];
+        }
+        if (wave == 0) {   // tables (lane j = token j; neutral past the end)
+            const float v = wave_scan(rgate * kLog2e);   // inclusive cumsum (log2)
+            const float gam = fast_exp2(v);
+            tG[lane] = v;
+            tGam[lane] = gam;
+            tBeta[lane] = rbeta;
+            tBG[lane] = rbeta * gam;
+            tRho[lane] = fast_exp2(readlane(v, 63) - v);
+        }
+    };
+
+    if (nch > 0) {
+        stage_load(0);
+        stage_store();
+    }
+    lds_barrier();
 
     const float scale = a.scale;
     for (int c = 0; c < nch; ++c) {
         const int64_t t0 = tb + (int64_t)c * CH;
         const int Lc = min(CH, L - c * CH);
+        if (c + 1 < nch) stage_load(c + 1);
 
-        // ---- load the chunk: K, Q rows (256 B), this slice of V (128 B), gate, beta
-        {
+        // ---- (1) Mq sub-tiles: lane (g, q): i = 16 I + q, j = 16 J + 4 g + r
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int piece = tid + 256 * i, r = piece >> 4, cpos = piece & 15;   // 64 rows x 16 pieces
-                u32x4 kv = {0, 0, 0, 0}, qv = {0, 0, 0, 0};
-                if (r < Lc) {
-                    const int64_t off = ((t0 + r) * G + grp) * DK + 8 * cpos;
-                    kv = *reinterpret_cast<const u32x4 *>(a.k + off);
-                    qv = *reinterpret_cast<const u32x4 *>(a.q + off);
-                }
-                *reinterpret_cast<u32x4 *>(sK + gbrow(r) + 16 * cpos) = kv;
-                *reinterpret_cast<u32x4 *>(sQ + r * kPC + 16 * cpos) = qv;
-            }
+        for (int n = 0; n < 3; ++n) {
+            const int code = sub_tile(wave, n), I = code >> 4, J = code & 15;
+            f32x4 qk = {0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int piece = tid + 256 * i, r = piece >> 3, cpos = piece & 7;    // 64 rows x 8 pieces
-                u32x4 vv = {0, 0, 0, 0};
-                if (r < Lc) vv = *reinterpret_cast<const u32x4 *>(a.v + ((t0 + r) * H + h) * DV + v0 + 8 * cpos);
-                *reinterpret_cast<u32x4 *>(sV + r * kPX + 16 * cpos) = vv;
-            }
-            if (wave == 0) {   // tables from gate and beta (lane j = token j; 0 past the end)
-                const float gt = lane < Lc ? a.gate[(t0 + lane) * H + h] * kLog2e : 0.0f;
-                const float bt = lane < Lc ? a.beta[(t0 + lane) * H + h] : 0.0f;
-                const float v = wave_scan(gt);   // inclusive cumsum (log2)
-                const float e0 = readlane(v, 15), e1 = readlane(v, 31), e2 = readlane(v, 47), e3 = readlane(v, 63);
-                const int blk = lane >> 4;
-                const float s_prev = blk == 0 ? 0.0f : (blk == 1 ? e0 : (blk == 2 ? e1 : e2));
-                const float s_end = blk == 0 ? e0 : (blk == 1 ? e1 : (blk == 2 ? e2 : e3));
-                const float gam = fast_exp2(v);
-                tG[lane] = v;
-                tGam[lane] = gam;
-                tBeta[lane] = bt;
-                tBG[lane] = bt * gam;
-                tRho[lane] = fast_exp2(e3 - v);
-                tVf[lane] = fast_exp2(v - s_prev);     // e^(G_i - G_end(block(i) - 1))
-                tBf[lane] = fast_exp2(s_end - v);      // e^(G_end(block(j)) - G_j)
-                if (lane < 16) {
-                    const int J = lane >> 2, dd = lane & 3, I = J + dd;
-                    const float ea = I == 1 ? e0 : (I == 2 ? e1 : e2), eb = J == 0 ? e0 : (J == 1 ? e1 : e2);
-                    tP[lane] = dd == 0 ? 1.0f : (I >= 4 ? 0.0f : fast_exp2(ea - eb));   // e^(G_end(I-1) - G_end(J))
-                }
-            }
-        }
-        lds_barrier();
-
-        // ---- K K^T and Q K^T sub-tiles (I, J = w), I = w .. 3, masked by the decay:
-        //      A[i][j] = beta_i e^(G_i - G_j) k_i.k_j (j < i, float32), Mq[i][j] = e^(G_i - G_j) q_i.k_j (j <= i, bf16)
-        {
-            const int J = wave;
-            Frag kj[4];   // K rows of column block J (row fragments, permuted k order)
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) kj[kc] = O::rowk_perm(sK + gbrow(16 * J + q) + (32 * kc + 4 * g) * 2);
-            float sj[4], bfj[4];
+            for (int kc = 0; kc < 4; ++kc) qk = O::mma(qk, rt_frag(sK, 16 * J + q, kc, g), rt_frag(sQ, 16 * I + q, kc, g));
+            const int i = 16 * I + q;
+            const float gi = tG[i];
+            const f32x4 gj = *reinterpret_cast<const f32x4 *>(tG + 16 * J + 4 * g);
+            float fq[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                sj[r] = tG[16 * J + 4 * g + r];
-                bfj[r] = tBf[16 * J + 4 * g + r];
+                const float e = fast_exp2(fminf(gi - gj[r], 0.0f));
+                fq[r] = (16 * J + 4 * g + r <= i) ? qk[r] * e : 0.0f;
+            }
+            O::mstore4(sMq + i * kMPB + (16 * J + 4 * g) * 2, fq);
+        }
+        // W^T = (beta gamma K)^T T^T: wave w computes key rows 32 w .. 32 w + 31 (u = 2 w, 2 w + 1)
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+            const int u = 2 * wave + uu;
+            Frag kt[2];   // (beta gamma K)^T fragments: key column 16 u + q, tokens 32 ks + 8 g + slot
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 8 * g);
+                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 8 * g + 4);
+                const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+                kt[ks] = O::scale(rt_tr(sK, 32 * ks + 8 * g, 16 * u, q), w8);
             }
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                if (I < J) continue;
-                f32x4 kk = {0, 0, 0, 0}, qk = {0, 0, 0, 0};
+            for (int d = 0; d < 4; ++d) {
+                f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-                for (int kc = 0; kc < 4; ++kc) {
-                    kk = O::mma(kk, kj[kc], O::rowk_perm(sK + gbrow(16 * I + q) + (32 * kc + 4 * g) * 2));
-                    qk = O::mma(qk, kj[kc], O::rowk_perm(sQ + (16 * I + q) * kPC + (32 * kc + 4 * g) * 2));
-                }
-                // lane (g, q): i = 16 I + q, j = 16 J + 4 g + r
-                const int i = 16 * I + q;
-                const float bi = tBeta[i];
-                float fa[4], fq[4];
-                if (I == J) {
-                    const float si = tG[i];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int jr = 4 * g + r;
-                        const float f = jr <= q ? fast_exp2(si - sj[r]) : 0.0f;
-                        fq[r] = qk[r] * f;
-                        fa[r] = jr < q ? bi * kk[r] * f : 0.0f;
-                    }
-                } else {
-                    const float rowf = tVf[i] * tP[4 * J + (I - J)];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float f = rowf * bfj[r];
-                        fq[r] = qk[r] * f;
-                        fa[r] = bi * kk[r] * f;
-                    }
-                }
-                float *ar = fA + i * kPF + 16 * J + 4 * g;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) ar[r] = fa[r];
-                O::mstore4(sMq + i * kMPB + (16 * J + 4 * g) * 2, fq);
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks <= d / 2) acc = O::mma(acc, kt[ks], O::mrow(sT + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2));
+                // acc[r] = W[token 16 d + q][key 16 u + 4 g + r]
+                *reinterpret_cast<u32x2 *>(sW + rt_row(16 * d + q) + rt_col(16 * u + 4 * g)) =
+                    u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
             }
         }
-        lds_barrier();
-
-        // ---- T = (I + A)^-1: diagonal blocks by forward substitution (wave w: block w,
-        //      lane j < 16 owns column j): T[i][j] = [i == j] - sum_{j <= m < i} A[i][m] T[m][j]
-        {
-            const int base = 16 * wave;
-            if (lane < 16) {
-                float tc[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float acc = i == lane ? 1.0f : 0.0f;
-#pragma unroll
-                    for (int m = 0; m < i; ++m) acc -= fA[(base + i) * kPF + base + m] * tc[m];
-                    tc[i] = i < lane ? 0.0f : acc;
-                }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) fT[(base + i) * kPF + base + lane] = tc[i];
-            }
-        }
-        lds_barrier();
-        // blocks below the diagonal, by distance from it (wave w: block (w + dist, w)):
-        //   T_IJ = -T_II X,  X = sum_{J <= K < I} A_IK T_KJ   (16 x 16 float32 products on the
-        //   VALU; lane: row lane / 4, columns 4 (lane mod 4) ..), X staged through the unused
-        //   strictly-upper part of A (row block J, column block I)
-#pragma unroll
-        for (int dist = 1; dist < 4; ++dist) {
-            if (wave + dist < 4) {
-                const int J = wave, I = wave + dist;
-                const int r = lane >> 2, c4 = 4 * (lane & 3);
-                float x[4] = {0, 0, 0, 0};
-                for (int K = J; K < I; ++K)
-                    for (int m = 0; m < 16; ++m) {
-                        const float aim = fA[(16 * I + r) * kPF + 16 * K + m];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] = fmaf(aim, fT[(16 * K + m) * kPF + 16 * J + c4 + e], x[e]);
-                    }
-                float *xs = fA + (16 * J + r) * kPF + 16 * I + c4;   // row block J, column block I: unused by A
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xs[e] = x[e];
-                __builtin_amdgcn_wave_barrier();
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                float t4[4] = {0, 0, 0, 0};
-                for (int m = 0; m < 16; ++m) {
-                    const float tim = fT[(16 * I + r) * kPF + 16 * I + m];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) t4[e] = fmaf(tim, fA[(16 * J + m) * kPF + 16 * I + c4 + e], t4[e]);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) fT[(16 * I + r) * kPF + 16 * J + c4 + e] = -t4[e];
-            }
-            lds_barrier();
-        }
-        // T (lower, unit diagonal) -> bf16 tile: the 10 lower sub-tiles
-        for (int idx = tid; idx < 10 * 64; idx += 256) {
-            static constexpr int kI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3}, kJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-            const int sub = idx >> 6, e = idx & 63, r = e >> 2, c4 = 4 * (e & 3);
-            const int I = kI[sub], J = kJ[sub], i = 16 * I + r;
-            float v4[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int j = 16 * J + c4 + x;
-                v4[x] = j <= i ? fT[i * kPF + j] : 0.0f;
-            }
-            O::mstore4(sT + i * kMPB + (16 * J + c4) * 2, v4);
-        }
-        lds_barrier();
-
-        // ---- W^T = (beta gamma K)^T T^T: wave w computes key rows 32 w .. 32 w + 31 (u = 2 w, 2 w + 1)
-        {
-#pragma unroll
-            for (int uu = 0; uu < 2; ++uu) {
-                const int u = 2 * wave + uu;
-                Frag kt[2];   // (beta gamma K)^T fragments: key column 16 u + q, tokens 32 ks + 8 g + slot
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const Frag raw = O::tr(sK + gbrow(32 * ks + 8 * g) + O::tr_row(q) * kPB + (16 * u + O::tr_col(q)) * 2,
-                                           4 * kPB);
-                    float w8[8];
-#pragma unroll
-                    for (int sl = 0; sl < 8; ++sl) w8[sl] = tBG[32 * ks + 8 * g + sl];
-                    kt[ks] = O::scale(raw, w8);
-                }
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks)
-                        if (ks <= d / 2) acc = O::mma(acc, kt[ks], O::mrow(sT + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2));
-                    // acc[r] = W[token 16 d + q][key 16 u + 4 g + r]
-                    const float w4[4] = {acc[0], acc[1], acc[2], acc[3]};
-                    O::mstore4(sW + (16 * d + q) * kPC + (16 * u + 4 * g) * 2, w4);
-                }
-            }
-        }
-        lds_barrier();
-
-        // ---- U^T = (beta V)^T T^T - H0^T W^T (this wave's 16 value columns) -> U tile
+        // this wave's (beta V)^T T^T and H0^T Q^T (tokens 16 d + q, columns 16 w + 4 g + r)
         Frag hf[4];   // H0^T = S0 rows as operands: k step c covers keys 32 c .. + 31 (permuted order)
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) hf[kc] = O::from_f32(st[2 * kc], st[2 * kc + 1]);
+        f32x4 u1[4], o1[4];
         {
             Frag vf[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const Frag raw = O::tr(sV + (32 * ks + 8 * g + O::tr_row(q)) * kPX + (16 * wave + O::tr_col(q)) * 2, 4 * kPX);
-                float w8[8];
-#pragma unroll
-                for (int sl = 0; sl < 8; ++sl) w8[sl] = tBeta[32 * ks + 8 * g + sl];
-                vf[ks] = O::scale(raw, w8);
+                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(tBeta + 32 * ks + 8 * g);
+                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(tBeta + 32 * ks + 8 * g + 4);
+                const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+                vf[ks] = O::scale(O::tr(sV + (32 * ks + 8 * g + O::tr_row(q)) * kPX + (16 * wave + O::tr_col(q)) * 2,
+                                        4 * kPX), w8);
             }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                f32x4 u1 = {0, 0, 0, 0}, u2 = {0, 0, 0, 0};
+                u1[d] = f32x4{0, 0, 0, 0};
+                o1[d] = f32x4{0, 0, 0, 0};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= d / 2) u1 = O::mma(u1, vf[ks], O::mrow(sT + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2));
+                    if (ks <= d / 2) u1[d] = O::mma(u1[d], vf[ks], O::mrow(sT + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2));
 #pragma unroll
-                for (int kc = 0; kc < 4; ++kc)
-                    u2 = O::mma(u2, hf[kc], O::rowk_perm(sW + (16 * d + q) * kPC + (32 * kc + 4 * g) * 2));
-                // (u1 - u2)[r] = U[token 16 d + q][value column 16 w + 4 g + r]
-                const float uv[4] = {u1[0] - u2[0], u1[1] - u2[1], u1[2] - u2[2], u1[3] - u2[3]};
-                *(uint2 *)(sU + (16 * d + q) * kPX + (16 * wave + 4 * g) * 2) =
-                    uint2{pack_bf16(uv[0], uv[1]), pack_bf16(uv[2], uv[3])};
+                for (int kc = 0; kc < 4; ++kc) o1[d] = O::mma(o1[d], hf[kc], rt_frag(sQ, 16 * d + q, kc, g));
             }
         }
         lds_barrier();
 
-        // ---- O^T = scale ((H0^T Q^T) diag(gamma) + U^T Mq^T); then the state update
-        //      H = gamma_last H + K^T (rho o U)
+        // ---- (2) U^T = (beta V)^T T^T - H0^T W^T -> this wave's columns of the U tile
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            f32x4 u2 = {0, 0, 0, 0};
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) u2 = O::mma(u2, hf[kc], rt_frag(sW, 16 * d + q, kc, g));
+            const f32x4 uv = u1[d] - u2;   // U[token 16 d + q][value column 16 w + 4 g + r]
+            *reinterpret_cast<u32x2 *>(sU + (16 * d + q) * kPX + (16 * wave + 4 * g) * 2) =
+                u32x2{pack_bf16(uv[0], uv[1]), pack_bf16(uv[2], uv[3])};
+        }
+        // the U columns are this wave's own: its LDS writes complete before the transposed reads
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         {
             Frag uf[2];   // U^T fragments: value column 16 w + q, tokens 32 ks + 8 g + slot
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 uf[ks] = O::tr(sU + (32 * ks + 8 * g + O::tr_row(q)) * kPX + (16 * wave + O::tr_col(q)) * 2, 4 * kPX);
+            const __amdgpu_buffer_rsrc_t ro = rsrc(a.o + (t0 * H + h) * DV + vw, (int64_t)(Lc - 1) * vrow + 32);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                f32x4 o1 = {0, 0, 0, 0}, o2 = {0, 0, 0, 0};
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc)
-                    o1 = O::mma(o1, hf[kc], O::rowk_perm(sQ + (16 * d + q) * kPC + (32 * kc + 4 * g) * 2));
+                f32x4 o2 = {0, 0, 0, 0};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
                     if (ks <= d / 2) o2 = O::mma(o2, uf[ks], O::mrow(sMq + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2));
                 const int i = 16 * d + q;
                 const float gi = tGam[i];
-                if (i < Lc) {
-                    uint16_t *dst = a.o + ((t0 + i) * H + h) * DV + vw + 4 * g;
-                    *(uint2 *)dst = uint2{pack_bf16(scale * fmaf(o1[0], gi, o2[0]), scale * fmaf(o1[1], gi, o2[1])),
-                                          pack_bf16(scale * fmaf(o1[2], gi, o2[2]), scale * fmaf(o1[3], gi, o2[3]))};
-                }
+                // rows past the chunk fall outside the buffer range and are dropped
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{pack_bf16(scale * fmaf(o1[d][0], gi, o2[0]), scale * fmaf(o1[d][1], gi, o2[1])),
+                          pack_bf16(scale * fmaf(o1[d][2], gi, o2[2]), scale * fmaf(o1[d][3], gi, o2[3]))},
+                    ro, i * vrow + 8 * g, 0, 0);
             }
             // state update: st[u] (key rows 16 u + 4 g + r, value column q) = gamma_last st[u] + sum_ks Kt[u] (rho U)
             Frag ru[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                float w8[8];
-#pragma unroll
-                for (int sl = 0; sl < 8; ++sl) w8[sl] = tRho[32 * ks + 8 * g + sl];
+                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 8 * g);
+                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 8 * g + 4);
+                const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
                 ru[ks] = O::scale(uf[ks], w8);
             }
             const float gl = tGam[63];
@@ -392,10 +529,7 @@ void ssd_gdn_chunk_kernel(GdnArgs a)
             for (int u = 0; u < 8; ++u) {
                 st[u] *= gl;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    st[u] = O::mma(st[u],
-                                   O::tr(sK + gbrow(32 * ks + 8 * g) + O::tr_row(q) * kPB + (16 * u + O::tr_col(q)) * 2, 4 * kPB),
-                                   ru[ks]);
+                for (int ks = 0; ks < 2; ++ks) st[u] = O::mma(st[u], rt_tr(sK, 32 * ks + 8 * g, 16 * u, q), ru[ks]);
             }
         }
         // the state after the chunk into its checkpoint slot
@@ -412,7 +546,13 @@ void ssd_gdn_chunk_kernel(GdnArgs a)
                 for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u + 4 * g) = st[u];
             }
         }
-        lds_barrier();   // the chunk's tiles are consumed before the next chunk's loads
+
+        // ---- (3) the next chunk's tiles and tables
+        if (c + 1 < nch) {
+            lds_barrier();   // every wave is done with this chunk's tiles
+            stage_store();
+            lds_barrier();
+        }
     }
 
     float *fd = a.final_states + ((int64_t)(s * H + h) * DV + vw + q) * DK;
@@ -422,9 +562,15 @@ void ssd_gdn_chunk_kernel(GdnArgs a)
 #endif
 
 hipError_t launch_gdn(const GdnArgs &a, hipStream_t stream) {
+    const int64_t prep = (int64_t)a.max_chunks * a.H;
+    if (prep > 0 && a.T > 0) {
+        hipLaunchKernelGGL(ssd_gdn_prep_kernel, dim3((unsigned)prep), dim3(256), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int64_t blocks = (int64_t)a.S * a.H * a.nptiles;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(ssd_gdn_chunk_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(ssd_gdn_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

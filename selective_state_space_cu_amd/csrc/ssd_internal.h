@@ -100,6 +100,7 @@ hipError_t launch_conv1d(const Conv1dArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, int dstate, hipStream_t stream);
 
 // Chunked gated delta rule (see ssd_gdn.hip).
+constexpr int kGdnWsBytes = 64 * 64 * 2;   // workspace per (chunk, value head): T (64 x 64 bf16)
 struct GdnArgs {
     const uint16_t *q, *k, *v;          // (T,G,dk), (T,G,dk), (T,H,dv) bf16
     const float *gate, *beta;           // (T,H)
@@ -109,7 +110,8 @@ struct GdnArgs {
     float *final_states;                // (S,H,dv,dk)
     float *chunk_states;                // checkpoint cache or null
     const int32_t *chunk_state_dst;     // slot per chunk or null (-> chunk index)
-    const int32_t *cu_seqlens, *seq_chunk_start, *seq_order;
+    uint16_t *workspace;                // (max_chunks, H, 64, 64) bf16
+    const int32_t *cu_seqlens, *seq_chunk_start, *seq_order, *chunk_offsets, *chunk_seq_idx;
     int32_t *error_flag;
     float scale;
     int32_t T, S, H, G, dv, max_chunks, capacity, nptiles;

@@ -142,6 +142,11 @@ def test_gdn_argument_checks():
     small = torch.zeros((1, 2, 64, 128), device="cuda")
     with pytest.raises(ssd.SSDError, match="capacity"):
         ssd.gated_delta_chunk_varlen(d["q"], d["k"], d["v"], d["gate"], d["beta"], meta, chunk_states=small)
+    need = ssd.gated_delta_workspace_size(meta, 2)
+    assert need == meta.max_chunks * 2 * 64 * 64 * 2
+    ws = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ssd.SSDError, match="capacity"):
+        ssd.gated_delta_chunk_varlen(d["q"], d["k"], d["v"], d["gate"], d["beta"], meta, workspace=ws)
     torch.cuda.synchronize()
 
 
