@@ -27,10 +27,11 @@
 //    written to the workspace as bf16 (64 x 64 per chunk and head). T depends
 //    on neither the state nor the values, so no chunk waits for another here.
 //  ssd_gdn_scan_kernel, one workgroup per (sequence, value head, 64 value
-//    columns), walks the chunks in order with the state in registers; per chunk
-//    only matrix-core products: W, T beta V, Q H0, the causal Q K^T (masked), then
-//    U = T beta V - W H0, O and the state update. The next chunk's K, Q, V and T
-//    are loaded into registers while the current chunk computes.
+//    columns), walks the chunks in order with the state in registers, split by
+//    keys over two waves per SIMD; per chunk only matrix-core products: W,
+//    T beta V, Q H0, the causal Q K^T (masked), then U = T beta V - W H0, O and
+//    the state update. The next chunk's K, Q, V and T are loaded into registers
+//    while the current chunk computes.
 #include <hip/hip_runtime.h>
 
 #include "ssd_scan.hpp"
@@ -81,6 +82,8 @@ static_assert(kGdnWsBytes == kGdnChunk * kGdnChunk * 2, "workspace: one bf16 T p
     *reinterpret_cast<u32x2 *>(row + rt_col(8 * cpos)) = u32x2{v[0], v[1]};
     *reinterpret_cast<u32x2 *>(row + rt_col(8 * cpos + 4)) = u32x2{v[2], v[3]};
 }
+// compiler fence: LDS reads issued above it stay above (batched ahead of their products)
+[[maybe_unused]] __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 [[maybe_unused]] __device__ __forceinline__ int tri_blk(int I, int J) { return (I * (I + 1) / 2 + J) * kBlk; }
 
 [[maybe_unused]] __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -281,18 +284,24 @@ __global__ __launch_bounds__(256) void ssd_gdn_prep_kernel(GdnArgs a)
 // The chunk walk of one (sequence, value head, 64 value columns)
 // ---------------------------------------------------------------------------
 //
-// Four waves, one per SIMD: wave w owns value columns 16 w .. 16 w + 15 of the
-// slice and carries their state rows S[v][0..dk) (float32, in the accumulator
-// layout of the state update: register u, element r = S[16 w + q][16 u + 4 g + r]
-// for lane (g, q)) from chunk to chunk. Per chunk:
-//   (1) Mq = (e^(G_i - G_j) q_i . k_j)_{j <= i} (bf16, sub-tiles over the waves),
-//       W^T = (beta gamma K)^T T^T (wave w: keys 32 w ..), and in registers this
-//       wave's (beta V)^T T^T and H0^T Q^T; the next chunk's loads in flight;
-//   (2) U^T = (beta V)^T T^T - H0^T W^T -> this wave's columns of the U tile;
-//       O^T = scale ((H0^T Q^T) diag(gamma) + U^T Mq^T); H = gamma_last H + K^T (rho U),
-//       rho_j = e^(G_last - G_j); the state after the chunk to its checkpoint slot;
+// Eight waves, two per SIMD: wave w = (vb, kh), vb = w mod 4, kh = w / 4, owns
+// value columns 16 vb .. 16 vb + 15 of the slice and keys 64 kh .. 64 kh + 63
+// of their state rows (float32, in the accumulator layout of the state update:
+// st[u][r] = S[16 vb + q][64 kh + 16 u + 4 g + r] for lane (g, q)), carried
+// from chunk to chunk. Per chunk:
+//   (1) Mq = (e^(G_i - G_j) q_i . k_j)_{j <= i} (bf16 sub-tiles over the waves),
+//       W (wave w: keys 16 w ..), and in registers the wave's share of
+//       T beta V and its key half of Q H0; the next chunk's loads in flight;
+//   (2) its key half of W H0; the two halves of U = T beta V - W H0 and of
+//       Q H0 are added through LDS; U stays in registers in the accumulator
+//       layout (token 16 d + 4 g + r, column q), which is the operand layout of
+//       both remaining products once their other operand is read in the same
+//       token order (32 ks + 4 g + r, then 32 ks + 16 + 4 g + r):
+//       O = scale (diag(gamma) Q H0 + Mq U) for the wave's half of the rows,
+//       H = gamma_last H + K^T (rho U) for its key half; the state after the
+//       chunk to its checkpoint slot;
 //   (3) the next chunk's tiles into LDS and its tables.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ssd_gdn_scan_kernel(GdnArgs a)
 #if !defined(__HIP_DEVICE_COMPILE__)
 {
@@ -307,9 +316,12 @@ void ssd_gdn_scan_kernel(GdnArgs a)
     __shared__ __align__(16) unsigned char sQ[kTileR];
     __shared__ __align__(16) unsigned char sW[kTileR];
     __shared__ __align__(16) unsigned char sV[kTileV];
-    __shared__ __align__(16) unsigned char sU[kTileV];
     __shared__ __align__(16) unsigned char sT[kTileM];
     __shared__ __align__(16) unsigned char sMq[kTileM];
+    // exchange between the two key halves: U partials (4 row blocks) and Q H0
+    // partials (the 2 row blocks the partner outputs), 16 bytes per lane each
+    __shared__ __align__(16) f32x4 xU[8 * 4 * 64];
+    __shared__ __align__(16) f32x4 xO[8 * 2 * 64];
     // tables of the chunk: G (log2), gamma, beta, beta gamma, rho (64 each)
     __shared__ __align__(16) float tab[5 * 64];
     float *const tG = tab, *const tGam = tab + 64, *const tBeta = tab + 128, *const tBG = tab + 192,
@@ -317,6 +329,7 @@ void ssd_gdn_scan_kernel(GdnArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int vb = wave & 3, kh = wave >> 2;
     const int q = lane & 15, g = lane >> 4;
 
     if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
@@ -335,61 +348,73 @@ void ssd_gdn_scan_kernel(GdnArgs a)
     const int nch = (L + CH - 1) / CH;
     const int c0 = a.seq_chunk_start[s];
     const int v0 = pt * kGdnCols;              // first value column of the workgroup
-    const int vw = v0 + 16 * wave;             // first value column of this wave
+    const int vw = v0 + 16 * vb;               // first value column of this wave
+    const int k0 = 64 * kh;                    // first key of this wave
 
-    // state rows of this wave's 16 columns: st[u][r] = S[vw + q][16 u + 4 g + r]
-    f32x4 st[8];
+    // st[u][r] = S[vw + q][k0 + 16 u + 4 g + r]
+    f32x4 st[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) st[u] = f32x4{0, 0, 0, 0};
+    for (int u = 0; u < 4; ++u) st[u] = f32x4{0, 0, 0, 0};
     if (a.init != nullptr && (a.has_init == nullptr || a.has_init[s] != 0)) {
-        const float *src = a.init + ((int64_t)(s * H + h) * DV + vw + q) * DK;
+        const float *src = a.init + ((int64_t)(s * H + h) * DV + vw + q) * DK + k0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) st[u] = *reinterpret_cast<const f32x4 *>(src + 16 * u + 4 * g);
+        for (int u = 0; u < 4; ++u) st[u] = *reinterpret_cast<const f32x4 *>(src + 16 * u + 4 * g);
     }
 
     // the strictly-upper sub-tiles that the causal products read (row block 0 x
     // column block 1, row block 2 x column block 3) stay zero in Mq
-    {
+    if (tid < 256) {
         const int t2 = tid & 127, r = t2 >> 3, part = t2 & 7;   // 16 rows x 8 pieces of 4 bytes per sub-tile
         const int I = (tid >> 7) ? 2 : 0, row = 16 * I + r, col = 16 * (I + 1) + 2 * part;
         *reinterpret_cast<uint32_t *>(sMq + row * kMPB + col * 2) = 0u;
     }
 
     // ---- staging of one chunk: global loads into registers, then LDS
-    u32x4 rk[4], rq[4], rv[2], rt[2];
+    u32x4 rk[2], rq[2], rv, rt;
     float rgate = 0.0f, rbeta = 0.0f;
-    const int vrow = H * DV * 2;
+    int next_dst = -1;
+    const int vrow = H * DV * 2, krow = G * DK * 2;
+    // (issued in two parts, so that the issue of the loads is spread over the chunk's work)
     auto stage_load = [&](int c) {
         const int64_t t0 = tb + (int64_t)c * CH;
         const int Lc = min(CH, L - c * CH);
-        load_rows(rk, a.k, t0, Lc, G, grp, tid);
-        load_rows(rq, a.q, t0, Lc, G, grp, tid);
-        const __amdgpu_buffer_rsrc_t r = rsrc(a.v + (t0 * H + h) * DV + v0, (int64_t)(Lc - 1) * vrow + 128);
-        const uint16_t *tsrc = a.workspace + ((int64_t)(c0 + c) * H + h) * (CH * CH);
+        const __amdgpu_buffer_rsrc_t rK = rsrc(a.k + (t0 * G + grp) * DK, (int64_t)(Lc - 1) * krow + 256);
+        const __amdgpu_buffer_rsrc_t rQ = rsrc(a.q + (t0 * G + grp) * DK, (int64_t)(Lc - 1) * krow + 256);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int piece = tid + 256 * i;
-            rv[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (piece >> 3) * vrow + 16 * (piece & 7), 0, 0);
-            rt[i] = *reinterpret_cast<const u32x4 *>(tsrc + 8 * piece);
+            const int piece = tid + 512 * i, off = (piece >> 4) * krow + 16 * (piece & 15);
+            rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0);
+            rq[i] = __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, 0);
         }
+    };
+    auto stage_load2 = [&](int c) {
+        const int64_t t0 = tb + (int64_t)c * CH;
+        const int Lc = min(CH, L - c * CH);
+        const __amdgpu_buffer_rsrc_t rV = rsrc(a.v + (t0 * H + h) * DV + v0, (int64_t)(Lc - 1) * vrow + 128);
+        rv = __builtin_amdgcn_raw_buffer_load_b128(rV, (tid >> 3) * vrow + 16 * (tid & 7), 0, 0);
+        rt = *reinterpret_cast<const u32x4 *>(a.workspace + ((int64_t)(c0 + c) * H + h) * (CH * CH) + 8 * tid);
         if (wave == 0) {
             rgate = load_token(a.gate, t0, Lc, H, h, lane);
             rbeta = load_token(a.beta, t0, Lc, H, h, lane);
         }
+        // checkpoint slot of the chunk (-1: none), kept in a vector register until
+        // it is used so that nothing waits for this load before then
+        const int gc = c0 + c;
+        next_dst = -1;
+        if (a.chunk_states != nullptr && gc >= 0 && gc < a.max_chunks)
+            next_dst = a.chunk_state_dst
+                           ? (int)__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.chunk_state_dst + gc, 4), 0, 0, 0)
+                           : gc;
     };
     auto stage_store = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int piece = tid + 256 * i;
+        for (int i = 0; i < 2; ++i) {
+            const int piece = tid + 512 * i;
             rt_store(sK, piece >> 4, piece & 15, rk[i]);
             rt_store(sQ, piece >> 4, piece & 15, rq[i]);
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int piece = tid + 256 * i, r = piece >> 3, cpos = piece & 7;
-            *reinterpret_cast<u32x4 *>(sV + r * kPX + 16 * cpos) = rv[i];
-            *reinterpret_cast<u32x4 *>(sT + r * kMPB + 16 * cpos) = rt[i];
-        }
+        *reinterpret_cast<u32x4 *>(sV + (tid >> 3) * kPX + 16 * (tid & 7)) = rv;
+        *reinterpret_cast<u32x4 *>(sT + (tid >> 3) * kMPB + 16 * (tid & 7)) = rt;
         if (wave == 0) {   // tables (lane j = token j; neutral past the end)
             const float v = wave_scan(rgate * kLog2e);   // inclusive cumsum (log2)
             const float gam = fast_exp2(v);
@@ -401,9 +426,12 @@ void ssd_gdn_scan_kernel(GdnArgs a)
         }
     };
 
+    int cur_dst = -1;
     if (nch > 0) {
         stage_load(0);
+        stage_load2(0);
         stage_store();
+        cur_dst = next_dst;
     }
     lds_barrier();
 
@@ -413,16 +441,27 @@ void ssd_gdn_scan_kernel(GdnArgs a)
         const int Lc = min(CH, L - c * CH);
         if (c + 1 < nch) stage_load(c + 1);
 
-        // ---- (1) Mq sub-tiles: lane (g, q): i = 16 I + q, j = 16 J + 4 g + r
+        // ---- (1) Mq sub-tiles (I, J), I >= J, ten over the eight waves (waves 0 and 1 take two);
+        //      lane (g, q): i = 16 I + q, j = 16 J + 4 g + r. Fragments are read in batches
+        //      ahead of their products (the fences keep the reads together).
 #pragma unroll
-        for (int n = 0; n < 3; ++n) {
-            const int code = sub_tile(wave, n), I = code >> 4, J = code & 15;
-            f32x4 qk = {0, 0, 0, 0};
+        for (int n = 0; n < 2; ++n) {
+            if (n == 1 && wave >= 2) break;
+            const int code = n == 0 ? (int)((0x3130222120111000ull >> (8 * wave)) & 0xff) : 0x32 + wave;
+            const int I = code >> 4, J = code & 15;
+            Frag kf[4], qf[4];
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) qk = O::mma(qk, rt_frag(sK, 16 * J + q, kc, g), rt_frag(sQ, 16 * I + q, kc, g));
+            for (int kc = 0; kc < 4; ++kc) {
+                kf[kc] = rt_frag(sK, 16 * J + q, kc, g);
+                qf[kc] = rt_frag(sQ, 16 * I + q, kc, g);
+            }
             const int i = 16 * I + q;
             const float gi = tG[i];
             const f32x4 gj = *reinterpret_cast<const f32x4 *>(tG + 16 * J + 4 * g);
+            lds_fence();
+            f32x4 qk = {0, 0, 0, 0};
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) qk = O::mma(qk, kf[kc], qf[kc]);
             float fq[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -431,119 +470,161 @@ void ssd_gdn_scan_kernel(GdnArgs a)
             }
             O::mstore4(sMq + i * kMPB + (16 * J + 4 * g) * 2, fq);
         }
-        // W^T = (beta gamma K)^T T^T: wave w computes key rows 32 w .. 32 w + 31 (u = 2 w, 2 w + 1)
+        // W = T diag(beta gamma) K, keys 16 w .. 16 w + 15 (from W^T = (beta gamma K)^T T^T), this
+        // wave's key half of Q H0 (token 16 d + q, column 4 g + r) and its two row blocks of
+        // T beta V (token 16 d + 4 g + r, column q): d = 0, 3 for kh = 0 and d = 1, 2 for kh = 1,
+        // which balances the causal products between the halves
+        Frag hf[2];   // H0 fragments of this wave's key half: k step kc covers keys k0 + 32 kc .. (permuted)
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-            const int u = 2 * wave + uu;
-            Frag kt[2];   // (beta gamma K)^T fragments: key column 16 u + q, tokens 32 ks + 8 g + slot
+        for (int kc = 0; kc < 2; ++kc) hf[kc] = O::from_f32(st[2 * kc], st[2 * kc + 1]);
+        f32x4 o1[4], u1[2];
+        {
+            Frag kt[2], vf[2], tf[4][2], qf[4][2];
+            f32x4 bg[2][2], be[2][2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 8 * g);
-                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 8 * g + 4);
-                const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-                kt[ks] = O::scale(rt_tr(sK, 32 * ks + 8 * g, 16 * u, q), w8);
+                kt[ks] = rt_tr(sK, 32 * ks + 8 * g, 16 * wave, q);
+                vf[ks] = O::tr(sV + (32 * ks + 8 * g + O::tr_row(q)) * kPX + (16 * vb + O::tr_col(q)) * 2, 4 * kPX);
+                bg[ks][0] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 8 * g);
+                bg[ks][1] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 8 * g + 4);
+                be[ks][0] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * ks + 8 * g);
+                be[ks][1] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * ks + 8 * g + 4);
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    tf[d][ks] = O::mrow(sT + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2);
+                    qf[d][ks] = rt_frag(sQ, 16 * d + q, 2 * kh + ks, g);
+                }
+            lds_fence();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const float wb[8] = {bg[ks][0][0], bg[ks][0][1], bg[ks][0][2], bg[ks][0][3],
+                                     bg[ks][1][0], bg[ks][1][1], bg[ks][1][2], bg[ks][1][3]};
+                const float wv[8] = {be[ks][0][0], be[ks][0][1], be[ks][0][2], be[ks][0][3],
+                                     be[ks][1][0], be[ks][1][1], be[ks][1][2], be[ks][1][3]};
+                kt[ks] = O::scale(kt[ks], wb);   // (beta gamma K)^T: key column 16 w + q, tokens 32 ks + 8 g + slot
+                vf[ks] = O::scale(vf[ks], wv);   // (beta V): tokens 32 ks + 8 g + slot, value column 16 vb + q
             }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= d / 2) acc = O::mma(acc, kt[ks], O::mrow(sT + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2));
-                // acc[r] = W[token 16 d + q][key 16 u + 4 g + r]
-                *reinterpret_cast<u32x2 *>(sW + rt_row(16 * d + q) + rt_col(16 * u + 4 * g)) =
+                    if (ks <= d / 2) acc = O::mma(acc, kt[ks], tf[d][ks]);
+                // acc[r] = W[token 16 d + q][key 16 w + 4 g + r]
+                *reinterpret_cast<u32x2 *>(sW + rt_row(16 * d + q) + rt_col(16 * wave + 4 * g)) =
                     u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
-            }
-        }
-        // this wave's (beta V)^T T^T and H0^T Q^T (tokens 16 d + q, columns 16 w + 4 g + r)
-        Frag hf[4];   // H0^T = S0 rows as operands: k step c covers keys 32 c .. + 31 (permuted order)
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) hf[kc] = O::from_f32(st[2 * kc], st[2 * kc + 1]);
-        f32x4 u1[4], o1[4];
-        {
-            Frag vf[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(tBeta + 32 * ks + 8 * g);
-                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(tBeta + 32 * ks + 8 * g + 4);
-                const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-                vf[ks] = O::scale(O::tr(sV + (32 * ks + 8 * g + O::tr_row(q)) * kPX + (16 * wave + O::tr_col(q)) * 2,
-                                        4 * kPX), w8);
-            }
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                u1[d] = f32x4{0, 0, 0, 0};
                 o1[d] = f32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= d / 2) u1[d] = O::mma(u1[d], vf[ks], O::mrow(sT + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2));
+                for (int kc = 0; kc < 2; ++kc) o1[d] = O::mma(o1[d], hf[kc], qf[d][kc]);
+            }
+            // (register arrays are indexed by compile-time values only: the row blocks of
+            // this key half, d = 0, 3 (kh 0) or 1, 2 (kh 1), are selected, not indexed)
 #pragma unroll
-                for (int kc = 0; kc < 4; ++kc) o1[d] = O::mma(o1[d], hf[kc], rt_frag(sQ, 16 * d + q, kc, g));
+            for (int dd = 0; dd < 2; ++dd) {
+                u1[dd] = f32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks == 0 || dd == 1)
+                        u1[dd] = O::mma(u1[dd], kh ? tf[1 + dd][ks] : tf[3 * dd][ks], vf[ks]);
             }
         }
         lds_barrier();
+        if (c + 1 < nch) stage_load2(c + 1);
 
-        // ---- (2) U^T = (beta V)^T T^T - H0^T W^T -> this wave's columns of the U tile
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            f32x4 u2 = {0, 0, 0, 0};
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) u2 = O::mma(u2, hf[kc], rt_frag(sW, 16 * d + q, kc, g));
-            const f32x4 uv = u1[d] - u2;   // U[token 16 d + q][value column 16 w + 4 g + r]
-            *reinterpret_cast<u32x2 *>(sU + (16 * d + q) * kPX + (16 * wave + 4 * g) * 2) =
-                u32x2{pack_bf16(uv[0], uv[1]), pack_bf16(uv[2], uv[3])};
-        }
-        // the U columns are this wave's own: its LDS writes complete before the transposed reads
-        __builtin_amdgcn_wave_barrier();
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // ---- (2) this key half's share of U = T beta V - W H0 (token 16 d + 4 g + r, column q)
+        f32x4 uu[4];
         {
-            Frag uf[2];   // U^T fragments: value column 16 w + q, tokens 32 ks + 8 g + slot
+            Frag wf[4][2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                uf[ks] = O::tr(sU + (32 * ks + 8 * g + O::tr_row(q)) * kPX + (16 * wave + O::tr_col(q)) * 2, 4 * kPX);
-            const __amdgpu_buffer_rsrc_t ro = rsrc(a.o + (t0 * H + h) * DV + vw, (int64_t)(Lc - 1) * vrow + 32);
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) wf[d][kc] = rt_frag(sW, 16 * d + q, 2 * kh + kc, g);
+            lds_fence();
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
+                f32x4 u2 = {0, 0, 0, 0};
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) u2 = O::mma(u2, wf[d][kc], hf[kc]);
+                // row block d belongs to key half kh = (d == 1 || d == 2), as u1[d == 3 || d == 2]
+                uu[d] = (((d == 1 || d == 2) ? 1 : 0) == kh ? u1[(d == 2 || d == 3) ? 1 : 0] : f32x4{0, 0, 0, 0}) - u2;
+                xU[(wave * 4 + d) * 64 + lane] = uu[d];
+            }
+        }
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd) xO[(wave * 2 + dd) * 64 + lane] = kh ? o1[3 * dd] : o1[1 + dd];
+        lds_barrier();
+        const int partner = wave ^ 4;
+        {
+            // fragments of the remaining products, read in the token order of the U fragments
+            // (32 ks + 4 g + r in slots 0-3, 32 ks + 16 + 4 g + r in slots 4-7)
+            Frag mf[2][2], ktr[4][2];
+            f32x4 xu[4], xo[2], r0[2], r1[2];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) xu[d] = xU[(partner * 4 + d) * 64 + lane];
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+                xo[dd] = xO[(partner * 2 + dd) * 64 + lane];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    mf[dd][ks] = O::rowk_perm(sMq + (16 * (kh ? 1 + dd : 3 * dd) + q) * kMPB + (32 * ks + 4 * g) * 2);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                r0[ks] = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 4 * g);
+                r1[ks] = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 16 + 4 * g);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    ktr[u][ks] = O::tr(sK + rt_row(32 * ks + 4 * g) + O::tr_row(q) * kPB + rt_col(k0 + 16 * u + O::tr_col(q)),
+                                       2 * kGB);
+            }
+            const f32x4 gam = {tGam[16 * (kh ? 1 : 0) + q], tGam[16 * (kh ? 2 : 3) + q], 0.0f, 0.0f};
+            const float gl = tGam[63];
+            lds_fence();
+#pragma unroll
+            for (int d = 0; d < 4; ++d) uu[d] += xu[d];
+            Frag uf[2], ru[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uf[ks] = O::from_f32(uu[2 * ks], uu[2 * ks + 1]);
+                ru[ks] = O::from_f32(uu[2 * ks] * r0[ks], uu[2 * ks + 1] * r1[ks]);
+            }
+            // O rows of this key half (d = 0, 3 or 1, 2): O[token 16 d + q][column 4 g + r]
+            const __amdgpu_buffer_rsrc_t ro = rsrc(a.o + (t0 * H + h) * DV + vw, (int64_t)(Lc - 1) * vrow + 32);
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+                const int d = kh ? 1 + dd : 3 * dd;
                 f32x4 o2 = {0, 0, 0, 0};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= d / 2) o2 = O::mma(o2, uf[ks], O::mrow(sMq + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2));
-                const int i = 16 * d + q;
-                const float gi = tGam[i];
+                    if (ks == 0 || dd == 1) o2 = O::mma(o2, uf[ks], mf[dd][ks]);
+                const f32x4 oq = (kh ? o1[1 + dd] : o1[3 * dd]) + xo[dd];
+                const float gi = gam[dd];
                 // rows past the chunk fall outside the buffer range and are dropped
                 __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{pack_bf16(scale * fmaf(o1[d][0], gi, o2[0]), scale * fmaf(o1[d][1], gi, o2[1])),
-                          pack_bf16(scale * fmaf(o1[d][2], gi, o2[2]), scale * fmaf(o1[d][3], gi, o2[3]))},
-                    ro, i * vrow + 8 * g, 0, 0);
+                    u32x2{pack_bf16(scale * fmaf(oq[0], gi, o2[0]), scale * fmaf(oq[1], gi, o2[1])),
+                          pack_bf16(scale * fmaf(oq[2], gi, o2[2]), scale * fmaf(oq[3], gi, o2[3]))},
+                    ro, (16 * d + q) * vrow + 8 * g, 0, 0);
             }
-            // state update: st[u] (key rows 16 u + 4 g + r, value column q) = gamma_last st[u] + sum_ks Kt[u] (rho U)
-            Frag ru[2];
+            // state update of this key half: st[u] = gamma_last st[u] + K^T (rho U)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 8 * g);
-                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 8 * g + 4);
-                const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-                ru[ks] = O::scale(uf[ks], w8);
-            }
-            const float gl = tGam[63];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 4; ++u) {
                 st[u] *= gl;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) st[u] = O::mma(st[u], rt_tr(sK, 32 * ks + 8 * g, 16 * u, q), ru[ks]);
+                for (int ks = 0; ks < 2; ++ks) st[u] = O::mma(st[u], ktr[u][ks], ru[ks]);
             }
         }
         // the state after the chunk into its checkpoint slot
-        if (a.chunk_states != nullptr) {
-            const int gc = c0 + c;
-            int dsl = (gc >= 0 && gc < a.max_chunks) ? (a.chunk_state_dst ? a.chunk_state_dst[gc] : gc) : -1;
-            if (dsl >= a.capacity) {
+        if (__builtin_amdgcn_readfirstlane(cur_dst) >= 0) {
+            if (__builtin_amdgcn_readfirstlane(cur_dst) >= a.capacity) {
                 if (tid == 0) atomicOr(a.error_flag, SSD_DATA_BAD_SLOT);
-                dsl = -1;
-            }
-            if (dsl >= 0) {
-                float *dst = a.chunk_states + ((int64_t)dsl * H + h) * DV * DK + (int64_t)(vw + q) * DK;
+            } else {
+                float *dst = a.chunk_states + ((int64_t)__builtin_amdgcn_readfirstlane(cur_dst) * H + h) * DV * DK +
+                             (int64_t)(vw + q) * DK + k0;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u + 4 * g) = st[u];
+                for (int u = 0; u < 4; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u + 4 * g) = st[u];
             }
         }
 
@@ -551,13 +632,14 @@ void ssd_gdn_scan_kernel(GdnArgs a)
         if (c + 1 < nch) {
             lds_barrier();   // every wave is done with this chunk's tiles
             stage_store();
+            cur_dst = next_dst;
             lds_barrier();
         }
     }
 
-    float *fd = a.final_states + ((int64_t)(s * H + h) * DV + vw + q) * DK;
+    float *fd = a.final_states + ((int64_t)(s * H + h) * DV + vw + q) * DK + k0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4 *>(fd + 16 * u + 4 * g) = st[u];
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<f32x4 *>(fd + 16 * u + 4 * g) = st[u];
 }
 #endif
 
@@ -570,7 +652,7 @@ hipError_t launch_gdn(const GdnArgs &a, hipStream_t stream) {
     }
     const int64_t blocks = (int64_t)a.S * a.H * a.nptiles;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(ssd_gdn_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(ssd_gdn_scan_kernel, dim3((unsigned)blocks), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 
