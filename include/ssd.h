@@ -308,6 +308,26 @@ ssd_status ssd_gated_delta_chunk_varlen(
  * metadata has `max_chunks` and for `nheads` value heads (0 for no chunks). */
 size_t ssd_gated_delta_workspace_size(int32_t max_chunks, int32_t nheads);
 
+/*
+ * ssd_gated_delta_chunk_varlen without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): it calls no hipMalloc, hipFree or
+ * allocating routine and uses a static 32 MiB device array of the library
+ * instead (one per GPU, held until the process ends). Same arguments, layouts
+ * and results as ssd_gated_delta_chunk_varlen.
+ * Limit: ssd_gated_delta_workspace_size(meta->max_chunks, nheads) <= 32 MiB
+ * (max_chunks * nheads <= 4096), else SSD_ERR_CAPACITY before any work.
+ * Every call on one GPU shares that array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and must not be issued. Nothing in
+ * it needs clearing between calls. The first call on a device resolves the
+ * array's address (hipGetSymbolAddress); SSD_ERR_HIP if that fails.
+ */
+ssd_status ssd_gated_delta_chunk_varlen_noalloc(
+    const void *q, const void *k, const void *v, const float *gate, const float *beta, float scale,
+    ssd_dtype in_dtype, const ssd_varlen_meta *meta, int32_t nheads, int32_t nkheads, int32_t dk, int32_t dv,
+    const float *initial_states, const int32_t *has_initial_state, void *o, float *final_states,
+    float *chunk_states, const int32_t *chunk_state_dst, int32_t chunk_states_capacity, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *ssd_status_string(ssd_status status);
 

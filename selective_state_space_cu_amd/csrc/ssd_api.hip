@@ -240,6 +240,25 @@ ssd_status ssd_gated_delta_chunk_varlen(const void *q, const void *k, const void
     return ssd::launch_gdn(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
+ssd_status ssd_gated_delta_chunk_varlen_noalloc(const void *q, const void *k, const void *v, const float *gate,
+                                                const float *beta, float scale, ssd_dtype in_dtype,
+                                                const ssd_varlen_meta *meta, int32_t nheads, int32_t nkheads,
+                                                int32_t dk, int32_t dv, const float *initial_states,
+                                                const int32_t *has_initial_state, void *o, float *final_states,
+                                                float *chunk_states, const int32_t *chunk_state_dst,
+                                                int32_t chunk_states_capacity, void *stream) {
+    const ssd_status st = check_meta(meta);
+    if (st != SSD_OK) return st;
+    const size_t need = meta->total_tokens > 0 ? ssd_gated_delta_workspace_size(meta->max_chunks, nheads) : 0;
+    if (need > ssd::kGdnScratchBytes) return SSD_ERR_CAPACITY;
+    void *ws = nullptr;
+    if (need > 0 && ssd::gdn_scratch(&ws) != hipSuccess) return SSD_ERR_HIP;
+    return ssd_gated_delta_chunk_varlen(q, k, v, gate, beta, scale, in_dtype, meta, nheads, nkheads, dk, dv,
+                                        initial_states, has_initial_state, o, final_states, chunk_states,
+                                        chunk_state_dst, chunk_states_capacity, ws, ws ? ssd::kGdnScratchBytes : 0,
+                                        stream);
+}
+
 ssd_status ssd_prefill_bites(int32_t nseqs, const int32_t *num_computed_tokens, const int32_t *prompt_len,
                              const int32_t *budget, int32_t align, int32_t *num_scheduled) {
     if (nseqs < 0 || align <= 0) return SSD_ERR_SHAPE;

@@ -34,6 +34,8 @@
 //    while the current chunk computes.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "ssd_scan.hpp"
 
 namespace ssd {
@@ -642,6 +644,30 @@ void ssd_gdn_scan_kernel(GdnArgs a)
     for (int u = 0; u < 4; ++u) *reinterpret_cast<f32x4 *>(fd + 16 * u + 4 * g) = st[u];
 }
 #endif
+
+// Workspace of the allocation-free entry point: one file-scope array, of which
+// every GPU the library runs on holds its own copy until the process ends. In
+// host code `scratch` only names the symbol; its device address (per device)
+// comes from hipGetSymbolAddress, resolved on the first call on each device.
+static __device__ __align__(256) unsigned char scratch[kGdnScratchBytes];
+
+hipError_t gdn_scratch(void **ptr) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_gdn(const GdnArgs &a, hipStream_t stream) {
     const int64_t prep = (int64_t)a.max_chunks * a.H;

@@ -117,6 +117,10 @@ struct GdnArgs {
     int32_t T, S, H, G, dv, max_chunks, capacity, nptiles;
 };
 hipError_t launch_gdn(const GdnArgs &a, hipStream_t stream);
+// The allocation-free variant's static workspace (per device) and its size.
+constexpr size_t kGdnScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t gdn_scratch(void **ptr);
 
 struct MetaArgs {
     const int32_t *cu_seqlens;

@@ -22,6 +22,7 @@ DATA_BAD_CU_SEQLENS, DATA_TOO_MANY_CHUNKS, DATA_BAD_SLOT, DATA_BAD_BLOCK = 1, 2,
 # names exported by libssd.so (checked by the CPU tests against include/ssd.h)
 EXPORTS = ("ssd_varlen_metadata", "ssd_chunk_scan_varlen", "ssd_export_chunk_states",
            "ssd_decode_step", "ssd_causal_conv1d_varlen", "ssd_gated_delta_chunk_varlen", "ssd_gated_delta_workspace_size",
+           "ssd_gated_delta_chunk_varlen_noalloc",
            "ssd_prefill_bites",
            "ssd_status_string")
 
@@ -76,6 +77,10 @@ def load_library(path: str = LIB_PATH):
     lib.ssd_gated_delta_chunk_varlen.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, st, ctypes.POINTER(_Meta),
                                                  i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp,
                                                  ctypes.c_size_t, vp]
+    lib.ssd_gated_delta_chunk_varlen_noalloc.restype = st
+    lib.ssd_gated_delta_chunk_varlen_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, st,
+                                                         ctypes.POINTER(_Meta), i32, i32, i32, i32, vp, vp, vp, vp,
+                                                         vp, vp, i32, vp]
     lib.ssd_gated_delta_workspace_size.restype = ctypes.c_size_t
     lib.ssd_gated_delta_workspace_size.argtypes = [i32, i32]
     lib.ssd_prefill_bites.restype = st
@@ -283,11 +288,14 @@ def gated_delta_chunk_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                              o: Optional[torch.Tensor] = None, final_states: Optional[torch.Tensor] = None,
                              chunk_states: Optional[torch.Tensor] = None,
                              chunk_state_dst: Optional[torch.Tensor] = None,
-                             workspace: Optional[torch.Tensor] = None):
+                             workspace: Optional[torch.Tensor] = None, no_alloc: bool = False):
     """ssd_gated_delta_chunk_varlen: q, k (T,G,dk), v (T,H,dv) bf16; gate, beta (T,H) float32;
     states (S,H,dv,dk) float32. `workspace` (uint8 on the device, at least
     gated_delta_workspace_size(meta, H) bytes) is allocated per call when not
-    given. Returns (o, final_states)."""
+    given. no_alloc=True calls ssd_gated_delta_chunk_varlen_noalloc instead (the
+    library's static workspace; pass o and final_states too for a call that
+    allocates nothing).
+    Returns (o, final_states)."""
     lib = load_library()
     device = v.device
     T, H, DV = v.shape
@@ -322,6 +330,13 @@ def gated_delta_chunk_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
         _data(chunk_states, "chunk_states", device, torch.float32)
         cap = chunk_states.shape[0]
     dst = _index(chunk_state_dst, device) if chunk_state_dst is not None else None
+    if no_alloc:
+        m = meta.c_struct()
+        _check("ssd_gated_delta_chunk_varlen_noalloc", lib.ssd_gated_delta_chunk_varlen_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), float(scale if scale is not None else DK ** -0.5),
+            _dtype_code(v), ctypes.byref(m), H, G, DK, DV, _ptr(initial_states), _ptr(has), _ptr(o),
+            _ptr(final_states), _ptr(chunk_states), _ptr(dst), cap, _stream(device)))
+        return o, final_states
     ws_bytes = gated_delta_workspace_size(meta, H)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device)
