@@ -361,8 +361,9 @@ const char *ssd_status_string(ssd_status status);
  * misaligned buffers), SSD_ERR_UNSUPPORTED (channels % 8, width outside 1..4,
  * unknown activation), SSD_ERR_DTYPE, SSD_ERR_CHUNK_SIZE / SSD_ERR_CAPACITY
  * (meta), SSD_ERR_HIP. Device data error: SSD_DATA_BAD_SLOT in
- * meta->error_flag (a slot >= num_slots; that sequence is skipped: nothing of
- * it read or written).
+ * meta->error_flag (a slot >= num_slots, or read_slot == write_slot >= 0 for a
+ * sequence of more than one chunk; that sequence is skipped: nothing of it
+ * read or written).
  */
 ssd_status ssd_causal_conv1d_varlen(
     const void *x, const float *weight, const float *bias, ssd_dtype in_dtype,

@@ -129,7 +129,11 @@ __global__ __launch_bounds__(kConvThreads) void ssd_conv1d_kernel(Conv1dArgs a) 
     }
     const int rs = a.read_slot != nullptr ? a.read_slot[s] : -1;
     const int ws = a.write_slot != nullptr ? a.write_slot[s] : -1;
-    if (rs >= a.num_slots || ws >= a.num_slots) {   // refused: nothing read or written
+    // refused (nothing of the sequence read or written): a slot past the cache, or
+    // one slot read and written by a sequence of several chunks, whose last
+    // chunk could overwrite it before the first chunk has read it
+    const bool in_place_multi = rs >= 0 && rs == ws && a.seq_chunk_start[s + 1] - a.seq_chunk_start[s] > 1;
+    if (rs >= a.num_slots || ws >= a.num_slots || in_place_multi) {
         if (ch == 0 && first) atomicOr(a.error_flag, SSD_DATA_BAD_SLOT);
         return;
     }

@@ -111,6 +111,29 @@ def test_conv1d_refuses_slot_past_the_cache():
     _compare(b, got, st, ref, st_ref, mag, "with a refused sequence")
 
 
+def test_conv1d_refuses_in_place_multi_chunk_sequence():
+    """read_slot == write_slot for a sequence of more than one chunk (its last
+    chunk could overwrite the slot before its first chunk reads it):
+    SSD_DATA_BAD_SLOT, that sequence skipped (rows and slot untouched), the
+    others computed, a single-chunk in-place sequence included."""
+    b = make_conv_inputs([70, 10, 140], 16, 4, 8, dtype="bf16", seed=80)
+    rs = b.read_slot.numpy().copy()
+    ws = b.write_slot.numpy().copy()
+    ws[0] = rs[0]   # 70 tokens = 2 chunks of 64: refused
+    ws[1] = rs[1]   # 10 tokens = 1 chunk: allowed
+    sentinel = torch.full_like(b.x, 7.0)
+    got, st, flag = _run(b, 64, rs=rs, ws=ws, out=sentinel)
+    assert flag & ssd.DATA_BAD_SLOT
+    rs_ref, ws_ref = rs.copy(), ws.copy()
+    rs_ref[0] = ws_ref[0] = -1   # the oracle leaves the refused sequence's slot alone
+    ref, st_ref, rc, mag = _ref(b, rs=rs_ref, ws=ws_ref)
+    cu = b.cu_seqlens.numpy()
+    assert torch.all(got[cu[0]:cu[1]] == 7.0), "refused sequence's rows were written"
+    ref[cu[0]:cu[1]] = 7.0
+    mag[cu[0]:cu[1]] = 0.0
+    _compare(b, got, st, ref, st_ref, mag, "with a refused in-place sequence")
+
+
 def test_conv1d_continues_through_the_cache():
     """Two calls: the second part of every sequence reads the slot the first
     part wrote; the outputs equal one call over the whole sequences."""
