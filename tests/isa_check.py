@@ -400,3 +400,23 @@ def store_data_hazards(asm_text, need=2):
                     break
             ws += int(nt.split()[1]) + 1 if nt.startswith("s_nop") else 1
     return bad, count
+
+
+def kernel_resources(asm_text):
+    """{kernel symbol: {field: value}} from the code object metadata of an assembly
+    text (private_segment_fixed_size = scratch bytes per lane, vgpr_count, ...)."""
+    out, cur = {}, None
+    meta = asm_text[asm_text.find("amdhsa.kernels:"):]
+    for line in meta.splitlines():
+        s = line.strip()
+        if s.startswith("- .") or s.startswith("-   ."):
+            cur = {}
+            s = s[1:].strip()
+        if cur is None or ":" not in s or not s.startswith("."):
+            continue
+        k, v = s[1:].split(":", 1)
+        v = v.strip()
+        cur[k] = int(v) if v.lstrip("-").isdigit() else v
+        if k == "name":
+            out[v] = cur
+    return out

@@ -4,13 +4,15 @@ after the stage's last load as its vmcnt assumes; the split-state scan's
 untracked register loads of x are never overwritten or reused before their
 wait, on any path; no direct-to-LDS load directly follows a write of M0; and no
 vector memory instruction reads an SGPR that a VALU instruction wrote fewer
-than five wait states before (inline assembly is not padded by the compiler)."""
+than five wait states before (inline assembly is not padded by the compiler);
+and no kernel spills to scratch memory (a register array indexed at run time
+lands there, and its loads then wait behind the pipelines' vector memory)."""
 import os
 import shutil
 
 import pytest
 
-from isa_check import (HIPCC, kernel_asm, m0_lds_dma_hazards, untracked_load_violations,
+from isa_check import (HIPCC, kernel_asm, kernel_resources, m0_lds_dma_hazards, untracked_load_violations,
                        store_data_hazards, valu_sgpr_vmem_hazards, vmcnt_stage_violations)
 
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None,
@@ -174,3 +176,34 @@ def test_store_data_checker_flags_a_planted_hazard():
                       "\tv_mov_b32_e32 v11, 0"])
     bad, count = store_data_hazards(text)
     assert count == 4 and [b[0] for b in bad] == [1, 3, 9]
+
+
+ALL_SOURCES = ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_decode.hip",
+               "ssd_conv1d.hip", "ssd_gdn.hip", "ssd_meta.hip"]
+
+
+# The general kernel's bf16 instances for dstate 256 on one or two waves (headdim
+# 16 or 32) hold 64 state floats per lane plus their fragments and spill
+# registers to scratch; the stage-wait check above counts those memory
+# instructions like any other. Every other kernel keeps everything in registers.
+SPILL_ALLOWED = ("_ZN3ssd15ssd_scan_kernelItLi1ELi256EEEvNS_8ScanArgsEPKi",
+                 "_ZN3ssd15ssd_scan_kernelItLi2ELi256EEEvNS_8ScanArgsEPKi")
+
+
+@pytest.mark.parametrize("src", ALL_SOURCES)
+def test_no_kernel_uses_scratch(src):
+    res = kernel_resources(kernel_asm(src))
+    assert res, f"no kernels found in {src}"
+    spill = {k: v.get("private_segment_fixed_size") for k, v in res.items()
+             if k not in SPILL_ALLOWED and
+             (v.get("private_segment_fixed_size", 0) != 0 or v.get("vgpr_spill_count", 0) != 0)}
+    assert not spill, f"kernels with scratch memory: {spill}"
+
+
+def test_scratch_check_reads_the_metadata():
+    text = "\n".join(["\t.amdgpu_metadata", "amdhsa.kernels:", "  - .agpr_count:     0",
+                      "    .name:           k1", "    .private_segment_fixed_size: 144",
+                      "    .vgpr_count:     64", "  - .agpr_count:     0", "    .name:           k2",
+                      "    .private_segment_fixed_size: 0", "    .vgpr_count:     32"])
+    res = kernel_resources(text)
+    assert res["k1"]["private_segment_fixed_size"] == 144 and res["k2"]["private_segment_fixed_size"] == 0
