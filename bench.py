@@ -608,7 +608,8 @@ def main():
     # workloads: each timed scan preceded by a write of FLUSH_MIB outside the
     # events (evicts L2 and the Infinity Cache), median / p10 / p90
     graded = {}
-    for ci in ([args.config] + [c for c in GRADED if c != args.config] if args.all_configs else [args.config]):
+    for ci in (([args.config] + [c for c in GRADED if c != args.config] if args.all_configs else [args.config])
+               if args.cold_calls > 0 else []):
         r = run if ci == args.config else PrefillRun(ci, dev)
         graded[CONFIGS[ci]["name"]] = cold_stats(r, flush, args.cold_calls)
         if r is not run:

@@ -86,6 +86,15 @@ static_assert(kGdnWsBytes == kGdnChunk * kGdnChunk * 2, "workspace: one bf16 T p
 }
 // compiler fence: LDS reads issued above it stay above (batched ahead of their products)
 [[maybe_unused]] __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
+// XCD-aware work order: workgroup b runs on XCD b mod 8, each XCD with its own
+// L2. Items that read the same key-head data (R of them per key head) are put
+// 8 apart in b, on one XCD, so that their q and k rows come from one L2; plain
+// order when the grid does not split evenly. Returns (key-head item, sharer).
+[[maybe_unused]] __device__ __forceinline__ int2 xcd_order(int b, int nblocks, int R) {
+    if (R <= 1 || nblocks % (8 * R) != 0) return int2{b / R, b % R};
+    const int r = b >> 3;
+    return int2{(r / R) * 8 + (b & 7), r % R};
+}
 [[maybe_unused]] __device__ __forceinline__ int tri_blk(int I, int J) { return (I * (I + 1) / 2 + J) * kBlk; }
 
 [[maybe_unused]] __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
@@ -157,14 +166,15 @@ __global__ __launch_bounds__(256) void ssd_gdn_prep_kernel(GdnArgs a)
 
     if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
     const int H = a.H, G = a.G;
-    const int gc = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+    // (chunk, key head) items; the value heads of one key head share its k rows
+    const int2 it = xcd_order(blockIdx.x, gridDim.x, H / G);
+    const int gc = it.x / G, grp = it.x - (it.x / G) * G, h = grp * (H / G) + it.y;
     if (gc >= a.max_chunks) return;
     const int s = a.chunk_seq_idx[gc];
     if (s < 0 || s >= a.S) return;
     const int t0 = a.chunk_offsets[gc], t1 = a.chunk_offsets[gc + 1];
     if (t0 < 0 || t1 > a.T || t1 <= t0 || t1 - t0 > CH) return;
     const int Lc = t1 - t0;
-    const int grp = h / (H / G);
 
     {
         u32x4 kv[4];
@@ -335,14 +345,14 @@ void ssd_gdn_scan_kernel(GdnArgs a)
     const int q = lane & 15, g = lane >> 4;
 
     if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
-    const int b = blockIdx.x;
-    const int per_seq = a.H * a.nptiles;
-    const int rank = b / per_seq, rem = b - rank * per_seq;
-    const int h = rem / a.nptiles, pt = rem - (rem / a.nptiles) * a.nptiles;
+    const int H = a.H, G = a.G, DV = a.dv;
+    // (sequence, key head) items; the value heads of one key head and their
+    // column slices share its q and k rows
+    const int2 it = xcd_order(blockIdx.x, gridDim.x, (H / G) * a.nptiles);
+    const int rank = it.x / G, grp = it.x - (it.x / G) * G;
+    const int h = grp * (H / G) + it.y / a.nptiles, pt = it.y - (it.y / a.nptiles) * a.nptiles;
     const int s = a.seq_order[rank];
     if (s < 0 || s >= a.S) return;
-    const int H = a.H, G = a.G, DV = a.dv;
-    const int grp = h / (H / G);
     int64_t tb = a.cu_seqlens[s], te = a.cu_seqlens[s + 1];
     tb = tb < 0 ? 0 : (tb > a.T ? a.T : tb);
     te = te < tb ? tb : (te > a.T ? a.T : te);
