@@ -372,6 +372,10 @@ void ssd_gdn_scan_kernel(GdnArgs a)
 #pragma unroll
         for (int u = 0; u < 4; ++u) st[u] = *reinterpret_cast<const f32x4 *>(src + 16 * u + 4 * g);
     }
+    // the state loads complete here: left pending into the chunk loop, the
+    // compiler's wait before the state's first use inside the loop would also
+    // wait for every chunk's prefetch loads issued just before it
+    __builtin_amdgcn_s_waitcnt(0);
 
     // the strictly-upper sub-tiles that the causal products read (row block 0 x
     // column block 1, row block 2 x column block 3) stay zero in Mq
@@ -410,13 +414,15 @@ void ssd_gdn_scan_kernel(GdnArgs a)
             rbeta = load_token(a.beta, t0, Lc, H, h, lane);
         }
         // checkpoint slot of the chunk (-1: none), kept in a vector register until
-        // it is used so that nothing waits for this load before then
+        // it is used so that nothing waits for this load before then; loaded
+        // unconditionally (an empty buffer range reads zero) so that no path
+        // leaves it pending
         const int gc = c0 + c;
-        next_dst = -1;
-        if (a.chunk_states != nullptr && gc >= 0 && gc < a.max_chunks)
-            next_dst = a.chunk_state_dst
-                           ? (int)__builtin_amdgcn_raw_buffer_load_b32(rsrc(a.chunk_state_dst + gc, 4), 0, 0, 0)
-                           : gc;
+        const bool in_grid = a.chunk_states != nullptr && gc >= 0 && gc < a.max_chunks;
+        const bool table = in_grid && a.chunk_state_dst != nullptr;
+        const int slot = (int)__builtin_amdgcn_raw_buffer_load_b32(
+            rsrc(table ? a.chunk_state_dst + gc : a.chunk_state_dst, table ? 4 : 0), 0, 0, 0);
+        next_dst = table ? slot : (in_grid ? gc : -1);
     };
     auto stage_store = [&]() {
 #pragma unroll
@@ -451,7 +457,11 @@ void ssd_gdn_scan_kernel(GdnArgs a)
     for (int c = 0; c < nch; ++c) {
         const int64_t t0 = tb + (int64_t)c * CH;
         const int Lc = min(CH, L - c * CH);
-        if (c + 1 < nch) stage_load(c + 1);
+        // the next chunk's tiles (the last chunk stages itself again: every
+        // iteration takes the same path, so no load is left pending on a path
+        // the compiler's waits must cover)
+        const int cn = c + 1 < nch ? c + 1 : c;
+        stage_load(cn);
 
         // ---- (1) Mq sub-tiles (I, J), I >= J, ten over the eight waves (waves 0 and 1 take two);
         //      lane (g, q): i = 16 I + q, j = 16 J + 4 g + r. Fragments are read in batches
@@ -544,7 +554,7 @@ void ssd_gdn_scan_kernel(GdnArgs a)
             }
         }
         lds_barrier();
-        if (c + 1 < nch) stage_load2(c + 1);
+        stage_load2(cn);
 
         // ---- (2) this key half's share of U = T beta V - W H0 (token 16 d + 4 g + r, column q)
         f32x4 uu[4];
@@ -641,12 +651,10 @@ void ssd_gdn_scan_kernel(GdnArgs a)
         }
 
         // ---- (3) the next chunk's tiles and tables
-        if (c + 1 < nch) {
-            lds_barrier();   // every wave is done with this chunk's tiles
-            stage_store();
-            cur_dst = next_dst;
-            lds_barrier();
-        }
+        lds_barrier();   // every wave is done with this chunk's tiles
+        stage_store();
+        cur_dst = next_dst;
+        lds_barrier();
     }
 
     float *fd = a.final_states + ((int64_t)(s * H + h) * DV + vw + q) * DK + k0;
