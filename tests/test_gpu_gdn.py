@@ -119,6 +119,19 @@ def test_gdn_slow_decay_long_sequence():
     check_close(fin, fin_ref, TOL["bf16"], "final states")
 
 
+def test_gdn_strong_decay_and_full_writes():
+    """Gates 50x stronger (decay factors down to e^-10 per token: the state forgets
+    within a few tokens, the decay tables underflow to zero) and beta = 1 (every
+    token overwrites its key direction entirely)."""
+    w = make_gdn_inputs([200, 70], 2, 1, 128, 128, init_seqs=(0, 1), seed=18)
+    w.gate.mul_(50.0)
+    w.beta.fill_(1.0)
+    _, o, fin, _ = _run(w)
+    o_ref, fin_ref, _ = _oracle(w)
+    check_close(o, o_ref, TOL["bf16"], "o")
+    check_close(fin, fin_ref, TOL["bf16"], "final states")
+
+
 def test_gdn_bit_deterministic():
     w = make_gdn_inputs([500, 77, 128], 4, 2, 128, 128, init_seqs=(0,), seed=9)
     d = _dev(w)
