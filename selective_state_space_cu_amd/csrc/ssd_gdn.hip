@@ -11,6 +11,7 @@
 // gamma_i = e^(G_i):
 //     A_ij = beta_i e^(G_i - G_j) k_i . k_j   (j < i),   T = (I + A)^-1 (unit lower triangular)
 //     W = T diag(beta gamma) K,   U = T diag(beta) V - W H0          (the chunk's write values)
+//       = T (diag(beta) V - diag(beta gamma) K H0)                   (the form computed here)
 //     O = scale (diag(gamma) Q H0 + (e^(G_i - G_j) q_i . k_j)_{j <= i} U)
 //     H_next = gamma_last H0 + K^T diag(e^(G_last - G)) U
 // (U_i is the delta-rule write value of token i; the token loop computes the
@@ -28,10 +29,10 @@
 //    on neither the state nor the values, so no chunk waits for another here.
 //  ssd_gdn_scan_kernel, one workgroup per (sequence, value head, 64 value
 //    columns), walks the chunks in order with the state in registers, split by
-//    keys over two waves per SIMD; per chunk only matrix-core products: W,
-//    T beta V, Q H0, the causal Q K^T (masked), then U = T beta V - W H0, O and
-//    the state update. The next chunk's K, Q, V and T are loaded into registers
-//    while the current chunk computes.
+//    keys over two waves per SIMD; per chunk only matrix-core products: K H0,
+//    Q H0, the causal Q K^T (masked), U = T (beta V - beta gamma K H0), O and the
+//    state update, with two barriers. The next chunk's K, Q, V and T are loaded
+//    into registers while the current chunk computes.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -302,17 +303,20 @@ __global__ __launch_bounds__(256) void ssd_gdn_prep_kernel(GdnArgs a)
 // st[u][r] = S[16 vb + q][64 kh + 16 u + 4 g + r] for lane (g, q)), carried
 // from chunk to chunk. Per chunk:
 //   (1) Mq = (e^(G_i - G_j) q_i . k_j)_{j <= i} (bf16 sub-tiles over the waves),
-//       W (wave w: keys 16 w ..), and in registers the wave's share of
-//       T beta V and its key half of Q H0; the next chunk's loads in flight;
-//   (2) its key half of W H0; the two halves of U = T beta V - W H0 and of
-//       Q H0 are added through LDS; U stays in registers in the accumulator
+//       and in registers the wave's key half of K H0 and of Q H0, and its
+//       share of U: T applied to beta V on tokens 32 kh .. 32 kh + 31 (zero on
+//       the others) minus beta gamma times its key half of K H0;
+//       the next chunk's loads in flight;
+//   (2) the two key halves' shares of U and of Q H0 are added through LDS
+//       (one barrier); U stays in registers in the accumulator
 //       layout (token 16 d + 4 g + r, column q), which is the operand layout of
 //       both remaining products once their other operand is read in the same
 //       token order (32 ks + 4 g + r, then 32 ks + 16 + 4 g + r):
 //       O = scale (diag(gamma) Q H0 + Mq U) for the wave's half of the rows,
 //       H = gamma_last H + K^T (rho U) for its key half; the state after the
 //       chunk to its checkpoint slot;
-//   (3) the next chunk's tiles into LDS and its tables.
+//   (3) the next chunk's tiles into LDS and its tables (K and the tables into
+//       their second buffers), then one barrier: two per chunk.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ssd_gdn_scan_kernel(GdnArgs a)
 #if !defined(__HIP_DEVICE_COMPILE__)
@@ -324,9 +328,10 @@ void ssd_gdn_scan_kernel(GdnArgs a)
     using Frag = O::Frag;
     constexpr int DK = kGdnDk, CH = kGdnChunk;
 
-    __shared__ __align__(16) unsigned char sK[kTileR];
+    // K and the tables are double-buffered: the next chunk's are staged while this
+    // chunk's state update still reads its own
+    __shared__ __align__(16) unsigned char sK[2 * kTileR];
     __shared__ __align__(16) unsigned char sQ[kTileR];
-    __shared__ __align__(16) unsigned char sW[kTileR];
     __shared__ __align__(16) unsigned char sV[kTileV];
     __shared__ __align__(16) unsigned char sT[kTileM];
     __shared__ __align__(16) unsigned char sMq[kTileM];
@@ -335,9 +340,8 @@ void ssd_gdn_scan_kernel(GdnArgs a)
     __shared__ __align__(16) f32x4 xU[8 * 4 * 64];
     __shared__ __align__(16) f32x4 xO[8 * 2 * 64];
     // tables of the chunk: G (log2), gamma, beta, beta gamma, rho (64 each)
-    __shared__ __align__(16) float tab[5 * 64];
-    float *const tG = tab, *const tGam = tab + 64, *const tBeta = tab + 128, *const tBG = tab + 192,
-                 *const tRho = tab + 256;
+    constexpr int kTab = 5 * 64;
+    __shared__ __align__(16) float tab[2 * kTab];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -424,23 +428,24 @@ void ssd_gdn_scan_kernel(GdnArgs a)
             rsrc(table ? a.chunk_state_dst + gc : a.chunk_state_dst, table ? 4 : 0), 0, 0, 0);
         next_dst = table ? slot : (in_grid ? gc : -1);
     };
-    auto stage_store = [&]() {
+    auto stage_store = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int piece = tid + 512 * i;
-            rt_store(sK, piece >> 4, piece & 15, rk[i]);
+            rt_store(sK + buf * kTileR, piece >> 4, piece & 15, rk[i]);
             rt_store(sQ, piece >> 4, piece & 15, rq[i]);
         }
         *reinterpret_cast<u32x4 *>(sV + (tid >> 3) * kPX + 16 * (tid & 7)) = rv;
         *reinterpret_cast<u32x4 *>(sT + (tid >> 3) * kMPB + 16 * (tid & 7)) = rt;
-        if (wave == 0) {   // tables (lane j = token j; neutral past the end)
+        if (wave == 0) {   // tables G, gamma, beta, beta gamma, rho (lane j = token j; neutral past the end)
+            float *const tb = tab + buf * kTab;
             const float v = wave_scan(rgate * kLog2e);   // inclusive cumsum (log2)
             const float gam = fast_exp2(v);
-            tG[lane] = v;
-            tGam[lane] = gam;
-            tBeta[lane] = rbeta;
-            tBG[lane] = rbeta * gam;
-            tRho[lane] = fast_exp2(readlane(v, 63) - v);
+            tb[lane] = v;
+            tb[64 + lane] = gam;
+            tb[128 + lane] = rbeta;
+            tb[192 + lane] = rbeta * gam;
+            tb[256 + lane] = fast_exp2(readlane(v, 63) - v);
         }
     };
 
@@ -448,7 +453,7 @@ void ssd_gdn_scan_kernel(GdnArgs a)
     if (nch > 0) {
         stage_load(0);
         stage_load2(0);
-        stage_store();
+        stage_store(0);
         cur_dst = next_dst;
     }
     lds_barrier();
@@ -462,6 +467,10 @@ void ssd_gdn_scan_kernel(GdnArgs a)
         // the compiler's waits must cover)
         const int cn = c + 1 < nch ? c + 1 : c;
         stage_load(cn);
+        const int cb = c & 1;   // this chunk's K and table buffers
+        const unsigned char *const cK = sK + cb * kTileR;
+        const float *const tG = tab + cb * kTab, *const tGam = tG + 64, *const tBeta = tG + 128,
+                    *const tBG = tG + 192, *const tRho = tG + 256;
 
         // ---- (1) Mq sub-tiles (I, J), I >= J, ten over the eight waves (waves 0 and 1 take two);
         //      lane (g, q): i = 16 I + q, j = 16 J + 4 g + r. Fragments are read in batches
@@ -474,7 +483,7 @@ void ssd_gdn_scan_kernel(GdnArgs a)
             Frag kf[4], qf[4];
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
-                kf[kc] = rt_frag(sK, 16 * J + q, kc, g);
+                kf[kc] = rt_frag(cK, 16 * J + q, kc, g);
                 qf[kc] = rt_frag(sQ, 16 * I + q, kc, g);
             }
             const int i = 16 * I + q;
@@ -492,89 +501,85 @@ void ssd_gdn_scan_kernel(GdnArgs a)
             }
             O::mstore4(sMq + i * kMPB + (16 * J + 4 * g) * 2, fq);
         }
-        // W = T diag(beta gamma) K, keys 16 w .. 16 w + 15 (from W^T = (beta gamma K)^T T^T), this
-        // wave's key half of Q H0 (token 16 d + q, column 4 g + r) and its two row blocks of
-        // T beta V (token 16 d + 4 g + r, column q): d = 0, 3 for kh = 0 and d = 1, 2 for kh = 1,
-        // which balances the causal products between the halves
+        // U = T (diag(beta) V - diag(beta gamma) K H0) (W = T diag(beta gamma) K is never formed):
+        // this wave's key half of K H0 (token 16 d + 4 g + r, column q) and of Q H0 (token 16 d + q,
+        // column 4 g + r); then its share of U, with the beta V term of k step ks = kh, for all four
+        // row blocks: U is linear in the key halves, whose shares meet through LDS
         Frag hf[2];   // H0 fragments of this wave's key half: k step kc covers keys k0 + 32 kc .. (permuted)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) hf[kc] = O::from_f32(st[2 * kc], st[2 * kc + 1]);
-        f32x4 o1[4], u1[2];
+        f32x4 o1[4], uu[4];
         {
-            Frag kt[2], vf[2], tf[4][2], qf[4][2];
-            f32x4 bg[2][2], be[2][2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                kt[ks] = rt_tr(sK, 32 * ks + 8 * g, 16 * wave, q);
-                vf[ks] = O::tr(sV + (32 * ks + 8 * g + O::tr_row(q)) * kPX + (16 * vb + O::tr_col(q)) * 2, 4 * kPX);
-                bg[ks][0] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 8 * g);
-                bg[ks][1] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 8 * g + 4);
-                be[ks][0] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * ks + 8 * g);
-                be[ks][1] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * ks + 8 * g + 4);
-            }
+            Frag kf[4][2], qf[4][2];
 #pragma unroll
             for (int d = 0; d < 4; ++d)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    tf[d][ks] = O::mrow(sT + (16 * d + q) * kMPB + (32 * ks + 8 * g) * 2);
-                    qf[d][ks] = rt_frag(sQ, 16 * d + q, 2 * kh + ks, g);
+                for (int kc = 0; kc < 2; ++kc) {
+                    kf[d][kc] = rt_frag(cK, 16 * d + q, 2 * kh + kc, g);
+                    qf[d][kc] = rt_frag(sQ, 16 * d + q, 2 * kh + kc, g);
                 }
             lds_fence();
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const float wb[8] = {bg[ks][0][0], bg[ks][0][1], bg[ks][0][2], bg[ks][0][3],
-                                     bg[ks][1][0], bg[ks][1][1], bg[ks][1][2], bg[ks][1][3]};
-                const float wv[8] = {be[ks][0][0], be[ks][0][1], be[ks][0][2], be[ks][0][3],
-                                     be[ks][1][0], be[ks][1][1], be[ks][1][2], be[ks][1][3]};
-                kt[ks] = O::scale(kt[ks], wb);   // (beta gamma K)^T: key column 16 w + q, tokens 32 ks + 8 g + slot
-                vf[ks] = O::scale(vf[ks], wv);   // (beta V): tokens 32 ks + 8 g + slot, value column 16 vb + q
-            }
+            f32x4 pk[4];
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= d / 2) acc = O::mma(acc, kt[ks], tf[d][ks]);
-                // acc[r] = W[token 16 d + q][key 16 w + 4 g + r]
-                *reinterpret_cast<u32x2 *>(sW + rt_row(16 * d + q) + rt_col(16 * wave + 4 * g)) =
-                    u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+                pk[d] = f32x4{0, 0, 0, 0};
                 o1[d] = f32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) o1[d] = O::mma(o1[d], hf[kc], qf[d][kc]);
+                for (int kc = 0; kc < 2; ++kc) {
+                    pk[d] = O::mma(pk[d], kf[d][kc], hf[kc]);
+                    o1[d] = O::mma(o1[d], hf[kc], qf[d][kc]);
+                }
             }
-            // (register arrays are indexed by compile-time values only: the row blocks of
-            // this key half, d = 0, 3 (kh 0) or 1, 2 (kh 1), are selected, not indexed)
-#pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
-                u1[dd] = f32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks == 0 || dd == 1)
-                        u1[dd] = O::mma(u1[dd], kh ? tf[1 + dd][ks] : tf[3 * dd][ks], vf[ks]);
-            }
-        }
-        lds_barrier();
-        stage_load2(cn);
-
-        // ---- (2) this key half's share of U = T beta V - W H0 (token 16 d + 4 g + r, column q)
-        f32x4 uu[4];
-        {
-            Frag wf[4][2];
+            // the right operand of T (.) for k step ks, in the token order of the accumulator
+            // layout (32 ks + 4 g + r in slots 0-3, 32 ks + 16 + 4 g + r in slots 4-7); T rows are
+            // read in the same order
+            Frag tf[4][2];
 #pragma unroll
             for (int d = 0; d < 4; ++d)
 #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) wf[d][kc] = rt_frag(sW, 16 * d + q, 2 * kh + kc, g);
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks <= d / 2) tf[d][ks] = O::rowk_perm(sT + (16 * d + q) * kMPB + (32 * ks + 4 * g) * 2);
+            const Frag vf = O::tr(sV + (32 * kh + 4 * g + O::tr_row(q)) * kPX + (16 * vb + O::tr_col(q)) * 2, 16 * kPX);
+            f32x4 bg[2][2], be[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bg[ks][0] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 4 * g);
+                bg[ks][1] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 16 + 4 * g);
+            }
+            be[0] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * kh + 4 * g);
+            be[1] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * kh + 16 + 4 * g);
             lds_fence();
+            f32x4 bv[2];   // beta V of k step kh (slots 0-3, 4-7)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t w = vf.w[r >> 1];
+                bv[0][r] = be[0][r] * ((r & 1) ? bf16_hi(w) : bf16_lo(w));
+                const uint32_t w2 = vf.w[2 + (r >> 1)];
+                bv[1][r] = be[1][r] * ((r & 1) ? bf16_hi(w2) : bf16_lo(w2));
+            }
+            Frag xf[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bool own = ks == kh;
+                f32x4 lo, hi;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    lo[r] = (own ? bv[0][r] : 0.0f) - bg[ks][0][r] * pk[2 * ks][r];
+                    hi[r] = (own ? bv[1][r] : 0.0f) - bg[ks][1][r] * pk[2 * ks + 1][r];
+                }
+                xf[ks] = O::from_f32(lo, hi);
+            }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                f32x4 u2 = {0, 0, 0, 0};
+                uu[d] = f32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int kc = 0; kc < 2; ++kc) u2 = O::mma(u2, wf[d][kc], hf[kc]);
-                // row block d belongs to key half kh = (d == 1 || d == 2), as u1[d == 3 || d == 2]
-                uu[d] = (((d == 1 || d == 2) ? 1 : 0) == kh ? u1[(d == 2 || d == 3) ? 1 : 0] : f32x4{0, 0, 0, 0}) - u2;
-                xU[(wave * 4 + d) * 64 + lane] = uu[d];
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks <= d / 2) uu[d] = O::mma(uu[d], tf[d][ks], xf[ks]);
             }
         }
+        stage_load2(cn);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) xU[(wave * 4 + d) * 64 + lane] = uu[d];
 #pragma unroll
         for (int dd = 0; dd < 2; ++dd) xO[(wave * 2 + dd) * 64 + lane] = kh ? o1[3 * dd] : o1[1 + dd];
         lds_barrier();
@@ -599,7 +604,7 @@ void ssd_gdn_scan_kernel(GdnArgs a)
                 r1[ks] = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 16 + 4 * g);
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    ktr[u][ks] = O::tr(sK + rt_row(32 * ks + 4 * g) + O::tr_row(q) * kPB + rt_col(k0 + 16 * u + O::tr_col(q)),
+                    ktr[u][ks] = O::tr(cK + rt_row(32 * ks + 4 * g) + O::tr_row(q) * kPB + rt_col(k0 + 16 * u + O::tr_col(q)),
                                        2 * kGB);
             }
             const f32x4 gam = {tGam[16 * (kh ? 1 : 0) + q], tGam[16 * (kh ? 2 : 3) + q], 0.0f, 0.0f};
@@ -650,9 +655,10 @@ void ssd_gdn_scan_kernel(GdnArgs a)
             }
         }
 
-        // ---- (3) the next chunk's tiles and tables
-        lds_barrier();   // every wave is done with this chunk's tiles
-        stage_store();
+        // ---- (3) the next chunk's K and tables into the other buffers, its Q, V and T over
+        //      this chunk's (no wave reads those past the first barrier); one barrier then
+        //      makes them visible and orders this chunk's Mq reads before the next chunk's writes
+        stage_store(cb ^ 1);
         cur_dst = next_dst;
         lds_barrier();
     }
