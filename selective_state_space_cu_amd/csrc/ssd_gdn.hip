@@ -144,151 +144,220 @@ static_assert(kGdnWsBytes == kGdnChunk * kGdnChunk * 2, "workspace: one bf16 T p
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// T = (I + A)^-1 for one (chunk, value head)
+// T = (I + A)^-1 for every (chunk, value head)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void ssd_gdn_prep_kernel(GdnArgs a)
+//
+// Persistent workgroups of four waves; item = (chunk, key head, block of up to
+// four of its value heads), taken in steps of the grid. The item's k rows and
+// their Gram sub-tiles K K^T are shared by its value heads, which differ only
+// in beta and the gates: per value head, A from the Gram sub-tiles held in
+// registers, then T. The next item's k rows, gates and betas are loaded into
+// registers while the current one computes (wave w: value head w of the block),
+// and nothing waits for them before the next item begins.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void ssd_gdn_prep_kernel(GdnArgs a)
 #if !defined(__HIP_DEVICE_COMPILE__)
 {
 }
 #else
 {
     using O = Ops<uint16_t>;
-    constexpr int CH = kGdnChunk;
-    __shared__ __align__(16) float fTT[2 * kTri];   // K rows (row tile) first; then T and T^T blocks
-    __shared__ __align__(16) float fA[kTri];        // A blocks (float32, strictly lower)
-    __shared__ __align__(16) float tab[2 * 64];     // G (log2), beta
+    constexpr int CH = kGdnChunk, kHB = 4;   // value heads per item (at most)
+    __shared__ __align__(16) float fTT[2 * kTri];    // K rows (row tile) first; then T and T^T blocks
+    __shared__ __align__(16) float fA[kTri];         // A blocks (float32, strictly lower)
+    __shared__ __align__(16) float tab[kHB * 2 * 64]; // per value head of the item: G (log2), beta
     unsigned char *const sK = reinterpret_cast<unsigned char *>(fTT);
     float *const fT = fTT, *const fTt = fTT + kTri;   // T_IJ blocks; (T_IJ)^T blocks
-    float *const tG = tab, *const tBeta = tab + 64;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane & 15, g = lane >> 4;
+    // the waves' roles in the phases below rotate between workgroups, so that the
+    // longer roles of the workgroups on one CU fall on different SIMDs
+    const int role = (wave + (int)(blockIdx.x >> 8)) & 3;
 
     if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
-    const int H = a.H, G = a.G;
-    // (chunk, key head) items; the value heads of one key head share its k rows
-    const int2 it = xcd_order(blockIdx.x, gridDim.x, H / G);
-    const int gc = it.x / G, grp = it.x - (it.x / G) * G, h = grp * (H / G) + it.y;
-    if (gc >= a.max_chunks) return;
-    const int s = a.chunk_seq_idx[gc];
-    if (s < 0 || s >= a.S) return;
-    const int t0 = a.chunk_offsets[gc], t1 = a.chunk_offsets[gc + 1];
-    if (t0 < 0 || t1 > a.T || t1 <= t0 || t1 - t0 > CH) return;
-    const int Lc = t1 - t0;
-
-    {
-        u32x4 kv[4];
-        load_rows(kv, a.k, t0, Lc, G, grp, tid);
-        float gt = 0.0f, bt = 0.0f;
-        if (wave == 0) {
-            gt = load_token(a.gate, t0, Lc, H, h, lane);
-            bt = load_token(a.beta, t0, Lc, H, h, lane);
+    const int H = a.H, G = a.G, R = H / G;
+    const int nblk = (R + kHB - 1) / kHB;            // value-head blocks per key head
+    const int nitems = a.max_chunks * G * nblk;
+    // an item's chunk, token range, first value head and value-head count; false for a
+    // chunk that holds no tokens
+    struct Item { int gc, t0, Lc, h0, nh; };
+    auto span = [&](int it, Item &m) -> bool {
+        m.gc = it / (G * nblk);
+        const int rest = it - m.gc * (G * nblk), grp = rest / nblk, blk = rest - grp * nblk;
+        m.h0 = grp * R + kHB * blk;
+        m.nh = min(kHB, R - kHB * blk);
+        // read through the constant address space (scalar loads): vector loads here would
+        // make the item's first wait also wait for the previous item's stores
+        typedef const __attribute__((address_space(4))) int cint;
+        const int sq = ((cint *)(uintptr_t)a.chunk_seq_idx)[m.gc];
+        if (sq < 0 || sq >= a.S) return false;
+        const int c0 = ((cint *)(uintptr_t)a.chunk_offsets)[m.gc], c1 = ((cint *)(uintptr_t)a.chunk_offsets)[m.gc + 1];
+        if (c0 < 0 || c1 > a.T || c1 <= c0 || c1 - c0 > CH) return false;
+        m.t0 = c0;
+        m.Lc = c1 - c0;
+        return true;
+    };
+    u32x4 kv[4];                  // the item's k rows, 4 pieces of 16 bytes per thread
+    float gt = 0.0f, bt = 0.0f;   // wave w: gate and beta of the item's value head w (lane = token)
+    // issued on every path, with empty buffer ranges (reads of zero) where there is
+    // nothing to load, so that no register copy has to wait for these loads
+    auto prefetch = [&](const Item &m, bool valid) {
+        const int rowb = G * kGdnDk * 2;
+        const __amdgpu_buffer_rsrc_t rk =
+            rsrc(a.k + ((int64_t)m.t0 * G + m.h0 / R) * kGdnDk, valid ? (int64_t)(m.Lc - 1) * rowb + 256 : 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int piece = tid + 256 * i;
+            kv[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (piece >> 4) * rowb + 16 * (piece & 15), 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rt_store(sK, (tid + 256 * i) >> 4, (tid + 256 * i) & 15, kv[i]);
-        if (wave == 0) {   // inclusive cumsum of the log2-decay (zero past the chunk: neutral)
-            tG[lane] = wave_scan(gt * kLog2e);
-            tBeta[lane] = bt;
-        }
-    }
-    lds_barrier();
+        const bool head = valid && wave < m.nh;
+        const int64_t tok = (int64_t)m.t0 * H + m.h0 + (head ? wave : 0);
+        const int64_t tb = head ? (int64_t)(m.Lc - 1) * H * 4 + 4 : 0;
+        gt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(a.gate + tok, tb), lane * H * 4, 0, 0));
+        bt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(a.beta + tok, tb), lane * H * 4, 0, 0));
+    };
 
-    // ---- A sub-tiles: A[i][j] = beta_i e^(G_i - G_j) k_i . k_j (j < i); lane (g, q): i = 16 I + q,
-    //      j = 16 J + 4 g + r
+    int item = blockIdx.x;
+    Item cur = {0, 0, 0, 0, 0};
+    bool ok = item < nitems && span(item, cur);
+    prefetch(cur, ok);
+    while (item < nitems) {
+        const int nxt = item + (int)gridDim.x;
+        Item nx = {0, 0, 0, 0, 0};
+        const bool okn = nxt < nitems && span(nxt, nx);
+        f32x4 kk[3];
+        if (ok) {
+            lds_barrier();   // the previous item's reads of its tables and of its last T are done
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        const int code = sub_tile(wave, n), I = code >> 4, J = code & 15;
-        f32x4 kk = {0, 0, 0, 0};
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) kk = O::mma(kk, rt_frag(sK, 16 * J + q, kc, g), rt_frag(sK, 16 * I + q, kc, g));
-        const int i = 16 * I + q;
-        const float gi = tG[i], bi = tBeta[i];
-        const f32x4 gj = *reinterpret_cast<const f32x4 *>(tG + 16 * J + 4 * g);
-        f32x4 fa;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float e = fast_exp2(fminf(gi - gj[r], 0.0f));
-            fa[r] = (16 * J + 4 * g + r < i) ? bi * kk[r] * e : 0.0f;
-        }
-        *reinterpret_cast<f32x4 *>(fA + tri_blk(I, J) + q * kBP + 4 * g) = fa;
-    }
-    lds_barrier();
-
-    // ---- diagonal blocks by forward substitution (wave w: block w; lane column j = q;
-    //      the four lane groups compute the same column): T[i][j] = [i == j] - sum_{m < i} A[i][m] T[m][j]
-    {
-        const float *ab = fA + tri_blk(wave, wave);
-        float tc[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tc[i] = i == q ? 1.0f : 0.0f;
-#pragma unroll
-        for (int m = 0; m < 15; ++m)
-#pragma unroll
-            for (int i = m + 1; i < 16; ++i) tc[i] = fmaf(-ab[i * kBP + m], tc[m], tc[i]);
-        if (g == 0) {
-            float *tb = fT + tri_blk(wave, wave), *tt = fTt + tri_blk(wave, wave);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) tb[i * kBP + q] = tc[i];
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-                *reinterpret_cast<f32x4 *>(tt + q * kBP + 4 * i4) =
-                    f32x4{tc[4 * i4], tc[4 * i4 + 1], tc[4 * i4 + 2], tc[4 * i4 + 3]};
-        }
-    }
-    lds_barrier();
-
-    // ---- blocks next to the diagonal: T_10 (wave 0), T_32 (wave 1): T_{J+1,J} = -T_{J+1,J+1} A_{J+1,J} T_JJ
-    if (wave < 2) {
-        const int J = 2 * wave, I = J + 1;
-        const f32x4 p = mm16(*reinterpret_cast<const f32x4 *>(fA + tri_blk(I, J) + q * kBP + 4 * g),
-                             *reinterpret_cast<const f32x4 *>(fTt + tri_blk(J, J) + q * kBP + 4 * g),
-                             f32x4{0, 0, 0, 0});
-        const f32x4 t = -mm16(*reinterpret_cast<const f32x4 *>(fT + tri_blk(I, I) + q * kBP + 4 * g), p,
-                              f32x4{0, 0, 0, 0});
-        // t[r] = T[16 I + 4 g + r][16 J + q]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) fT[tri_blk(I, J) + (4 * g + r) * kBP + q] = t[r];
-        *reinterpret_cast<f32x4 *>(fTt + tri_blk(I, J) + q * kBP + 4 * g) = t;
-    }
-    lds_barrier();
-
-    // ---- the 32 x 32 corner, one block per wave ((2,0), (2,1), (3,0), (3,1)):
-    //      Y_KJ = sum_{J <= L <= 1} A_KL T_LJ,  T_IJ = -sum_{2 <= K <= I} T_IK Y_KJ
-    {
-        const int I = 2 + (wave >> 1), J = wave & 1;
-        f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-        for (int K = 2; K < 4; ++K) {
-            if (K > I) continue;
-            f32x4 y = {0, 0, 0, 0};
-#pragma unroll
-            for (int L = 0; L < 2; ++L) {
-                if (L < J) continue;
-                y = mm16(*reinterpret_cast<const f32x4 *>(fA + tri_blk(K, L) + q * kBP + 4 * g),
-                         *reinterpret_cast<const f32x4 *>(fTt + tri_blk(L, J) + q * kBP + 4 * g), y);
+            for (int i = 0; i < 4; ++i) rt_store(sK, (tid + 256 * i) >> 4, (tid + 256 * i) & 15, kv[i]);
+            if (wave < cur.nh) {   // inclusive cumsum of the log2-decay (zero past the chunk: neutral)
+                tab[wave * 128 + lane] = wave_scan(gt * kLog2e);
+                tab[wave * 128 + 64 + lane] = bt;
             }
-            acc = mm16(*reinterpret_cast<const f32x4 *>(fT + tri_blk(I, K) + q * kBP + 4 * g), y, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) fT[tri_blk(I, J) + (4 * g + r) * kBP + q] = -acc[r];
-    }
-    lds_barrier();
+            lds_barrier();
 
-    // ---- T (unit lower triangular) -> bf16, row-major 64 x 64, into the workspace
-    {
-        uint16_t *ws = a.workspace + ((int64_t)gc * H + h) * (CH * CH);
+            // ---- Gram sub-tiles kk[m][x] = k_i . k_j of the role's sub-tiles (I, J), I >= J;
+            //      lane (g, q): i = 16 I + q, j = 16 J + 4 g + x
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int e = 8 * (tid + 256 * it), i = e >> 6, j0 = e & 63, I = i >> 4, J = j0 >> 4;
-            const float *src = fT + tri_blk(I, J <= I ? J : I) + (i & 15) * kBP + (j0 & 15);
-            const f32x4 lo = *reinterpret_cast<const f32x4 *>(src), hi = *reinterpret_cast<const f32x4 *>(src + 4);
-            float v8[8];
+            for (int m = 0; m < 3; ++m) {
+                const int code = sub_tile(role, m), I = code >> 4, J = code & 15;
+                kk[m] = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int x = 0; x < 8; ++x) v8[x] = j0 + x <= i ? (x < 4 ? lo[x] : hi[x - 4]) : 0.0f;
-            *reinterpret_cast<u32x4 *>(ws + e) = u32x4{pack_bf16(v8[0], v8[1]), pack_bf16(v8[2], v8[3]),
-                                                       pack_bf16(v8[4], v8[5]), pack_bf16(v8[6], v8[7])};
+                for (int kc = 0; kc < 4; ++kc)
+                    kk[m] = O::mma(kk[m], rt_frag(sK, 16 * J + q, kc, g), rt_frag(sK, 16 * I + q, kc, g));
+            }
         }
+        prefetch(nx, okn);   // the next item's loads fly while this one computes
+        if (ok) {
+            for (int r = 0; r < cur.nh; ++r) {
+                const float *const tG = tab + r * 128, *const tBeta = tG + 64;
+                // ---- A sub-tiles: A[i][j] = beta_i e^(G_i - G_j) k_i . k_j (j < i)
+#pragma unroll
+                for (int m = 0; m < 3; ++m) {
+                    const int code = sub_tile(role, m), I = code >> 4, J = code & 15;
+                    const int i = 16 * I + q;
+                    const float gi = tG[i], bi = tBeta[i];
+                    const f32x4 gj = *reinterpret_cast<const f32x4 *>(tG + 16 * J + 4 * g);
+                    f32x4 fa;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const float e = fast_exp2(fminf(gi - gj[x], 0.0f));
+                        fa[x] = (16 * J + 4 * g + x < i) ? bi * kk[m][x] * e : 0.0f;
+                    }
+                    *reinterpret_cast<f32x4 *>(fA + tri_blk(I, J) + q * kBP + 4 * g) = fa;
+                }
+                lds_barrier();
+
+                // ---- diagonal blocks by forward substitution, all four by the wave of role 0 (lane
+                //      group g: block g; lane column j = q): T[i][j] = [i == j] - sum_{m < i} A[i][m] T[m][j]
+                if (role == 0) {
+                    const float *ab = fA + tri_blk(g, g);
+                    float tc[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) tc[i] = i == q ? 1.0f : 0.0f;
+                    // columns of A in pairs, each read as 8-byte row pieces just before its two
+                    // steps (a fence before each pair keeps the reads from all being issued up
+                    // front, which would take more registers than there are)
+                    float2 ar[16];
+#pragma unroll
+                    for (int m = 0; m < 15; ++m) {
+                        if ((m & 1) == 0) {
+                            lds_fence();
+#pragma unroll
+                            for (int i = m + 1; i < 16; ++i) ar[i] = *reinterpret_cast<const float2 *>(ab + i * kBP + m);
+                        }
+#pragma unroll
+                        for (int i = m + 1; i < 16; ++i) tc[i] = fmaf(-((m & 1) ? ar[i].y : ar[i].x), tc[m], tc[i]);
+                    }
+                    float *tb = fT + tri_blk(g, g), *tt = fTt + tri_blk(g, g);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) tb[i * kBP + q] = tc[i];
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4)
+                        *reinterpret_cast<f32x4 *>(tt + q * kBP + 4 * i4) =
+                            f32x4{tc[4 * i4], tc[4 * i4 + 1], tc[4 * i4 + 2], tc[4 * i4 + 3]};
+                }
+                lds_barrier();
+
+                // ---- blocks next to the diagonal: T_10 (role 0), T_32 (role 1): T_{J+1,J} = -T_{J+1,J+1} A_{J+1,J} T_JJ
+                if (role < 2) {
+                    const int J = 2 * role, I = J + 1;
+                    const f32x4 p = mm16(*reinterpret_cast<const f32x4 *>(fA + tri_blk(I, J) + q * kBP + 4 * g),
+                                         *reinterpret_cast<const f32x4 *>(fTt + tri_blk(J, J) + q * kBP + 4 * g),
+                                         f32x4{0, 0, 0, 0});
+                    const f32x4 t = -mm16(*reinterpret_cast<const f32x4 *>(fT + tri_blk(I, I) + q * kBP + 4 * g), p,
+                                          f32x4{0, 0, 0, 0});
+                    // t[x] = T[16 I + 4 g + x][16 J + q]
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) fT[tri_blk(I, J) + (4 * g + x) * kBP + q] = t[x];
+                    *reinterpret_cast<f32x4 *>(fTt + tri_blk(I, J) + q * kBP + 4 * g) = t;
+                }
+                lds_barrier();
+
+                // ---- the 32 x 32 corner, one block per role ((2,0), (2,1), (3,0), (3,1)):
+                //      Y_KJ = sum_{J <= L <= 1} A_KL T_LJ,  T_IJ = -sum_{2 <= K <= I} T_IK Y_KJ
+                {
+                    const int I = 2 + (role >> 1), J = role & 1;
+                    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+                    for (int K = 2; K < 4; ++K) {
+                        if (K > I) continue;
+                        f32x4 y = {0, 0, 0, 0};
+#pragma unroll
+                        for (int L = 0; L < 2; ++L) {
+                            if (L < J) continue;
+                            y = mm16(*reinterpret_cast<const f32x4 *>(fA + tri_blk(K, L) + q * kBP + 4 * g),
+                                     *reinterpret_cast<const f32x4 *>(fTt + tri_blk(L, J) + q * kBP + 4 * g), y);
+                        }
+                        acc = mm16(*reinterpret_cast<const f32x4 *>(fT + tri_blk(I, K) + q * kBP + 4 * g), y, acc);
+                    }
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) fT[tri_blk(I, J) + (4 * g + x) * kBP + q] = -acc[x];
+                }
+                lds_barrier();
+
+                // ---- T (unit lower triangular) -> bf16, row-major 64 x 64, into the workspace
+                {
+                    uint16_t *ws = a.workspace + ((int64_t)cur.gc * H + cur.h0 + r) * (CH * CH);
+#pragma unroll
+                    for (int it = 0; it < 2; ++it) {
+                        const int e = 8 * (tid + 256 * it), i = e >> 6, j0 = e & 63, I = i >> 4, J = j0 >> 4;
+                        const float *src = fT + tri_blk(I, J <= I ? J : I) + (i & 15) * kBP + (j0 & 15);
+                        const f32x4 lo = *reinterpret_cast<const f32x4 *>(src), hi = *reinterpret_cast<const f32x4 *>(src + 4);
+                        float v8[8];
+#pragma unroll
+                        for (int x = 0; x < 8; ++x) v8[x] = j0 + x <= i ? (x < 4 ? lo[x] : hi[x - 4]) : 0.0f;
+                        *reinterpret_cast<u32x4 *>(ws + e) = u32x4{pack_bf16(v8[0], v8[1]), pack_bf16(v8[2], v8[3]),
+                                                                   pack_bf16(v8[4], v8[5]), pack_bf16(v8[6], v8[7])};
+                    }
+                }
+            }
+        }
+        item = nxt;
+        cur = nx;
+        ok = okn;
     }
 }
 #endif
@@ -694,10 +763,18 @@ hipError_t gdn_scratch(void **ptr) {
 }
 
 hipError_t launch_gdn(const GdnArgs &a, hipStream_t stream) {
-    const int64_t prep = (int64_t)a.max_chunks * a.H;
-    if (prep > 0 && a.T > 0) {
-        hipLaunchKernelGGL(ssd_gdn_prep_kernel, dim3((unsigned)prep), dim3(256), 0, stream, a);
-        const hipError_t e = hipGetLastError();
+    const int64_t items = (int64_t)a.max_chunks * a.G * ((a.H / a.G + 3) / 4);
+    if (items > 0 && a.T > 0) {
+        // four workgroups per CU, the items spread evenly over the rounds
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        const int64_t slots = 4 * (int64_t)(cus > 0 ? cus : 1);
+        const int64_t rounds = (items + slots - 1) / slots;
+        const int64_t grid = (items + rounds - 1) / rounds;
+        hipLaunchKernelGGL(ssd_gdn_prep_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t blocks = (int64_t)a.S * a.H * a.nptiles;
