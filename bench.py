@@ -350,9 +350,10 @@ def gdn_work(w, n_ckpt):
     """Algorithmic bytes and flops of one GDN chunk call. Bytes: q, k read once
     per key head, v read and o written once, gate and beta read once, each
     flagged initial state read, each final state and checkpoint written once.
-    Flops: per chunk of Lc tokens and value head, the chunked form's products
-    (K K^T and Q K^T lower triangles, W and T beta V, W H0, Q H0, the causal
-    Mq U and the state update K^T U), counted once per value head."""
+    Flops: per chunk of Lc tokens and value head, the products of the form the
+    kernels compute (K K^T and Q K^T lower triangles, K H0, Q H0, the triangular
+    T (beta V - beta gamma K H0), the causal Mq U and the state update K^T U),
+    counted once per value head."""
     T, G, dk = w.q.shape
     H, dv = w.v.shape[1], w.v.shape[2]
     state = H * dv * dk * 4
@@ -363,7 +364,7 @@ def gdn_work(w, n_ckpt):
         for c0 in range(0, L, w.chunk_size):
             Lc = min(w.chunk_size, L - c0)
             tri = Lc * (Lc + 1) // 2
-            flops += 2 * H * (2 * tri * dk + tri * dk + tri * dv + 3 * Lc * dk * dv + tri * dv + Lc * dk * dv)
+            flops += 2 * H * (2 * tri * dk + 2 * Lc * dk * dv + tri * dv + tri * dv + Lc * dk * dv)
     return bytes_, flops
 
 
