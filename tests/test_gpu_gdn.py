@@ -74,6 +74,10 @@ SHAPES = [
     ([300, 17], 2, 2, 64, (0,)),
     ([129, 5, 256], 3, 1, 192, (2,)),
     ([64] * 6, 8, 4, 128, (0, 1, 2, 3, 4, 5)),
+    # four value heads per key head (one full block of the prep kernel's items), and ten
+    # (three blocks, the last one of two heads)
+    ([70, 129], 8, 2, 128, (1,)),
+    ([100, 64, 3], 10, 1, 64, (0, 2)),
 ]
 
 
