@@ -528,209 +528,217 @@ void ssd_gdn_scan_kernel(GdnArgs a)
     lds_barrier();
 
     const float scale = a.scale;
-    for (int c = 0; c < nch; ++c) {
-        const int64_t t0 = tb + (int64_t)c * CH;
-        const int Lc = min(CH, L - c * CH);
-        // the next chunk's tiles (the last chunk stages itself again: every
-        // iteration takes the same path, so no load is left pending on a path
-        // the compiler's waits must cover)
-        const int cn = c + 1 < nch ? c + 1 : c;
-        stage_load(cn);
-        const int cb = c & 1;   // this chunk's K and table buffers
-        const unsigned char *const cK = sK + cb * kTileR;
-        const float *const tG = tab + cb * kTab, *const tGam = tG + 64, *const tBeta = tG + 128,
-                    *const tBG = tG + 192, *const tRho = tG + 256;
+    // the chunk loop, one copy per key half (kh is wave-uniform): the choices between the
+    // halves' row blocks and token ranges are then made at compile time, not by selects
+    auto walk = [&](auto khc) {
+        constexpr int kh = decltype(khc)::value;   // (shadows the run-time value)
+        constexpr int k0 = 64 * kh;
+        for (int c = 0; c < nch; ++c) {
+            const int64_t t0 = tb + (int64_t)c * CH;
+            const int Lc = min(CH, L - c * CH);
+            // the next chunk's tiles (the last chunk stages itself again: every
+            // iteration takes the same path, so no load is left pending on a path
+            // the compiler's waits must cover)
+            const int cn = c + 1 < nch ? c + 1 : c;
+            stage_load(cn);
+            const int cb = c & 1;   // this chunk's K and table buffers
+            const unsigned char *const cK = sK + cb * kTileR;
+            const float *const tG = tab + cb * kTab, *const tGam = tG + 64, *const tBeta = tG + 128,
+                        *const tBG = tG + 192, *const tRho = tG + 256;
 
-        // ---- (1) Mq sub-tiles (I, J), I >= J, ten over the eight waves (waves 0 and 1 take two);
-        //      lane (g, q): i = 16 I + q, j = 16 J + 4 g + r. Fragments are read in batches
-        //      ahead of their products (the fences keep the reads together).
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            if (n == 1 && wave >= 2) break;
-            const int code = n == 0 ? (int)((0x3130222120111000ull >> (8 * wave)) & 0xff) : 0x32 + wave;
-            const int I = code >> 4, J = code & 15;
-            Frag kf[4], qf[4];
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                kf[kc] = rt_frag(cK, 16 * J + q, kc, g);
-                qf[kc] = rt_frag(sQ, 16 * I + q, kc, g);
-            }
-            const int i = 16 * I + q;
-            const float gi = tG[i];
-            const f32x4 gj = *reinterpret_cast<const f32x4 *>(tG + 16 * J + 4 * g);
-            lds_fence();
-            f32x4 qk = {0, 0, 0, 0};
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) qk = O::mma(qk, kf[kc], qf[kc]);
-            float fq[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e = fast_exp2(fminf(gi - gj[r], 0.0f));
-                fq[r] = (16 * J + 4 * g + r <= i) ? qk[r] * e : 0.0f;
-            }
-            O::mstore4(sMq + i * kMPB + (16 * J + 4 * g) * 2, fq);
-        }
-        // U = T (diag(beta) V - diag(beta gamma) K H0) (W = T diag(beta gamma) K is never formed):
-        // this wave's key half of K H0 (token 16 d + 4 g + r, column q) and of Q H0 (token 16 d + q,
-        // column 4 g + r); then its share of U, with the beta V term of k step ks = kh, for all four
-        // row blocks: U is linear in the key halves, whose shares meet through LDS
-        Frag hf[2];   // H0 fragments of this wave's key half: k step kc covers keys k0 + 32 kc .. (permuted)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) hf[kc] = O::from_f32(st[2 * kc], st[2 * kc + 1]);
-        f32x4 o1[4], uu[4];
-        {
-            Frag kf[4][2], qf[4][2];
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    kf[d][kc] = rt_frag(cK, 16 * d + q, 2 * kh + kc, g);
-                    qf[d][kc] = rt_frag(sQ, 16 * d + q, 2 * kh + kc, g);
+            // ---- (1) Mq sub-tiles (I, J), I >= J, ten over the eight waves (waves 0 and 1 take two);
+            //      lane (g, q): i = 16 I + q, j = 16 J + 4 g + r. Fragments are read in batches
+            //      ahead of their products (the fences keep the reads together).
+    #pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                if (n == 1 && wave >= 2) break;
+                const int code = n == 0 ? (int)((0x3130222120111000ull >> (8 * wave)) & 0xff) : 0x32 + wave;
+                const int I = code >> 4, J = code & 15;
+                Frag kf[4], qf[4];
+    #pragma unroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    kf[kc] = rt_frag(cK, 16 * J + q, kc, g);
+                    qf[kc] = rt_frag(sQ, 16 * I + q, kc, g);
                 }
-            lds_fence();
-            f32x4 pk[4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                pk[d] = f32x4{0, 0, 0, 0};
-                o1[d] = f32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    pk[d] = O::mma(pk[d], kf[d][kc], hf[kc]);
-                    o1[d] = O::mma(o1[d], hf[kc], qf[d][kc]);
-                }
-            }
-            // the right operand of T (.) for k step ks, in the token order of the accumulator
-            // layout (32 ks + 4 g + r in slots 0-3, 32 ks + 16 + 4 g + r in slots 4-7); T rows are
-            // read in the same order
-            Frag tf[4][2];
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= d / 2) tf[d][ks] = O::rowk_perm(sT + (16 * d + q) * kMPB + (32 * ks + 4 * g) * 2);
-            const Frag vf = O::tr(sV + (32 * kh + 4 * g + O::tr_row(q)) * kPX + (16 * vb + O::tr_col(q)) * 2, 16 * kPX);
-            f32x4 bg[2][2], be[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bg[ks][0] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 4 * g);
-                bg[ks][1] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 16 + 4 * g);
-            }
-            be[0] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * kh + 4 * g);
-            be[1] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * kh + 16 + 4 * g);
-            lds_fence();
-            f32x4 bv[2];   // beta V of k step kh (slots 0-3, 4-7)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t w = vf.w[r >> 1];
-                bv[0][r] = be[0][r] * ((r & 1) ? bf16_hi(w) : bf16_lo(w));
-                const uint32_t w2 = vf.w[2 + (r >> 1)];
-                bv[1][r] = be[1][r] * ((r & 1) ? bf16_hi(w2) : bf16_lo(w2));
-            }
-            Frag xf[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bool own = ks == kh;
-                f32x4 lo, hi;
-#pragma unroll
+                const int i = 16 * I + q;
+                const float gi = tG[i];
+                const f32x4 gj = *reinterpret_cast<const f32x4 *>(tG + 16 * J + 4 * g);
+                lds_fence();
+                f32x4 qk = {0, 0, 0, 0};
+    #pragma unroll
+                for (int kc = 0; kc < 4; ++kc) qk = O::mma(qk, kf[kc], qf[kc]);
+                float fq[4];
+    #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    lo[r] = (own ? bv[0][r] : 0.0f) - bg[ks][0][r] * pk[2 * ks][r];
-                    hi[r] = (own ? bv[1][r] : 0.0f) - bg[ks][1][r] * pk[2 * ks + 1][r];
+                    const float e = fast_exp2(fminf(gi - gj[r], 0.0f));
+                    fq[r] = (16 * J + 4 * g + r <= i) ? qk[r] * e : 0.0f;
                 }
-                xf[ks] = O::from_f32(lo, hi);
+                O::mstore4(sMq + i * kMPB + (16 * J + 4 * g) * 2, fq);
             }
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uu[d] = f32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= d / 2) uu[d] = O::mma(uu[d], tf[d][ks], xf[ks]);
+            // U = T (diag(beta) V - diag(beta gamma) K H0) (W = T diag(beta gamma) K is never formed):
+            // this wave's key half of K H0 (token 16 d + 4 g + r, column q) and of Q H0 (token 16 d + q,
+            // column 4 g + r); then its share of U, with the beta V term of k step ks = kh, for all four
+            // row blocks: U is linear in the key halves, whose shares meet through LDS
+            Frag hf[2];   // H0 fragments of this wave's key half: k step kc covers keys k0 + 32 kc .. (permuted)
+    #pragma unroll
+            for (int kc = 0; kc < 2; ++kc) hf[kc] = O::from_f32(st[2 * kc], st[2 * kc + 1]);
+            f32x4 o1[4], uu[4];
+            {
+                Frag kf[4][2], qf[4][2];
+    #pragma unroll
+                for (int d = 0; d < 4; ++d)
+    #pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) {
+                        kf[d][kc] = rt_frag(cK, 16 * d + q, 2 * kh + kc, g);
+                        qf[d][kc] = rt_frag(sQ, 16 * d + q, 2 * kh + kc, g);
+                    }
+                lds_fence();
+                f32x4 pk[4];
+    #pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    pk[d] = f32x4{0, 0, 0, 0};
+                    o1[d] = f32x4{0, 0, 0, 0};
+    #pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) {
+                        pk[d] = O::mma(pk[d], kf[d][kc], hf[kc]);
+                        o1[d] = O::mma(o1[d], hf[kc], qf[d][kc]);
+                    }
+                }
+                // the right operand of T (.) for k step ks, in the token order of the accumulator
+                // layout (32 ks + 4 g + r in slots 0-3, 32 ks + 16 + 4 g + r in slots 4-7); T rows are
+                // read in the same order
+                Frag tf[4][2];
+    #pragma unroll
+                for (int d = 0; d < 4; ++d)
+    #pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        if (ks <= d / 2) tf[d][ks] = O::rowk_perm(sT + (16 * d + q) * kMPB + (32 * ks + 4 * g) * 2);
+                const Frag vf = O::tr(sV + (32 * kh + 4 * g + O::tr_row(q)) * kPX + (16 * vb + O::tr_col(q)) * 2, 16 * kPX);
+                f32x4 bg[2][2], be[2];
+    #pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    bg[ks][0] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 4 * g);
+                    bg[ks][1] = *reinterpret_cast<const f32x4 *>(tBG + 32 * ks + 16 + 4 * g);
+                }
+                be[0] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * kh + 4 * g);
+                be[1] = *reinterpret_cast<const f32x4 *>(tBeta + 32 * kh + 16 + 4 * g);
+                lds_fence();
+                f32x4 bv[2];   // beta V of k step kh (slots 0-3, 4-7)
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t w = vf.w[r >> 1];
+                    bv[0][r] = be[0][r] * ((r & 1) ? bf16_hi(w) : bf16_lo(w));
+                    const uint32_t w2 = vf.w[2 + (r >> 1)];
+                    bv[1][r] = be[1][r] * ((r & 1) ? bf16_hi(w2) : bf16_lo(w2));
+                }
+                Frag xf[2];
+    #pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bool own = ks == kh;
+                    f32x4 lo, hi;
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        lo[r] = (own ? bv[0][r] : 0.0f) - bg[ks][0][r] * pk[2 * ks][r];
+                        hi[r] = (own ? bv[1][r] : 0.0f) - bg[ks][1][r] * pk[2 * ks + 1][r];
+                    }
+                    xf[ks] = O::from_f32(lo, hi);
+                }
+    #pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    uu[d] = f32x4{0, 0, 0, 0};
+    #pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        if (ks <= d / 2) uu[d] = O::mma(uu[d], tf[d][ks], xf[ks]);
+                }
             }
-        }
-        stage_load2(cn);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) xU[(wave * 4 + d) * 64 + lane] = uu[d];
-#pragma unroll
-        for (int dd = 0; dd < 2; ++dd) xO[(wave * 2 + dd) * 64 + lane] = kh ? o1[3 * dd] : o1[1 + dd];
-        lds_barrier();
-        const int partner = wave ^ 4;
-        {
-            // fragments of the remaining products, read in the token order of the U fragments
-            // (32 ks + 4 g + r in slots 0-3, 32 ks + 16 + 4 g + r in slots 4-7)
-            Frag mf[2][2], ktr[4][2];
-            f32x4 xu[4], xo[2], r0[2], r1[2];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) xu[d] = xU[(partner * 4 + d) * 64 + lane];
-#pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
-                xo[dd] = xO[(partner * 2 + dd) * 64 + lane];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    mf[dd][ks] = O::rowk_perm(sMq + (16 * (kh ? 1 + dd : 3 * dd) + q) * kMPB + (32 * ks + 4 * g) * 2);
+            stage_load2(cn);
+    #pragma unroll
+            for (int d = 0; d < 4; ++d) xU[(wave * 4 + d) * 64 + lane] = uu[d];
+    #pragma unroll
+            for (int dd = 0; dd < 2; ++dd) xO[(wave * 2 + dd) * 64 + lane] = kh ? o1[3 * dd] : o1[1 + dd];
+            lds_barrier();
+            const int partner = wave ^ 4;
+            {
+                // fragments of the remaining products, read in the token order of the U fragments
+                // (32 ks + 4 g + r in slots 0-3, 32 ks + 16 + 4 g + r in slots 4-7)
+                Frag mf[2][2], ktr[4][2];
+                f32x4 xu[4], xo[2], r0[2], r1[2];
+    #pragma unroll
+                for (int d = 0; d < 4; ++d) xu[d] = xU[(partner * 4 + d) * 64 + lane];
+    #pragma unroll
+                for (int dd = 0; dd < 2; ++dd) {
+                    xo[dd] = xO[(partner * 2 + dd) * 64 + lane];
+    #pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        mf[dd][ks] = O::rowk_perm(sMq + (16 * (kh ? 1 + dd : 3 * dd) + q) * kMPB + (32 * ks + 4 * g) * 2);
+                }
+    #pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    r0[ks] = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 4 * g);
+                    r1[ks] = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 16 + 4 * g);
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        ktr[u][ks] = O::tr(cK + rt_row(32 * ks + 4 * g) + O::tr_row(q) * kPB + rt_col(k0 + 16 * u + O::tr_col(q)),
+                                           2 * kGB);
+                }
+                const f32x4 gam = {tGam[16 * (kh ? 1 : 0) + q], tGam[16 * (kh ? 2 : 3) + q], 0.0f, 0.0f};
+                const float gl = tGam[63];
+                lds_fence();
+    #pragma unroll
+                for (int d = 0; d < 4; ++d) uu[d] += xu[d];
+                Frag uf[2], ru[2];
+    #pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    uf[ks] = O::from_f32(uu[2 * ks], uu[2 * ks + 1]);
+                    ru[ks] = O::from_f32(uu[2 * ks] * r0[ks], uu[2 * ks + 1] * r1[ks]);
+                }
+                // O rows of this key half (d = 0, 3 or 1, 2): O[token 16 d + q][column 4 g + r]
+                const __amdgpu_buffer_rsrc_t ro = rsrc(a.o + (t0 * H + h) * DV + vw, (int64_t)(Lc - 1) * vrow + 32);
+    #pragma unroll
+                for (int dd = 0; dd < 2; ++dd) {
+                    const int d = kh ? 1 + dd : 3 * dd;
+                    f32x4 o2 = {0, 0, 0, 0};
+    #pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        if (ks == 0 || dd == 1) o2 = O::mma(o2, uf[ks], mf[dd][ks]);
+                    const f32x4 oq = (kh ? o1[1 + dd] : o1[3 * dd]) + xo[dd];
+                    const float gi = gam[dd];
+                    // rows past the chunk fall outside the buffer range and are dropped
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2{pack_bf16(scale * fmaf(oq[0], gi, o2[0]), scale * fmaf(oq[1], gi, o2[1])),
+                              pack_bf16(scale * fmaf(oq[2], gi, o2[2]), scale * fmaf(oq[3], gi, o2[3]))},
+                        ro, (16 * d + q) * vrow + 8 * g, 0, 0);
+                }
+                // state update of this key half: st[u] = gamma_last st[u] + K^T (rho U)
+    #pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    st[u] *= gl;
+    #pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) st[u] = O::mma(st[u], ktr[u][ks], ru[ks]);
+                }
             }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                r0[ks] = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 4 * g);
-                r1[ks] = *reinterpret_cast<const f32x4 *>(tRho + 32 * ks + 16 + 4 * g);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    ktr[u][ks] = O::tr(cK + rt_row(32 * ks + 4 * g) + O::tr_row(q) * kPB + rt_col(k0 + 16 * u + O::tr_col(q)),
-                                       2 * kGB);
+            // the state after the chunk into its checkpoint slot
+            if (__builtin_amdgcn_readfirstlane(cur_dst) >= 0) {
+                if (__builtin_amdgcn_readfirstlane(cur_dst) >= a.capacity) {
+                    if (tid == 0) atomicOr(a.error_flag, SSD_DATA_BAD_SLOT);
+                } else {
+                    float *dst = a.chunk_states + ((int64_t)__builtin_amdgcn_readfirstlane(cur_dst) * H + h) * DV * DK +
+                                 (int64_t)(vw + q) * DK + k0;
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u + 4 * g) = st[u];
+                }
             }
-            const f32x4 gam = {tGam[16 * (kh ? 1 : 0) + q], tGam[16 * (kh ? 2 : 3) + q], 0.0f, 0.0f};
-            const float gl = tGam[63];
-            lds_fence();
-#pragma unroll
-            for (int d = 0; d < 4; ++d) uu[d] += xu[d];
-            Frag uf[2], ru[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                uf[ks] = O::from_f32(uu[2 * ks], uu[2 * ks + 1]);
-                ru[ks] = O::from_f32(uu[2 * ks] * r0[ks], uu[2 * ks + 1] * r1[ks]);
-            }
-            // O rows of this key half (d = 0, 3 or 1, 2): O[token 16 d + q][column 4 g + r]
-            const __amdgpu_buffer_rsrc_t ro = rsrc(a.o + (t0 * H + h) * DV + vw, (int64_t)(Lc - 1) * vrow + 32);
-#pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
-                const int d = kh ? 1 + dd : 3 * dd;
-                f32x4 o2 = {0, 0, 0, 0};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks == 0 || dd == 1) o2 = O::mma(o2, uf[ks], mf[dd][ks]);
-                const f32x4 oq = (kh ? o1[1 + dd] : o1[3 * dd]) + xo[dd];
-                const float gi = gam[dd];
-                // rows past the chunk fall outside the buffer range and are dropped
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{pack_bf16(scale * fmaf(oq[0], gi, o2[0]), scale * fmaf(oq[1], gi, o2[1])),
-                          pack_bf16(scale * fmaf(oq[2], gi, o2[2]), scale * fmaf(oq[3], gi, o2[3]))},
-                    ro, (16 * d + q) * vrow + 8 * g, 0, 0);
-            }
-            // state update of this key half: st[u] = gamma_last st[u] + K^T (rho U)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                st[u] *= gl;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) st[u] = O::mma(st[u], ktr[u][ks], ru[ks]);
-            }
-        }
-        // the state after the chunk into its checkpoint slot
-        if (__builtin_amdgcn_readfirstlane(cur_dst) >= 0) {
-            if (__builtin_amdgcn_readfirstlane(cur_dst) >= a.capacity) {
-                if (tid == 0) atomicOr(a.error_flag, SSD_DATA_BAD_SLOT);
-            } else {
-                float *dst = a.chunk_states + ((int64_t)__builtin_amdgcn_readfirstlane(cur_dst) * H + h) * DV * DK +
-                             (int64_t)(vw + q) * DK + k0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) *reinterpret_cast<f32x4 *>(dst + 16 * u + 4 * g) = st[u];
-            }
-        }
 
-        // ---- (3) the next chunk's K and tables into the other buffers, its Q, V and T over
-        //      this chunk's (no wave reads those past the first barrier); one barrier then
-        //      makes them visible and orders this chunk's Mq reads before the next chunk's writes
-        stage_store(cb ^ 1);
-        cur_dst = next_dst;
-        lds_barrier();
-    }
+            // ---- (3) the next chunk's K and tables into the other buffers, its Q, V and T over
+            //      this chunk's (no wave reads those past the first barrier); one barrier then
+            //      makes them visible and orders this chunk's Mq reads before the next chunk's writes
+            stage_store(cb ^ 1);
+            cur_dst = next_dst;
+            lds_barrier();
+        }
+    };
+    if (kh) walk(std::integral_constant<int, 1>{});
+    else walk(std::integral_constant<int, 0>{});
 
     float *fd = a.final_states + ((int64_t)(s * H + h) * DV + vw + q) * DK + k0;
 #pragma unroll
