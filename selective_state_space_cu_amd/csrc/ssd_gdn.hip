@@ -18,8 +18,8 @@
 // same map one token at a time.)
 //
 // Two kernels on one stream:
-//  ssd_gdn_prep_kernel, one workgroup per (chunk, value head), all in parallel
-//    (four workgroups per CU):
+//  ssd_gdn_prep_kernel, persistent workgroups (four per CU) over the (chunk,
+//    key head) items, whose value heads share the K K^T sub-tiles:
 //    A on the matrix cores (bf16 K K^T, masked by the decay, float32), T by
 //    forward substitution on the four 16 x 16 diagonal blocks and block merges
 //    on the float32 matrix cores
@@ -134,10 +134,11 @@ static_assert(kGdnWsBytes == kGdnChunk * kGdnChunk * 2, "workspace: one bf16 T p
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, lane * H * 4, 0, 0));
 }
 
-// The three A (or Mq) sub-tiles (I, J), I >= J, of wave w: ten over four waves,
-// the last two waves repeat their last sub-tile (identical writes)
-[[maybe_unused]] __device__ __forceinline__ int sub_tile(int wave, int n) {
-    const uint32_t codes = wave == 0 ? 0x333000u : wave == 1 ? 0x311110u : wave == 2 ? 0x212120u : 0x333222u;
+// The three sub-tiles (I, J), I >= J, of the lower triangle of a 64 x 64 matrix
+// that role r (0..3) computes: ten over four roles, roles 2 and 3 repeat their
+// last sub-tile (identical writes)
+[[maybe_unused]] __device__ __forceinline__ int sub_tile(int r, int n) {
+    const uint32_t codes = r == 0 ? 0x333000u : r == 1 ? 0x311110u : r == 2 ? 0x212120u : 0x333222u;
     return (codes >> (8 * n)) & 0xff;   // I in the high nibble, J in the low
 }
 
