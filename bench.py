@@ -25,7 +25,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
 DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_dual_anchor_256_counters.json")
 KERNEL_SOURCES = ["ssd_scan.hpp", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_internal.h",
-                  "ssd_scan_split.hpp", "ssd_scan_split_bf16.hip"]
+                  "ssd_scan_split.hpp", "ssd_scan_split_bf16.hip", "ssd_scan_ws.hpp", "ssd_scan_ws_bf16.hip"]
 DECODE_SOURCES = ["ssd_decode.hip", "ssd_scan.hpp", "ssd_internal.h"]
 CONV_COUNTERS = os.path.join(ROOT, "profiles", "conv1d_prefix_cache_4x8894_counters.json")
 CONV_SOURCES = ["ssd_conv1d.hip", "ssd_scan.hpp", "ssd_internal.h"]
@@ -92,11 +92,24 @@ def ingest_counters(fetch_csv, write_csv, config, calib_mib, workload="prefill",
 
 
 def scan_kernel_name(config):
-    """The scan kernel the library launches for a workload (see ssd_api.hip)."""
+    """The scan kernel the library launches for a workload (the choice of
+    ssd_chunk_scan_varlen in ssd_api.hip): bf16 with dstate 128 and headdim a
+    multiple of 64 takes the warp-specialised kernel when each workgroup walks
+    one head and chunks are at least one 64-token tile, else the split-state
+    kernel; every other shape the general kernel."""
     from selective_state_space_cu_amd.workloads import CONFIGS
     c = CONFIGS[config]
-    split = c["dtype"] == "bf16" and c["dstate"] == 128 and c["headdim"] % 64 == 0
-    return "ssd_scan_split_kernel" if split else "ssd_scan_kernel"
+    if not (c["dtype"] == "bf16" and c["dstate"] == 128 and c["headdim"] % 64 == 0):
+        return "ssd_scan_kernel"
+    S, H, G = len(c["lengths"]), c["nheads"], c["ngroups"]
+    blocks = S * H * (c["headdim"] // 64)
+    items = 1
+    if (S * G) % 8 == 0 and G % 8 == 0:   # pair mapping, several heads per workgroup when there are many
+        for k in (4, 2):
+            if (H // G) % k == 0 and blocks // k >= 2048:
+                items = k
+                break
+    return "ssd_scan_ws_kernel" if items == 1 and c["chunk_size"] >= 64 else "ssd_scan_split_kernel"
 
 
 def algorithmic_work(w, n_ckpt):

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libssd.so")
 SOURCES = ["ssd_api.hip", "ssd_meta.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip",
-           "ssd_scan_split_bf16.hip", "ssd_decode.hip", "ssd_conv1d.hip", "ssd_gdn.hip"]
+           "ssd_scan_split_bf16.hip", "ssd_scan_ws_bf16.hip", "ssd_decode.hip", "ssd_conv1d.hip", "ssd_gdn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # no packed-fp32 instructions anywhere in the device code

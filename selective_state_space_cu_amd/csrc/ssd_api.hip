@@ -101,7 +101,10 @@ ssd_status ssd_chunk_scan_varlen(const void *x, const float *dt, const float *dt
                     : 1;
     if (meta->nseqs == 0) return SSD_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = split ? ssd::launch_scan_split_bf16(a, dstate, s)
+    // the warp-specialised kernel walks 64-token tiles of one head per workgroup
+    const bool ws = split && a.items == 1 && meta->chunk_size >= 64;
+    const hipError_t e = ws ? ssd::launch_scan_ws_bf16(a, dstate, s)
+                         : split ? ssd::launch_scan_split_bf16(a, dstate, s)
                          : in_dtype == SSD_BF16 ? ssd::launch_scan_bf16(a, waves, dstate, s)
                                                 : ssd::launch_scan_f32(a, waves, dstate, s);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;

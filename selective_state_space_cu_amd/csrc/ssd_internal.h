@@ -66,6 +66,9 @@ hipError_t launch_scan_bf16(const ScanArgs &a, int waves, int dstate, hipStream_
 hipError_t launch_scan_f32(const ScanArgs &a, int waves, int dstate, hipStream_t stream);
 // Split-state bf16 scan (eight waves per 64 headdim columns; dstate 128).
 hipError_t launch_scan_split_bf16(const ScanArgs &a, int dstate, hipStream_t stream);
+// Warp-specialised bf16 scan (four chain and four helper waves per 64 headdim
+// columns; dstate 128, chunk_size >= 64, one head per workgroup).
+hipError_t launch_scan_ws_bf16(const ScanArgs &a, int dstate, hipStream_t stream);
 
 // Decode step with dual state anchors (one token per sequence).
 struct DecodeArgs {

@@ -49,55 +49,132 @@ def _vregs(line):
     return out
 
 
+def _untracked_bodies(asm_text):
+    """Per function: [(line, text, inside inline assembly)], labels as "name:"
+    entries; a text with no function symbols is read as one function."""
+    lines = asm_text.split("\n")
+    have = any(re.match(r"^(_Z\w+):", l) for l in lines)
+    out, name, body, in_asm = [], (None if have else "_text"), [], False
+    for i, l in enumerate(lines):
+        m = re.match(r"^(_Z\w+):", l)
+        if m:
+            name, body = m.group(1), []
+            continue
+        if name is None:
+            continue
+        if l.startswith(".Lfunc_end"):
+            out.append((name, body))
+            name = None
+            continue
+        t = l.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif t.startswith(";;#ASMEND"):
+            in_asm = False
+        elif re.match(r"^(\.LBB\d+_\d+):", t):
+            body.append((i + 1, t.split(":")[0] + ":", False))
+        elif t and not t.startswith(";") and not t.startswith("."):
+            body.append((i + 1, t, in_asm))
+    if name is not None and body:
+        out.append((name, body))
+    return out
+
+
+def _split_blocks(body):
+    """Basic blocks of a body of (line, text, ...) entries, and label -> block."""
+    blocks, cur, label_of = [], [], {}
+    for e in body:
+        t = e[1]
+        if t.endswith(":"):
+            if cur:
+                blocks.append(cur)
+            cur = []
+            label_of[t[:-1]] = len(blocks)
+            continue
+        cur.append(e)
+        if t.startswith("s_branch") or t.startswith("s_cbranch") or t.startswith("s_endpgm"):
+            blocks.append(cur)
+            cur = []
+    if cur:
+        blocks.append(cur)
+    return blocks, label_of
+
+
+def _ckey(st):
+    f, sv, c, v = st
+    return (f, sv, tuple(sorted(c.items())), v)
+
+
 def untracked_load_violations(asm_text):
     """(load line, path description) for every path that touches an untracked
     load's registers before its stage store or a vmcnt(0) wait; and the number
-    of untracked loads found (register loads inside inline-assembly blocks)."""
-    lines = asm_text.split("\n")
-    labels = {}
-    for i, l in enumerate(lines):
-        m = re.match(r"^(\.LBB\d+_\d+):", l)
-        if m:
-            labels[m.group(1)] = i
+    of untracked loads found (register loads inside inline-assembly blocks).
+
+    Paths follow the control-flow graph with the same scalar control state as
+    the stage-wait check (exec known full, SGPR flags known 0 or -1, vcc known
+    zero / non-zero), so edges that no wave can take -- the fall-through of a
+    branch on a constant flag that the structurizer emits where two
+    wave-uniform branches of a kernel join, or a loop exit through
+    s_cbranch_execnz with a full mask -- are not followed."""
     bad, count = [], 0
-    in_asm = False
-    for i, l in enumerate(lines):
-        s = l.strip()
-        # only loads written in inline assembly (the compiler tracks its own)
-        if s.startswith(";;#ASMSTART"):
-            in_asm = True
-        elif s.startswith(";;#ASMEND"):
-            in_asm = False
-        if not (in_asm and s.startswith("buffer_load_dwordx4") and " lds" not in s and " offen" in s):
+    for _, body in _untracked_bodies(asm_text):
+        blocks, label_of = _split_blocks(body)
+        if not blocks:
             continue
-        m = re.search(r"v\[(\d+):(\d+)\]", s)
-        a, b = int(m.group(1)), int(m.group(2))
-        dst, tag = set(range(a, b + 1)), f"v[{a}:{b}]"
-        count += 1
-        stack, seen = [i + 1], set()
-        while stack:
-            j = stack.pop()
-            while j < len(lines):
-                if j in seen:
-                    break
-                seen.add(j)
-                t = lines[j].strip()
-                j += 1
-                if not t or t.startswith(";") or t.startswith("."):
+        # control states reaching each block from the entry
+        st0 = (True, frozenset(), {}, None)
+        states = [dict() for _ in blocks]
+        states[0][_ckey(st0)] = st0
+        work = [(0, st0)]
+        while work:
+            bi, st = work.pop()
+            for e in blocks[bi]:
+                st = _exec_step(e[1], st)
+            for sb in _edges(blocks[bi][-1][1], bi, len(blocks), label_of, st):
+                k = _ckey(st)
+                if k not in states[sb]:
+                    states[sb][k] = st
+                    work.append((sb, st))
+        for bi, blk in enumerate(blocks):
+            for k, (ln, t, in_asm) in enumerate(blk):
+                if not (in_asm and t.startswith("buffer_load_dwordx4") and " lds" not in t and " offen" in t):
                     continue
-                if t.startswith("s_endpgm"):
-                    break
-                if t.startswith("s_waitcnt") and "vmcnt(0)" in t:
-                    break
-                if t.startswith("ds_write_b128") and tag in t:
-                    break
-                if _vregs(t) & dst:
-                    bad.append((i + 1, f"line {j}: {t}"))
-                    break
-                if t.startswith("s_branch"):
-                    j = labels[t.split()[-1]]
-                elif t.startswith("s_cbranch"):
-                    stack.append(labels[t.split()[-1]])
+                m = re.search(r"v\[(\d+):(\d+)\]", t)
+                a, b = int(m.group(1)), int(m.group(2))
+                dst, tag = set(range(a, b + 1)), f"v[{a}:{b}]"
+                count += 1
+                seen, stack = set(), []
+                for st in states[bi].values():
+                    for e in blk[:k + 1]:
+                        st = _exec_step(e[1], st)
+                    stack.append((bi, k + 1, st))
+                done = False
+                while stack and not done:
+                    cb, ci, st = stack.pop()
+                    key = (cb, ci, _ckey(st))
+                    if key in seen:
+                        continue
+                    seen.add(key)
+                    stopped = False
+                    for (ln2, t2, _) in blocks[cb][ci:]:
+                        if t2.startswith("s_endpgm"):
+                            stopped = True
+                            break
+                        if t2.startswith("s_waitcnt") and _vmcnt_of(t2) == 0:
+                            stopped = True
+                            break
+                        if t2.startswith("ds_write_b128") and tag in t2:
+                            stopped = True
+                            break
+                        if _vregs(t2) & dst:
+                            bad.append((ln, f"line {ln2}: {t2}"))
+                            stopped = done = True
+                            break
+                        st = _exec_step(t2, st)
+                    if stopped:
+                        continue
+                    for sb in _edges(blocks[cb][-1][1], cb, len(blocks), label_of, st):
+                        stack.append((sb, 0, st))
     return bad, count
 
 

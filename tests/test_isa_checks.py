@@ -19,8 +19,9 @@ pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipc
                                 reason="hipcc not available")
 
 
-def test_split_scan_untracked_x_loads():
-    bad, count = untracked_load_violations(kernel_asm("ssd_scan_split_bf16.hip"))
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_ws_bf16.hip"])
+def test_split_scan_untracked_x_loads(src):
+    bad, count = untracked_load_violations(kernel_asm(src))
     assert count >= 6, f"expected the prologue and per-step x loads, found {count}"
     assert not bad, "untracked load registers touched before their wait: " + "; ".join(
         f"load at line {ln}: {why}" for ln, why in bad[:5])
@@ -49,7 +50,26 @@ def test_checker_flags_a_reused_register():
     assert untracked_load_violations(ok) == ([], 1)
 
 
-@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip",
+def test_untracked_checker_follows_constant_flags():
+    """Where the structurizer joins two wave-uniform branches through a flag
+    that is a known constant, the branch it guards always goes one way: the
+    other edge is not a path. A flag of -1 takes the fall-through instead."""
+    def text(flag):
+        return "\n".join([
+            "\t;;#ASMSTART", "\tbuffer_load_dwordx4 v[4:7], v1, s[0:3], 0 offen offset:0", "\t;;#ASMEND",
+            f"\ts_mov_b64 s[10:11], {flag}",
+            "\ts_and_b64 vcc, exec, s[10:11]",
+            "\ts_cbranch_vccz .LBB0_9",
+            "\tv_mov_b32_e32 v5, 0",
+            ".LBB0_9:",
+            "\tds_write_b128 v9, v[4:7]",
+            "\ts_endpgm"])
+    assert untracked_load_violations(text(0)) == ([], 1)
+    bad, count = untracked_load_violations(text(-1))
+    assert count == 1 and len(bad) == 1
+
+
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_ws_bf16.hip", "ssd_scan_bf16.hip",
                                  "ssd_scan_f32.hip"])
 def test_m0_written_a_wait_state_before_lds_dma(src):
     bad, count = m0_lds_dma_hazards(kernel_asm(src))
@@ -65,7 +85,7 @@ def test_m0_checker_flags_a_planted_hazard():
     assert count == 2 and [b[0] for b in bad] == [2]
 
 
-@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip",
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_ws_bf16.hip", "ssd_scan_bf16.hip",
                                  "ssd_scan_f32.hip", "ssd_decode.hip", "ssd_meta.hip"])
 def test_valu_sgpr_write_five_wait_states_before_vmem(src):
     bad = valu_sgpr_vmem_hazards(kernel_asm(src))
@@ -83,7 +103,7 @@ def test_valu_sgpr_checker_flags_a_planted_hazard():
     assert [b[0] for b in bad] == [5]
 
 
-@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip",
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_ws_bf16.hip", "ssd_scan_bf16.hip",
                                  "ssd_scan_f32.hip"])
 def test_stage_waits_cover_their_loads(src):
     """Each `s_waitcnt vmcnt(n)` that releases a pipeline stage sees at least
@@ -154,7 +174,7 @@ def test_vmcnt_checker_paths_exports_and_structurizer_edges():
     assert len(bad) == 1
 
 
-@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip",
+@pytest.mark.parametrize("src", ["ssd_scan_split_bf16.hip", "ssd_scan_ws_bf16.hip", "ssd_scan_bf16.hip",
                                  "ssd_scan_f32.hip", "ssd_decode.hip", "ssd_meta.hip", "ssd_conv1d.hip"])
 def test_wide_store_data_not_overwritten_at_once(src):
     bad, count = store_data_hazards(kernel_asm(src))
@@ -178,7 +198,7 @@ def test_store_data_checker_flags_a_planted_hazard():
     assert count == 4 and [b[0] for b in bad] == [1, 3, 9]
 
 
-ALL_SOURCES = ["ssd_scan_split_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_decode.hip",
+ALL_SOURCES = ["ssd_scan_split_bf16.hip", "ssd_scan_ws_bf16.hip", "ssd_scan_bf16.hip", "ssd_scan_f32.hip", "ssd_decode.hip",
                "ssd_conv1d.hip", "ssd_gdn.hip", "ssd_meta.hip"]
 
 
