@@ -59,13 +59,18 @@
 // (64 tokens x 64 columns), 3 M tiles of 8192 (64 x 64 bf16), 3 x 1024 tables,
 // 4 x 2048 checkpoint staging, 768 scratch (prefetch and placeholder loads):
 // 160,256 in all (one workgroup per CU).
-// Layouts (16-byte chunks XOR-swizzled by row, conflict-free for the
-// accesses that dominate; each checked with a 64-bank model):
-//   C, B rows (256 bytes): chunk k of row r at k ^ fbc(r mod 16), fbc a bit
-//     permutation (r0, r1, r2 ^ r3, r2), so that both the 16-byte row reads and
-//     the transposed 8-byte reads of B (rows {0..3, 8..11} + 4 hi per read)
-//     hit distinct banks;
-//   X and M rows (128 bytes): chunk k of row r at k ^ swz(r), swz = (r2, r1, r3).
+// Layouts (16-byte chunks XOR-swizzled by row). The masks were chosen by
+// measurement on this chip (the LDS bank-conflict counter over each access
+// pattern of this kernel, replayed alone): a mask that spreads the 16 lanes of
+// a quarter-wave over all banks is not enough for 16-byte reads, which the
+// hardware serves in an order that also couples quarter-waves.
+//   C, B rows (256 bytes): chunk k of row r at k ^ fbc(r mod 16), fbc the
+//     row's four bits rotated by one, (r0 r1 r2 r3) -> (r3 r0 r1 r2): both the
+//     16-byte row reads and the transposed 8-byte reads of B run at the
+//     conflict-free rate (a plain k ^ r costs twice the cycles on the former);
+//   x and y rows (128 bytes): chunk k of row r at k ^ swz(r), swz = (r2, r1, r3);
+//   decay matrix rows (128 bytes): chunk k at k ^ (r mod 8) (its 16-byte
+//     row reads; its 8-byte writes conflict 2-way in every layout tried).
 //
 // Operand layouts on v_mfma_f32_16x16x32_bf16: lane l = 16 g + q supplies
 // row/column q and k slots 8 g .. 8 g + 7 of both operands; any assignment of k
@@ -115,8 +120,11 @@ struct WsShape {
     static constexpr int kXStores = 4, kXLoads = 4;
     static constexpr int kWaitX = 2 * (kXStores + kXLoads) + kXStores;
     static_assert(kWaitX <= 63, "vmcnt range");
-    __device__ static int fbc(int r) { return (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2) | (((r >> 2) & 1) << 3); }
+    // 16-byte chunk swizzles (XOR masks by row): C and B tiles (256-byte rows),
+    // x / y tiles and the decay matrix (128-byte rows)
+    __device__ static int fbc(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
     __device__ static int swz(int r) { return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
+    __device__ static int swm(int r) { return r & 7; }
 };
 static_assert(WsShape::bytes() <= kLdsLimit, "LDS plan");
 
@@ -141,18 +149,25 @@ __device__ __forceinline__ void ws_dma4(const u32x4 &r0, uint32_t lds_base, int 
     asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds ; ssd-stage %4"
                  :: "v"(voff), "s"(r), "s"(lds_base), "i"(OFF), "i"(STAGE) : "memory", "m0", "scc");
 }
-// (an untracked register load: see load16_untracked)
+// An untracked register load of x (see load16_untracked), non-temporal: x is
+// read once, and keeping it out of the caches' retained lines measured 5 %
+// faster on the prefix-cache workload.
 template <int STAGE>
 __device__ __forceinline__ void ws_load16_untracked(u32x4 &dst, const u32x4 &r0, int voff) {
     const u32x4 r = sgpr4(r0);
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2, 0 offen ; ssd-stage %3"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2, 0 offen nt ; ssd-stage %3"
                  : "=v"(dst) : "v"(voff), "s"(r), "i"(STAGE) : "memory");
 }
-// A 16-byte y store (non-temporal + sc1), through a resource of wave-uniform
-// words; s_nop 1 after it: see export_store16.
-__device__ __forceinline__ void ws_store16_nt(const u32x4 &v, const u32x4 &r0, int off) {
+// A 16-byte y store through a resource of wave-uniform words (s_nop 1 after
+// it: see export_store16). Plain write-back stores: in this kernel they timed
+// 3-5 % faster than non-temporal ones, for y and for the checkpoints.
+__device__ __forceinline__ void ws_store16(const u32x4 &v, const u32x4 &r0, int off) {
     const u32x4 r = sgpr4(r0);
-    asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %0, %1, %2, 0 offen nt sc1\n\ts_nop 1" :: "v"(v), "v"(off), "s"(r) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1" :: "v"(v), "v"(off), "s"(r) : "memory");
+}
+// A 16-byte checkpoint store (plain; see ws_store16 and export_store16)
+__device__ __forceinline__ void ws_export_store16(const u32x4 &v, const u32x4 &r, int off) {
+    asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen ; ssd-export\n\ts_nop 1" :: "v"(v), "v"(off), "s"(r) : "memory");
 }
 #pragma clang diagnostic pop
 
@@ -277,7 +292,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         //   M rows 16 I + q, chunk 4 ks + g (swizzled)
         uint32_t amr[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) amr[ks] = lds_addr(sM) + q * RX + 16 * ((4 * ks + g) ^ SH::swz(q));
+        for (int ks = 0; ks < 2; ++ks) amr[ks] = lds_addr(sM) + q * RX + 16 * ((4 * ks + g) ^ SH::swm(q));
         //   y rows 16 I + q, columns 16 cw + 4 g .. + 3 (8 bytes)
         const uint32_t ayw = lds_addr(sX) + q * RX + 16 * ((2 * cw + (g >> 1)) ^ SH::swz(q)) + 8 * (g & 1);
 #pragma unroll
@@ -314,7 +329,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 for (int k = 0; k < 2; ++k) {
                     const int i = 2 * k + (lane >> 5), kk = lane & 31;
                     const u32x4 v = *(const lds_u32x4 *)(uintptr_t)(e_base + e_pos(i, kk));
-                    export_store16_nt(v, re, ((4 * rnd + i) * N) * 4 + 16 * kk);
+                    ws_export_store16(v, re, ((4 * rnd + i) * N) * 4 + 16 * kk);
                 }
                 wave_lds_sync();
             }
@@ -466,7 +481,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         {
             const int i = 32 * (lane >> 5) + (lane & 15), J = 1 + 2 * (lane >> 5), half = (lane >> 4) & 1;
             if (hw < 3) {
-                const uint32_t p = lds_addr(sM) + hw * SH::kTileM + i * RX + 16 * ((2 * J + half) ^ SH::swz(i));
+                const uint32_t p = lds_addr(sM) + hw * SH::kTileM + i * RX + 16 * ((2 * J + half) ^ SH::swm(i));
                 *(lds_u32x4 *)(uintptr_t)p = u32x4{0, 0, 0, 0};
             }
         }
@@ -527,7 +542,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                     v[r] = d[r] * f;
                     if constexpr (I == J) v[r] += j == i ? Dh : 0.0f;
                 }
-                *(lds_u32x2 *)(uintptr_t)(amw + SLOT * SH::kTileM + 16 * RX * I + 16 * ((2 * J + (g >> 1)) ^ SH::swz(q))) =
+                *(lds_u32x2 *)(uintptr_t)(amw + SLOT * SH::kTileM + 16 * RX * I + 16 * ((2 * J + (g >> 1)) ^ SH::swm(q))) =
                     u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
             });
         };
@@ -661,7 +676,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const u32x4 v = *(const lds_u32x4 *)(uintptr_t)(ly[k] + SLOT * SH::kTileX);
-                    ws_store16_nt(v, r, yo[k]);
+                    ws_store16(v, r, yo[k]);
                 }
             };
             const u32x4 r_null = buf_rsrc(y_seq, 0);
