@@ -383,23 +383,35 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             for (int I = 0; I < 4; ++I) eic[I] = tab[64 + 16 * I + q];
             const float sL = tab[63];
 
-            // ---- inter term: Y^T = h_in^T . C^T, column i scaled by 2^(s_i)
+            // ---- inter term: Y^T = h_in^T . C^T, column i scaled by 2^(s_i), and
+            // the state update h = 2^(s_last) h + B^T (w o x). The C fragments are
+            // read before the first matrix op and the first k step's B^T fragments
+            // half-way through the inter term (scheduling barriers keep the
+            // compiler from sinking the reads to their uses, which serialises LDS
+            // latency into the chain).
+            Frag cf[4][4], bt0[8];
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) cf[I][c] = rf16(ac[c] + OS + 16 * RB * I);
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 acc[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) acc[I] = f32x4{0, 0, 0, 0};
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                Frag cf[4];
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) cf[c] = rf16(ac[c] + OS + 16 * RB * I);
-                acc[I] = f32x4{0, 0, 0, 0};
+                for (int I = 0; I < 4; ++I) acc[I] = O::mma(acc[I], hf[c], cf[I][c]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[I] = O::mma(acc[I], hf[c], cf[c]);
-            }
+            for (int u = 0; u < 8; ++u) bt0[u] = tr2(abt[u][0] + OS, abt[u][1] + OS);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int c = 2; c < 4; ++c)
+#pragma unroll
+                for (int I = 0; I < 4; ++I) acc[I] = O::mma(acc[I], hf[c], cf[I][c]);
             __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-            for (int I = 0; I < 4; ++I) acc[I] *= eic[I];
-
-            // ---- state update: h = 2^(s_last) h + B^T (w o x)
             Frag xw[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -412,17 +424,18 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             const float e = fast_exp2(sL);
 #pragma unroll
             for (int u = 0; u < 8; ++u) st[u] *= e;
+            Frag bt1[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) bt1[u] = tr2(abt[u][0] + OS + 32 * RB, abt[u][1] + OS + 32 * RB);
+            __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                Frag bt[8];
+            for (int u = 0; u < 8; ++u) st[u] = O::mma(st[u], bt0[u], xw[0]);
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    bt[u] = tr2(abt[u][0] + OS + 32 * RB * ks, abt[u][1] + OS + 32 * RB * ks);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) st[u] = O::mma(st[u], bt[u], xw[ks]);
-            }
+            for (int u = 0; u < 8; ++u) st[u] = O::mma(st[u], bt1[u], xw[1]);
             __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+            for (int I = 0; I < 4; ++I) acc[I] *= eic[I];
             make_hf();
 #pragma unroll
             for (int I = 0; I < 4; ++I) accp[I] = acc[I];
@@ -618,7 +631,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % 3, FETCH = (SLOT + 2) % 3;
                 fetch(std::integral_constant<int, FETCH>{});            // tile t + 2
                 compute(slot_c, t);
-                wait_vm_stage<SH::kBcPerStep, NEXT>();                      // stage t + 1 landed
+                wait_vm_stage<SH::kBcWait, NEXT>();                         // stage t + 1 landed
             };
             int t = 0;
             while (t < nt + 2) {
