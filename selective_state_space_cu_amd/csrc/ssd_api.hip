@@ -101,8 +101,9 @@ ssd_status ssd_chunk_scan_varlen(const void *x, const float *dt, const float *dt
                     : 1;
     if (meta->nseqs == 0) return SSD_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    // the warp-specialised kernel walks 64-token tiles of one head per workgroup
-    const bool ws = split && a.items == 1 && meta->chunk_size >= 64;
+    // the warp-specialised kernel walks 64-token tiles (chunk_size >= 64), of
+    // one head or of a.items heads per workgroup
+    const bool ws = split && meta->chunk_size >= 64;
     const hipError_t e = ws ? ssd::launch_scan_ws_bf16(a, dstate, s)
                          : split ? ssd::launch_scan_split_bf16(a, dstate, s)
                          : in_dtype == SSD_BF16 ? ssd::launch_scan_bf16(a, waves, dstate, s)

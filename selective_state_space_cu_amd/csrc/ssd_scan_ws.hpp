@@ -182,7 +182,17 @@ struct WsBlocks3 { static constexpr int n = 2; __device__ static constexpr int I
 // their decay-matrix blocks (launches without checkpoints: 2-5 % faster there)
 // instead of in one burst at the start of the step (launches that write
 // checkpoints: the interleaved order timed 4-9 % slower with them).
-template <int N, bool kInterleave>
+// kMulti: the workgroup walks a.items consecutive heads of one (sequence,
+// group) pair as one stream of a.items x nt tiles (stream index u = k nt + j:
+// head h0 + k, tile j). The heads share the sequence's B and C tiles, so the
+// C/B fetch restarts at the sequence's first tile with each head, while dt, x
+// and y follow the head, and the per-head constants (A, D, dt bias) are read
+// from lanes of a register by the head index. The pipeline runs on from one
+// head into the next; at a head's last tile the chain waves store its final
+// state and load the next head's initial state, whose bf16 operand of the
+// inter term is formed in the next step, after the intra term (the load's
+// latency overlaps the barrier and that work).
+template <int N, bool kInterleave, bool kMulti>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #if !defined(__HIP_DEVICE_COMPILE__)
@@ -214,7 +224,8 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
     if (__builtin_nontemporal_load(a.error_flag) & SSD_DATA_BAD_CU_SEQLENS) return;
     int rank, h, pt;
-    decode_block(a, blockIdx.x, rank, h, pt);
+    if constexpr (kMulti) decode_block_multi(a, blockIdx.x, rank, h, pt);   // h: the first head
+    else decode_block(a, blockIdx.x, rank, h, pt);
     const int s = a.seq_order[rank];
     if (s < 0 || s >= a.S) return;
     const int grp = h / (a.H / a.G);
@@ -231,6 +242,8 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
     const int browg = G * N * 2;              // bytes between tokens of B / C
     auto clamp_len = [](int rem) __attribute__((always_inline)) { return rem < 0 ? 0 : (rem > kTile ? kTile : rem); };
     const bool has_init = a.init != nullptr && (a.has_init == nullptr || a.has_init[s] != 0);
+    const int K = kMulti ? a.items : 1;   // heads walked
+    const int ntot = K * nt;              // tiles of the stream
 
     if (wave < 4) {
         // =====================================================================
@@ -244,6 +257,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #pragma unroll
         for (int u = 0; u < 8; ++u) st[u] = f32x4{0, 0, 0, 0};
         const int64_t state_row = ((int64_t)(s * H + h) * P + pw + q) * N;
+        const int64_t head_state = (int64_t)P * N;   // between consecutive heads' states
         if (has_init) {
             const float *src = a.init + state_row;
 #pragma unroll
@@ -253,6 +267,16 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         if (nt == 0) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4 *>(fd + n_of(u)) = st[u];
+            if constexpr (kMulti) {   // the other heads: final = initial state
+                for (int k = 1; k < K; ++k) {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        st[u] = has_init ? *reinterpret_cast<const f32x4 *>(a.init + state_row + k * head_state + n_of(u))
+                                         : f32x4{0, 0, 0, 0};
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4 *>(fd + k * head_state + n_of(u)) = st[u];
+                }
+            }
             return;
         }
 
@@ -314,6 +338,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             return (gc >= 0 && gc < a.max_chunks) ? (dstmap ? dstmap[gc] : gc) : -1;
         };
         int slots = a.chunk_states != nullptr ? load_slots(ex_win) : -1;
+        const int slots0 = slots;   // (multi-head: every head restarts at the sequence's first chunk)
         uint64_t ck_base = uni64((uint64_t)(uintptr_t)a.chunk_states + (uint64_t)((h * P + pw) * N) * 4);
         const uint64_t ck_slot = uni64((uint64_t)H * P * N * 4);
         //   staging: 4 state rows x 512 bytes; chunk k of row i at k ^ (k >> 4 | 2 i)
@@ -344,13 +369,14 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 #pragma unroll
         for (int I = 0; I < 4; ++I) accp[I] = f32x4{0, 0, 0, 0};
         xtp[0].w = xtp[1].w = u32x4{0, 0, 0, 0};
+        int jt = 0, kh = 0;   // (multi-head) tile of the step within its head, and the head
 
         auto step = [&](auto slot_c, int t) __attribute__((always_inline)) {
             constexpr int SLOT = decltype(slot_c)::value, PREV = (SLOT + 2) % 3;
             constexpr int OS = SLOT * SH::kTileBC, OX = SLOT * SH::kTileX, OXP = PREV * SH::kTileX,
                           OMP = PREV * SH::kTileM;
             const float *tab = tabs + SLOT * TAB;
-            if (t > 0 && t <= nt) {
+            if (t > 0 && t <= ntot) {
                 // ---- intra-chunk and D terms of tile t - 1: Y^T += x^T M^T
                 Frag mf[4][2];
 #pragma unroll
@@ -369,7 +395,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                     *(lds_u32x2 *)(uintptr_t)(ayw + OXP + 16 * RX * I) =
                         u32x2{pack_bf16(accp[I][0], accp[I][1]), pack_bf16(accp[I][2], accp[I][3])};
             }
-            if (t >= nt) return;
+            if (t >= ntot) return;
 
             // ---- x^T of tile t (A operand of the intra term, B operand of the state update)
             Frag xt[2];
@@ -398,6 +424,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) cf[I][c] = rf16(ac[c] + OS + 16 * RB * I);
+            if constexpr (kMulti) make_hf();   // (h_in may be a new head's initial state, loaded late in the last step)
             __builtin_amdgcn_sched_barrier(0);
             f32x4 acc[4];
 #pragma unroll
@@ -440,14 +467,14 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int I = 0; I < 4; ++I) acc[I] *= eic[I];
-            make_hf();
+            if constexpr (!kMulti) make_hf();
 #pragma unroll
             for (int I = 0; I < 4; ++I) accp[I] = acc[I];
             xtp[0] = xt[0];
             xtp[1] = xt[1];
 
             // ---- checkpoint of the state after tile t
-            if (t == ex_tile) {
+            if ((kMulti ? jt : t) == ex_tile) {
                 if (ex_chunk - ex_win >= 64) {   // next window (once per 64 checkpoints)
                     ex_win = ex_chunk;
                     slots = load_slots(ex_win);
@@ -462,22 +489,43 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 ex_tile = min(ex_tile + tpc, nt - 1);
                 if (dsl >= 0) export_state(dsl);
             }
+            if constexpr (kMulti) {
+                if (++jt == nt) {   // the head's last tile: its final state out, the next head's initial state in
+                    jt = 0;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4 *>(fd + n_of(u)) = st[u];
+                    if (++kh < K) {
+                        fd += head_state;
+                        ck_base += (uint64_t)head_state * 4;
+                        ex_tile = a.chunk_states != nullptr ? min(tpc, nt) - 1 : nt;
+                        ex_chunk = c0;
+                        ex_win = c0;
+                        slots = slots0;
+                        const float *src = a.init + state_row + kh * head_state;
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            st[u] = has_init ? *reinterpret_cast<const f32x4 *>(src + n_of(u)) : f32x4{0, 0, 0, 0};
+                    }
+                }
+            }
         };
 
         int t = 0;
-        while (t < nt + 2) {
+        while (t < ntot + 2) {
             lds_barrier();
             step(std::integral_constant<int, 0>{}, t);
-            if (++t >= nt + 2) break;
+            if (++t >= ntot + 2) break;
             lds_barrier();
             step(std::integral_constant<int, 1>{}, t);
-            if (++t >= nt + 2) break;
+            if (++t >= ntot + 2) break;
             lds_barrier();
             step(std::integral_constant<int, 2>{}, t);
             ++t;
         }
+        if constexpr (!kMulti) {   // (multi-head: stored at each head's last tile)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4 *>(fd + n_of(u)) = st[u];
+            for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4 *>(fd + n_of(u)) = st[u];
+        }
     } else {
         // =====================================================================
         // helper waves: hw 0, 1 (on the SIMDs of chain waves 0, 1) fetch the C
@@ -489,9 +537,38 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         const int hw = wave - 4;
         if (nt == 0) return;
         __builtin_assume(nt > 0 && nt < (1 << 24));   // (every step loop below runs nt + 2 > 2 times)
-        const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-        const float a2 = a.A[h] * kLog2e;
-        const float Dh = a.D ? a.D[h] : 0.0f;
+        __builtin_assume(ntot >= nt && ntot < (1 << 26));
+        float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+        float a2 = a.A[h] * kLog2e;
+        float Dh = a.D ? a.D[h] : 0.0f;
+        // (multi-head) lane k holds the constants of head h + k; the stream
+        // position (head, tile) of the step in us / ut
+        float bias_v = 0.0f, a2_v = 0.0f, d_v = 0.0f;
+        if constexpr (kMulti) {
+            if (lane < K) {
+                bias_v = a.dt_bias ? a.dt_bias[h + lane] : 0.0f;
+                a2_v = a.A[h + lane] * kLog2e;
+                d_v = a.D ? a.D[h + lane] : 0.0f;
+            }
+        }
+        int us = 0, ut = 0;
+        // the tile after stream position (k, j)
+        auto next_pos = [&](int &k, int &j) __attribute__((always_inline)) {
+            const bool w = j + 1 == nt;
+            j = w ? 0 : j + 1;
+            k = w ? k + 1 : k;
+        };
+        // constants for the step's work: the tables of the next tile (its head's
+        // A and dt bias) and the decay matrix of this tile (its head's D)
+        auto step_consts = [&]() __attribute__((always_inline)) {
+            if constexpr (kMulti) {
+                const int kn = (ut + 1 == nt) ? us + 1 : us;
+                const int kc = kn < K ? kn : K - 1;
+                bias = readlane(bias_v, kc);
+                a2 = readlane(a2_v, kc);
+                Dh = readlane(d_v, us < K ? us : K - 1);
+            }
+        };
 
         // zero the blocks above the diagonal that the intra term reads (M rows
         // 0..15 x columns 16..31 and rows 32..47 x columns 48..63), all buffers
@@ -567,11 +644,12 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         // (from the dt that rode with stage t) and this helper's blocks of M_t
         auto compute = [&](auto slot_c, int t) __attribute__((always_inline)) {
             constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % 3;
-            if (t + 1 < nt) {   // tables of tile t + 1
-                const int Ln = clamp_len(L - (t + 1) * kTile);
+            if (t + 1 < ntot) {   // tables of tile t + 1
+                const int jn = kMulti ? ((ut + 1 == nt) ? 0 : ut + 1) : t + 1;
+                const int Ln = clamp_len(L - jn * kTile);
                 tables(tabs + NEXT * TAB, softplus_hw(sDt[SLOT * 64 + lane] + bias + (lane < Ln ? 0.0f : -INFINITY)));
             }
-            if (t < nt) {       // decay matrix of tile t
+            if (t < ntot) {     // decay matrix of tile t
                 if (hw == 0) mblocks(slot_c, WsBlocks0{});
                 else if (hw == 1) mblocks(slot_c, WsBlocks1{});
                 else if (hw == 2) mblocks(slot_c, WsBlocks2{});
@@ -627,8 +705,9 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         using B2c = std::integral_constant<int, 2>;
         auto next_tables = [&](auto slot_c, int t) __attribute__((always_inline)) {   // tables of tile t + 1
             constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % 3;
-            if (t + 1 < nt) {
-                const int Ln = clamp_len(L - (t + 1) * kTile);
+            if (t + 1 < ntot) {
+                const int jn = kMulti ? ((ut + 1 == nt) ? 0 : ut + 1) : t + 1;
+                const int Ln = clamp_len(L - jn * kTile);
                 tables(tabs + NEXT * TAB, softplus_hw(sDt[SLOT * 64 + lane] + bias + (lane < Ln ? 0.0f : -INFINITY)));
             }
         };
@@ -662,36 +741,77 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 r.x = (uint32_t)v;
                 r.y = (uint32_t)(v >> 32);
             };
-            const int pk = (h % (H / G)) * a.nptiles + pt;   // this workgroup's share of the prefetch
-            const int go_pf = (lane < 8 && pk < 16) ? (4 * pk + (lane >> 1)) * browg + 128 * (lane & 1) : kOob;
+            int go_pf;
+            if constexpr (kMulti) {   // H / G / K x nptiles workgroups share a tile: 64 / that rows each (at least 4)
+                const int nsh = (H / G / K) * a.nptiles, rps = nsh >= 16 ? 4 : 64 / nsh;
+                const int pk = ((h % (H / G)) / K) * a.nptiles + pt;
+                go_pf = (lane < 2 * rps && rps * pk < 64) ? (rps * pk + (lane >> 1)) * browg + 128 * (lane & 1) : kOob;
+            } else {
+                const int pk = (h % (H / G)) * a.nptiles + pt;   // this workgroup's share of the prefetch
+                go_pf = (lane < 8 && pk < 16) ? (4 * pk + (lane >> 1)) * browg + 128 * (lane & 1) : kOob;
+            }
             const uint32_t lds_pfz = rfl(lds_addr(sDtNull) + 256 * hw);
+            // (multi-head) stream position of the tile being fetched, and the
+            // resources of that fetch: the sequence's C/B rows of its tile, the
+            // dt of the tile after (its head's column), and the L2 prefetch
+            // (during the first head only: the later heads find the tiles in L2)
+            int kf = 0, jf = 0;
+            u32x4 r_pfm = r_t;
+            auto multi_rsrc = [&]() __attribute__((always_inline)) {
+                const uint64_t t_base = (uint64_t)(uintptr_t)src + (uint64_t)((tb * G + grp) * N) * 2;
+                const uint64_t d_base = (uint64_t)(uintptr_t)a.dt + (uint64_t)(tb * H + h) * 4;
+                r_t = buf_rsrc(uni64(t_base + (uint64_t)jf * step_bc), kf < K ? clamp_len(L - jf * kTile) * browg : 0);
+                int kd = kf, jd = jf;
+                next_pos(kd, jd);
+                r_d = buf_rsrc(uni64(d_base + ((uint64_t)jd * kTile * H + kd) * 4),
+                               (hw == 0 && kd < K) ? clamp_len(L - jd * kTile) * H * 4 : 0);
+                const int jp = jf + SH::kPf;
+                r_pfm = buf_rsrc(uni64(t_base + (uint64_t)jp * step_bc),
+                                 (kf == 0 && jp < nt) ? clamp_len(L - jp * kTile) * browg : 0);
+            };
             auto fetch = [&](auto slot_c) __attribute__((always_inline)) {
                 constexpr int SLOT = decltype(slot_c)::value;
-                r_t.z = (uint32_t)(clamp_len(f_rem) * browg);
-                r_d.z = hw == 0 ? (uint32_t)(clamp_len(f_rem - kTile) * H * 4) : 0u;
+                if constexpr (kMulti) {
+                    multi_rsrc();
+                } else {
+                    r_t.z = (uint32_t)(clamp_len(f_rem) * browg);
+                    r_d.z = hw == 0 ? (uint32_t)(clamp_len(f_rem - kTile) * H * 4) : 0u;
+                }
                 static_for<16>([&](auto b_c) {
                     constexpr int Bk = decltype(b_c)::value;
                     ws_dma16<SLOT * SH::kTileBC + 1024 * Bk, SLOT>(r_t, lds_t, go[Bk]);
                 });
                 ws_dma4<SLOT * 256, SLOT>(r_d, lds_dt, go_d);
-                u32x4 r_pf = r_t;
-                advance(r_pf, SH::kPf * step_bc);
-                r_pf.z = (uint32_t)(clamp_len(f_rem - SH::kPf * kTile) * browg);
-                ws_dma4<0, 9>(r_pf, lds_pfz, go_pf);
-                advance(r_t, step_bc); advance(r_d, step_d);
-                f_rem -= kTile;
+                if constexpr (kMulti) {
+                    ws_dma4<0, 9>(r_pfm, lds_pfz, go_pf);
+                    next_pos(kf, jf);
+                } else {
+                    u32x4 r_pf = r_t;
+                    advance(r_pf, SH::kPf * step_bc);
+                    r_pf.z = (uint32_t)(clamp_len(f_rem - SH::kPf * kTile) * browg);
+                    ws_dma4<0, 9>(r_pf, lds_pfz, go_pf);
+                    advance(r_t, step_bc); advance(r_d, step_d);
+                    f_rem -= kTile;
+                }
             };
             // the same fetch in three parts (blocks 0-5, 6-11, 12-15 with dt and
             // the prefetch), placed between the decay-matrix blocks' math
             auto fetch_part = [&](auto slot_c, auto part_c) __attribute__((always_inline)) {
                 constexpr int SLOT = decltype(slot_c)::value, PART = decltype(part_c)::value;
                 constexpr int B0 = PART * 6, B1 = PART == 2 ? 16 : B0 + 6;
-                if constexpr (PART == 0) r_t.z = (uint32_t)(clamp_len(f_rem) * browg);
+                if constexpr (PART == 0) {
+                    if constexpr (kMulti) multi_rsrc();
+                    else r_t.z = (uint32_t)(clamp_len(f_rem) * browg);
+                }
                 static_for<B1 - B0>([&](auto b_c) {
                     constexpr int Bk = B0 + decltype(b_c)::value;
                     ws_dma16<SLOT * SH::kTileBC + 1024 * Bk, SLOT>(r_t, lds_t, go[Bk]);
                 });
-                if constexpr (PART == 2) {
+                if constexpr (PART == 2 && kMulti) {
+                    ws_dma4<SLOT * 256, SLOT>(r_d, lds_dt, go_d);
+                    ws_dma4<0, 9>(r_pfm, lds_pfz, go_pf);
+                    next_pos(kf, jf);
+                } else if constexpr (PART == 2) {
                     r_d.z = hw == 0 ? (uint32_t)(clamp_len(f_rem - kTile) * H * 4) : 0u;
                     ws_dma4<SLOT * 256, SLOT>(r_d, lds_dt, go_d);
                     u32x4 r_pf = r_t;
@@ -725,6 +845,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             };
             auto step = [&](auto slot_c, int t) __attribute__((always_inline)) {
                 constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % 3, FETCH = (SLOT + 2) % 3;
+                step_consts();
                 if constexpr (kInterleave) {
                     if (hw == 0) step_blocks(slot_c, WsBlocks0{});
                     else step_blocks(slot_c, WsBlocks1{});
@@ -734,15 +855,16 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                     compute(slot_c, t);
                 }
                 wait_vm_stage<SH::kBcWait, NEXT>();                         // stage t + 1 landed
+                if constexpr (kMulti) next_pos(us, ut);
             };
             int t = 0;
-            while (t < nt + 2) {
+            while (t < ntot + 2) {
                 lds_barrier();
                 step(std::integral_constant<int, 0>{}, t);
-                if (++t >= nt + 2) break;
+                if (++t >= ntot + 2) break;
                 lds_barrier();
                 step(std::integral_constant<int, 1>{}, t);
-                if (++t >= nt + 2) break;
+                if (++t >= ntot + 2) break;
                 lds_barrier();
                 step(std::integral_constant<int, 2>{}, t);
                 ++t;
@@ -777,17 +899,41 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             __builtin_amdgcn_s_waitcnt(WaitVm<0>::imm);   // nothing outstanding before the pipeline starts
             u32x4 xr[3][4];
             int xg_t = 1;
+            // (multi-head) stream positions of the next x tile to load and of the
+            // next y tile to store; advanced with selects only (no control flow
+            // may separate an untracked load from its wait)
+            int kx = 0, jx = 0, ky = 0, jy = 0;
+            if constexpr (kMulti) next_pos(kx, jx);   // tile 1
+            const uint32_t head_x = (uint32_t)(P * 2);   // bytes between consecutive heads' columns
             auto xload = [&](auto set_c) __attribute__((always_inline)) {   // x of tile xg_t into register set SET
                 constexpr int SET = decltype(set_c)::value;
-                const u32x4 r = buf_rsrc(x_seq + (uint64_t)xg_t * step_x, clamp_len(L - xg_t * kTile) * xrow);
+                if constexpr (kMulti) {
+                    const u32x4 r = buf_rsrc(x_seq + (uint64_t)kx * head_x + (uint64_t)jx * step_x,
+                                             kx < K ? clamp_len(L - jx * kTile) * xrow : 0);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) ws_load16_untracked<3 + SET>(xr[SET][k], r, go_x[k]);
+                    for (int k = 0; k < 4; ++k) ws_load16_untracked<3 + SET>(xr[SET][k], r, go_x[k]);
+                    next_pos(kx, jx);
+                } else {
+                    const u32x4 r = buf_rsrc(x_seq + (uint64_t)xg_t * step_x, clamp_len(L - xg_t * kTile) * xrow);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) ws_load16_untracked<3 + SET>(xr[SET][k], r, go_x[k]);
+                }
                 ++xg_t;
             };
             auto ystore = [&](auto slot_c, int yt) __attribute__((always_inline)) {   // y of tile yt from X[SLOT] (zero-sized range if no tile)
                 constexpr int SLOT = decltype(slot_c)::value;
-                const int len = (yt >= 0 && yt < nt) ? clamp_len(L - yt * kTile) : 0;
-                const u32x4 r = buf_rsrc(y_seq + (uint64_t)(yt < 0 ? 0 : yt) * step_x, len * xrow);
+                u32x4 r;
+                if constexpr (kMulti) {
+                    const int len = (yt >= 0 && yt < ntot) ? clamp_len(L - jy * kTile) : 0;
+                    r = buf_rsrc(y_seq + (uint64_t)ky * head_x + (uint64_t)jy * step_x, len * xrow);
+                    int k2 = ky, j2 = jy;
+                    next_pos(k2, j2);
+                    ky = yt >= 0 ? k2 : ky;
+                    jy = yt >= 0 ? j2 : jy;
+                } else {
+                    const int len = (yt >= 0 && yt < nt) ? clamp_len(L - yt * kTile) : 0;
+                    r = buf_rsrc(y_seq + (uint64_t)(yt < 0 ? 0 : yt) * step_x, len * xrow);
+                }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const u32x4 v = *(const lds_u32x4 *)(uintptr_t)(ly[k] + SLOT * SH::kTileX);
@@ -805,6 +951,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
             auto step = [&](auto slot_c, int t) __attribute__((always_inline)) {
                 constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % 3;
+                step_consts();
                 ystore(std::integral_constant<int, NEXT>{}, t - 2);    // y of tile t - 2 (in X[t + 1])
                 wait_vm_stage<SH::kWaitX, 3 + NEXT>();                  // x of tile t + 1
 #pragma unroll
@@ -813,9 +960,11 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                     *(lds_u32x4 *)(uintptr_t)(lx[k] + NEXT * SH::kTileX) = xr[NEXT][k];
                 }
                 xload(std::integral_constant<int, NEXT>{});             // tile t + 4
-                if constexpr (kInterleave) {
+                // (the multi-head instances always take this form: with the
+                // four-way block choice of compute() the compiler fails on them)
+                if constexpr (kInterleave || kMulti) {
                     next_tables(slot_c, t);
-                    if (t < nt) {   // this helper's blocks of M_t, one at a time
+                    if (t < ntot) {   // this helper's blocks of M_t, one at a time
                         Frag cf[3][4], bf[3][4];
                         if (hw == 2) {
                             mread(slot_c, WsBlocks2{}, B0c{}, cf, bf); mmath(slot_c, WsBlocks2{}, B0c{}, cf, bf);
@@ -828,15 +977,16 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 } else {
                     compute(slot_c, t);
                 }
+                if constexpr (kMulti) next_pos(us, ut);
             };
             int t = 0;
-            while (t < nt + 2) {
+            while (t < ntot + 2) {
                 lds_barrier();
                 step(std::integral_constant<int, 0>{}, t);
-                if (++t >= nt + 2) break;
+                if (++t >= ntot + 2) break;
                 lds_barrier();
                 step(std::integral_constant<int, 1>{}, t);
-                if (++t >= nt + 2) break;
+                if (++t >= ntot + 2) break;
                 lds_barrier();
                 step(std::integral_constant<int, 2>{}, t);
                 ++t;
@@ -850,14 +1000,17 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
 template <int N>
 hipError_t launch_scan_ws_instance(const ScanArgs &a, hipStream_t stream) {
-    const int64_t blocks = (int64_t)a.S * a.H * a.nptiles;
+    const int64_t blocks = (int64_t)a.S * a.H * a.nptiles / a.items;
     if (blocks == 0) return hipSuccess;
-    if (a.chunk_states != nullptr)
-        hipLaunchKernelGGL((ssd_scan_ws_kernel<N, false>), dim3((unsigned)blocks), dim3(WsShape::kThreads), 0, stream,
-                           a, a.chunk_state_dst);
-    else
-        hipLaunchKernelGGL((ssd_scan_ws_kernel<N, true>), dim3((unsigned)blocks), dim3(WsShape::kThreads), 0, stream,
-                           a, a.chunk_state_dst);
+    const dim3 grid((unsigned)blocks), wg(WsShape::kThreads);
+    const bool ex = a.chunk_states != nullptr;
+    if (a.items > 1) {
+        if (ex) hipLaunchKernelGGL((ssd_scan_ws_kernel<N, false, true>), grid, wg, 0, stream, a, a.chunk_state_dst);
+        else hipLaunchKernelGGL((ssd_scan_ws_kernel<N, true, true>), grid, wg, 0, stream, a, a.chunk_state_dst);
+    } else {
+        if (ex) hipLaunchKernelGGL((ssd_scan_ws_kernel<N, false, false>), grid, wg, 0, stream, a, a.chunk_state_dst);
+        else hipLaunchKernelGGL((ssd_scan_ws_kernel<N, true, false>), grid, wg, 0, stream, a, a.chunk_state_dst);
+    }
     return hipGetLastError();
 }
 
