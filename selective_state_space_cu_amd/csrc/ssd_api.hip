@@ -96,14 +96,14 @@ ssd_status ssd_chunk_scan_varlen(const void *x, const float *dt, const float *dt
     const bool split = in_dtype == SSD_BF16 && dstate == 128 && headdim % 64 == 0;
     a.nptiles = headdim / (16 * waves);
     a.xcd_mode = ssd::xcd_mode_for(meta->nseqs, nheads, ngroups, a.nptiles);
-    a.items = split ? ssd::split_items_for(a.xcd_mode, (int64_t)meta->nseqs * nheads * a.nptiles,
-                                           nheads / ngroups)
-                    : 1;
-    if (meta->nseqs == 0) return SSD_OK;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
     // the warp-specialised kernel walks 64-token tiles (chunk_size >= 64), of
     // one head or of a.items heads per workgroup
     const bool ws = split && meta->chunk_size >= 64;
+    const int64_t wgs = (int64_t)meta->nseqs * nheads * a.nptiles;
+    a.items = ws ? ssd::ws_items_for(a.xcd_mode, wgs, nheads / ngroups)
+                 : split ? ssd::split_items_for(a.xcd_mode, wgs, nheads / ngroups) : 1;
+    if (meta->nseqs == 0) return SSD_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = ws ? ssd::launch_scan_ws_bf16(a, dstate, s)
                          : split ? ssd::launch_scan_split_bf16(a, dstate, s)
                          : in_dtype == SSD_BF16 ? ssd::launch_scan_bf16(a, waves, dstate, s)

@@ -332,15 +332,23 @@ def test_no_sequences():
     assert y.shape[0] == 0 and fin.shape[0] == 0 and int(meta.nchunks.item()) == 0
 
 
-@pytest.mark.parametrize("S,seed", [(64, 21), (32, 22)], ids=["4-heads-per-workgroup", "2-heads-per-workgroup"])
-def test_multi_head_workgroups(S, seed):
-    """Many short sequences with G a multiple of 8: each workgroup walks 4 (S = 64) or
-    2 (S = 32) consecutive heads of one (sequence, group) as one tile stream. Lengths
+# (S, chunk size, seed): with 128 heads in 8 groups, the warp-specialised
+# kernel (chunk >= 64) walks 8 (S = 64), 4 (S = 32) or 2 (S = 16) heads per
+# workgroup, the split-state kernel (chunk 32) 4 (S = 64) or 2 (S = 32)
+MULTI_HEAD = [(64, 64, 21), (32, 64, 22), (16, 64, 23), (64, 32, 24), (32, 32, 25)]
+
+
+@pytest.mark.parametrize("export", [True, False], ids=["export", "no-export"])
+@pytest.mark.parametrize("S,cs,seed", MULTI_HEAD, ids=lambda v: str(v))
+def test_multi_head_workgroups(S, cs, seed, export):
+    """Many short sequences with G a multiple of 8: each workgroup walks several
+    consecutive heads of one (sequence, group) as one tile stream. Lengths
     include empty, one-token and tile-boundary cases; initial states on most
-    sequences; every chunk state exported."""
+    sequences; every chunk state exported (or none: the kernel instance without
+    the export)."""
     rng = np.random.default_rng(seed)
     L = [int(v) for v in rng.integers(1, 200, size=S)]
     L[:6] = [0, 1, 63, 64, 65, 129]
-    w = make_inputs(L, 128, 64, 128, 8, 64, dtype="bf16", init_seqs=[i for i in range(S) if i % 5],
+    w = make_inputs(L, 128, 64, 128, 8, cs, dtype="bf16", init_seqs=[i for i in range(S) if i % 5],
                     seed=seed)
-    _full_compare(w, what=f"multi-head S={S}")
+    _full_compare(w, dense=export, what=f"multi-head S={S} cs={cs} export={export}")
