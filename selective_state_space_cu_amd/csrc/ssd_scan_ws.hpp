@@ -370,6 +370,14 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         for (int I = 0; I < 4; ++I) accp[I] = f32x4{0, 0, 0, 0};
         xtp[0].w = xtp[1].w = u32x4{0, 0, 0, 0};
         int jt = 0, kh = 0;   // (multi-head) tile of the step within its head, and the head
+        // (multi-head) an L2 prefetch of the next head's initial state two tiles
+        // before the hand-over (or at the start of a one-tile head's step): one
+        // 4-byte direct load per 128-byte line of the wave's 16 state rows,
+        // into a scratch LDS area that no one reads. The register load at the
+        // hand-over then waits for L2, not HBM.
+        const uint32_t lds_pfc = __builtin_amdgcn_readfirstlane(lds_addr(sDtNull));
+        const int go_pfc = (lane >> 2) * N * 4 + 128 * (lane & 3);
+        const int64_t wave_state = ((int64_t)(s * H + h) * P + pw) * N;
 
         auto step = [&](auto slot_c, int t) __attribute__((always_inline)) {
             constexpr int SLOT = decltype(slot_c)::value, PREV = (SLOT + 2) % 3;
@@ -396,6 +404,12 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                         u32x2{pack_bf16(accp[I][0], accp[I][1]), pack_bf16(accp[I][2], accp[I][3])};
             }
             if (t >= ntot) return;
+            if constexpr (kMulti) {
+                if (has_init && kh + 1 < K && jt == (nt >= 2 ? nt - 2 : 0)) {
+                    const u32x4 rp = buf_rsrc(uni64((uint64_t)(uintptr_t)(a.init + wave_state + (kh + 1) * head_state)), 16 * N * 4);
+                    ws_dma4<0, 9>(rp, lds_pfc, go_pfc);
+                }
+            }
 
             // ---- x^T of tile t (A operand of the intra term, B operand of the state update)
             Frag xt[2];
