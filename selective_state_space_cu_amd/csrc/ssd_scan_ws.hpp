@@ -45,7 +45,9 @@
 //           x_t^T from X[t]; inter term of tile t from C_t (stage t) and h_{t-1};
 //           state update from B_t (stage t), x_t and the tables of tile t;
 //           checkpoint of h_t when tile t ends a chunk.
-//   helper: C/B of tile t+2 (+ dt of tile t+3) -> stage t+2 (direct loads),
+//   helper: C/B of tile t+2 (+ dt of tile t+3) -> stage t+2 (direct loads;
+//           in one burst at the start of the step in launches that write
+//           checkpoints, else in three parts between the M blocks below),
 //           then wait for stage t+1 (helpers 4, 5);
 //           y_{t-2} from X[t+1] -> HBM, then x_{t+1} (registers) -> X[t+1];
 //           x of tile t+4 -> registers (helpers 6, 7);
@@ -57,7 +59,7 @@
 //
 // LDS (bytes): 3 stages x (C 16384 + B 16384), 3 x 256 dt, 3 X tiles of 8192
 // (64 tokens x 64 columns), 3 M tiles of 8192 (64 x 64 bf16), 3 x 1024 tables,
-// 4 x 2048 checkpoint staging, 768 scratch (prefetch and placeholder loads):
+// 4 x 2048 checkpoint staging, 768 scratch (prefetch targets and the empty dt loads):
 // 160,256 in all (one workgroup per CU).
 // Layouts (16-byte chunks XOR-swizzled by row). The masks were chosen by
 // measurement on this chip (the LDS bank-conflict counter over each access
@@ -103,15 +105,16 @@ struct WsShape {
         return 6 * kTileBC + 3 * 256 + 3 * kTileX + 3 * kTileM + 3 * kTab * 4 + 4 * kStageE + 3 * 256;
     }
     // C/B helper: vector memory instructions per step (16 direct 1 KB loads of
-    // its tile and one of dt); its wait for the stage fetched one step earlier
-    // sees exactly one step's instructions after that stage's last load
+    // its tile, one of dt, then the L2 prefetch below); its wait for the stage
+    // fetched one step earlier sees that step's prefetch and one whole step
+    // after the stage's last load: kBcWait
     static constexpr int kBcPerStep = 18;
     // L2 prefetch of tile f + kPf while tile f is fetched, spread over the
     // workgroups that read the same C and B tiles (the heads of one group and
     // their headdim tiles, up to 16): each touches 4 rows (8 lines) of its
     // helper's tile with one 4-byte direct load into a scratch area, after the
-    // stage loads, so the wait for a stage also sees the prefetch of the step
-    // that issued it
+    // stage loads (in the several-heads instances with more rows per
+    // workgroup, during the first head only)
     static constexpr int kPf = 4;
     static constexpr int kBcWait = kBcPerStep + 1;
     // x helper: per step 4 y stores, then (after the wait) 4 register loads of
@@ -728,8 +731,9 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
 
         if (hw < 2) {
             // ---- C/B helper: hw 0 fetches the C tiles, hw 1 the B tiles (16
-            // direct 1 KB loads each), both the dt of the tile after (the same
-            // bytes to the same place): 17 vector memory instructions per step.
+            // direct 1 KB loads each), hw 0 also the dt of the tile after (hw 1
+            // an empty load in its place), and each one 4-byte L2 prefetch:
+            // 18 vector memory instructions per step.
             // Block b of a tile: lane l -> row 4 b + l / 16, LDS chunk l mod 16
             // <- global chunk (l mod 16) ^ fbc(row)
             int go[16];
