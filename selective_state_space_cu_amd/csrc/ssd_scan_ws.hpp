@@ -51,7 +51,8 @@
 //           then wait for stage t+1 (helpers 4, 5);
 //           y_{t-2} from X[t+1] -> HBM, then x_{t+1} (registers) -> X[t+1];
 //           x of tile t+4 -> registers (helpers 6, 7);
-//           tables of tile t+1 from its dt (which rode with stage t) -> T[t+1];
+//           tables of tile t+1 from its dt (which rode with stage t) -> T[t+1]
+//           (helpers 6, 7);
 //           blocks of M_t from stage t and T[t] -> M[t] (all four).
 // So stage t is read in step t only, X[t] holds x_t in step t and y_t from
 // step t+1 to t+2, M_t and the tables are produced one step before their
@@ -596,23 +597,25 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 *(lds_u32x4 *)(uintptr_t)p = u32x4{0, 0, 0, 0};
             }
         }
-        // scan tables of a tile from delta (lane j = token j, 0 past the end):
-        // helper hw writes table hw: S = s_j, E = 2^(s_j), Dl = delta_j,
-        // W = delta_j 2^(s_last - s_j)
+        // scan tables of a tile from delta (lane j = token j, 0 past the end),
+        // written by the x helpers from one prefix sum each: hw 2 S = s_j and
+        // Dl = delta_j, hw 3 E = 2^(s_j) and W = delta_j 2^(s_last - s_j). (The
+        // C/B helpers, the last to reach the barrier, compute none: one table
+        // per helper timed 2-5 % slower.)
         auto tables = [&](float *tab, float d) __attribute__((always_inline)) {
             const float v = wave_scan(d * a2);
-            const float e3 = readlane(v, 63);
-            float o;
-            if (hw == 0) o = v;
-            else if (hw == 1) o = fast_exp2(v);
-            else if (hw == 2) o = d;
-            else o = d * fast_exp2(e3 - v);
-            tab[64 * hw + lane] = o;
+            if (hw == 2) {
+                tab[lane] = v;
+                tab[128 + lane] = d;
+            } else {
+                tab[64 + lane] = fast_exp2(v);
+                tab[192 + lane] = d * fast_exp2(readlane(v, 63) - v);
+            }
         };
         {
             float d = 0.0f;
             if (lane < clamp_len(L)) d = softplus_hw(a.dt[(tb + lane) * H + h] + bias);
-            tables(tabs, d);
+            if (hw >= 2) tables(tabs, d);
         }
         // Decay-matrix blocks (I, J), J <= I: D[j][i] = B_j . C_i over n, then
         // M[i][j] = D 2^(s_i - s_j) delta_j (0 for j > i) + D_h [i == j].
@@ -661,7 +664,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         // (from the dt that rode with stage t) and this helper's blocks of M_t
         auto compute = [&](auto slot_c, int t) __attribute__((always_inline)) {
             constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % 3;
-            if (t + 1 < ntot) {   // tables of tile t + 1
+            if (hw >= 2 && t + 1 < ntot) {   // tables of tile t + 1
                 const int jn = kMulti ? ((ut + 1 == nt) ? 0 : ut + 1) : t + 1;
                 const int Ln = clamp_len(L - jn * kTile);
                 tables(tabs + NEXT * TAB, softplus_hw(sDt[SLOT * 64 + lane] + bias + (lane < Ln ? 0.0f : -INFINITY)));
@@ -722,7 +725,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
         using B2c = std::integral_constant<int, 2>;
         auto next_tables = [&](auto slot_c, int t) __attribute__((always_inline)) {   // tables of tile t + 1
             constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % 3;
-            if (t + 1 < ntot) {
+            if (hw >= 2 && t + 1 < ntot) {
                 const int jn = kMulti ? ((ut + 1 == nt) ? 0 : ut + 1) : t + 1;
                 const int Ln = clamp_len(L - jn * kTile);
                 tables(tabs + NEXT * TAB, softplus_hw(sDt[SLOT * 64 + lane] + bias + (lane < Ln ? 0.0f : -INFINITY)));
