@@ -442,7 +442,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) cf[I][c] = rf16(ac[c] + OS + 16 * RB * I);
-            if constexpr (kMulti) make_hf();   // (h_in may be a new head's initial state, loaded late in the last step)
+            if constexpr (kMulti) make_hf();   // (h_in may be a new head's initial state, loaded at the end of the last step)
             __builtin_amdgcn_sched_barrier(0);
             f32x4 acc[4];
 #pragma unroll
@@ -508,8 +508,19 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                 if (dsl >= 0) export_state(dsl);
             }
             if constexpr (kMulti) {
-                if (++jt == nt) {   // the head's last tile: its final state out, the next head's initial state in
+                if (++jt == nt) {   // the head's last tile: the next head's initial state in, this head's final state out
+                    // (the loads are issued before the stores, so that waiting for
+                    // them, vector memory retiring in issue order, does not also
+                    // wait for the stores; the operands of the step's products are
+                    // dead here, so the loaded state has registers of its own)
                     jt = 0;
+                    f32x4 nx[8];
+                    if (kh + 1 < K) {
+                        const float *src = a.init + state_row + (kh + 1) * head_state;
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            nx[u] = has_init ? *reinterpret_cast<const f32x4 *>(src + n_of(u)) : f32x4{0, 0, 0, 0};
+                    }
 #pragma unroll
                     for (int u = 0; u < 8; ++u) *reinterpret_cast<f32x4 *>(fd + n_of(u)) = st[u];
                     if (++kh < K) {
@@ -519,10 +530,8 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                         ex_chunk = c0;
                         ex_win = c0;
                         slots = slots0;
-                        const float *src = a.init + state_row + kh * head_state;
 #pragma unroll
-                        for (int u = 0; u < 8; ++u)
-                            st[u] = has_init ? *reinterpret_cast<const f32x4 *>(src + n_of(u)) : f32x4{0, 0, 0, 0};
+                        for (int u = 0; u < 8; ++u) st[u] = nx[u];
                     }
                 }
             }
