@@ -228,6 +228,45 @@ def test_prefix_cache_checkpoint_and_resume():
     assert torch.equal(fin_t, fin), "resumed final state differs"
 
 
+def test_multi_head_block_checkpoints():
+    """Block checkpoints through the plan in workgroups that walk 8 heads of one
+    (sequence, group) (64 short sequences, 128 heads in 8 groups, chunk 64, block
+    128): each head restarts the checkpoint schedule at its sequence's first
+    chunk, and only block-end chunks have a slot. The plan is bit-exact and every
+    written slot matches the oracle's chunk state, for every head."""
+    rng = np.random.default_rng(31)
+    L = [int(v) for v in rng.integers(1, 400, size=64)]
+    L[:5] = [0, 1, 128, 129, 64]
+    w = make_inputs(L, 128, 64, 128, 8, 64, dtype="bf16", init_seqs=[i for i in range(64) if i % 3],
+                    seed=31, block_size=128)
+    d = to_dev(w)
+    meta = ssd.varlen_metadata(d["cu_seqlens"], w.chunk_size, total_tokens=w.total_tokens)
+    bt = w.block_table
+    nslots = int(bt.numel())
+    ckpt_src, dst = ssd.export_chunk_states(meta, bt, w.block_size, num_slots=nslots)
+    ref_src, ref_dst = oracle.checkpoint_plan(w.cu_seqlens.numpy(), meta.seq_chunk_start.cpu().numpy(),
+                                              meta.max_chunks, bt.numpy(), w.block_size, w.chunk_size)
+    assert np.array_equal(ckpt_src.cpu().numpy(), ref_src)
+    assert np.array_equal(dst.cpu().numpy(), ref_dst)
+    cache = torch.full((nslots, w.nheads, w.headdim, w.dstate), float("nan"), device="cuda")
+    _, y, fin, _ = gpu_run(w, export="cache", state_cache=cache, chunk_state_dst=dst, d=d)
+    assert int(meta.error_flag.item()) == 0
+    tol = TOL[w.dtype]
+    yr, fr, cr = oracle_run(w, chunk_size=w.chunk_size)
+    check_close(y, yr, tol, "multi-head block y")
+    check_close(fin, fr, tol, "multi-head block final")
+    written = 0
+    for s in range(len(L)):
+        for k in range(bt.shape[1]):
+            src = int(ref_src[s, k])
+            if src < 0:
+                continue
+            check_close(cache[int(bt[s, k])][None], cr[src:src + 1], tol, f"slot s={s} k={k}")
+            written += 1
+    assert written > 64
+    log(f"multi-head block checkpoints: {written} slots checked")
+
+
 def test_dense_export_scatter_equals_at_source():
     w = make_inputs([700, 130, 0, 257], 4, 64, 64, 2, 64, dtype="bf16", init_seqs=[1, 3], seed=7,
                     block_size=128, num_slots=40)
