@@ -228,6 +228,19 @@ def test_prefix_cache_checkpoint_and_resume():
     assert torch.equal(fin_t, fin), "resumed final state differs"
 
 
+@pytest.mark.parametrize("export", [True, False], ids=["export", "no-export"])
+def test_multi_head_two_column_tiles(export):
+    """Several heads per workgroup with headdim 128 (two 64-column tiles per head):
+    32 sequences x 64 heads in 8 groups, so each workgroup walks 4 heads of one
+    (sequence, group) and one of the two column tiles."""
+    rng = np.random.default_rng(41)
+    L = [int(v) for v in rng.integers(1, 300, size=32)]
+    L[:4] = [0, 64, 65, 1]
+    w = make_inputs(L, 64, 128, 128, 8, 64, dtype="bf16", init_seqs=[i for i in range(32) if i % 4],
+                    seed=41)
+    _full_compare(w, dense=export, what=f"multi-head P=128 export={export}")
+
+
 def test_multi_head_block_checkpoints():
     """Block checkpoints through the plan in workgroups that walk 8 heads of one
     (sequence, group) (64 short sequences, 128 heads in 8 groups, chunk 64, block
