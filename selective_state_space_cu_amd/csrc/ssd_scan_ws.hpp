@@ -876,6 +876,11 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
             auto step = [&](auto slot_c, int t) __attribute__((always_inline)) {
                 constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % 3, FETCH = (SLOT + 2) % 3;
                 step_consts();
+                // (the C/B helpers, the last to reach the barrier, issue at the
+                // chain waves' raised priority during their step work: 1-2 %
+                // faster on the three bf16 workloads; the x helpers raised too,
+                // or these above the chain waves, timed no better)
+                __builtin_amdgcn_s_setprio(1);
                 if constexpr (kInterleave) {
                     if (hw == 0) step_blocks(slot_c, WsBlocks0{});
                     else step_blocks(slot_c, WsBlocks1{});
@@ -884,6 +889,7 @@ void ssd_scan_ws_kernel(ScanArgs a, const int32_t *__restrict__ dstmap)
                     fetch(std::integral_constant<int, FETCH>{});            // tile t + 2
                     compute(slot_c, t);
                 }
+                __builtin_amdgcn_s_setprio(0);
                 wait_vm_stage<SH::kBcWait, NEXT>();                         // stage t + 1 landed
                 if constexpr (kMulti) next_pos(us, ut);
             };
