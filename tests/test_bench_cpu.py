@@ -90,3 +90,33 @@ def test_conv1d_algorithmic_bytes():
     want = 2 * 35576 * 5120 * 2 + 8 * 3 * 5120 * 2 + 5120 * 4 * 4 + 5120 * 4
     assert want == 728_944_640
     assert bench.conv1d_work(b) == want
+
+
+def test_gdn_algorithmic_bytes():
+    """4 x 8894 tokens; q and k (16 key heads x 128 bf16) read once, v read and o
+    written (32 value heads x 128 bf16), gate and beta (32 float32 each); no
+    initial states, 4 final states and 140 block checkpoints (35 blocks of 256
+    tokens per sequence) of 32 x 128 x 128 float32. Shapes only: the tensors live
+    on the meta device, so nothing is drawn."""
+    from types import SimpleNamespace
+
+    import torch
+
+    from selective_state_space_cu_amd.workloads import GDN_CONFIG as c
+    assert (c["lengths"], c["nheads"], c["nkheads"], c["dk"], c["dv"], c["chunk_size"], c["block_size"]) == \
+        ([8894] * 4, 32, 16, 128, 128, 64, 256)
+    T = sum(c["lengths"])
+    w = SimpleNamespace(q=torch.empty(T, 16, 128, device="meta"), v=torch.empty(T, 32, 128, device="meta"),
+                        has_initial_state=torch.zeros(4, dtype=torch.bool), nseqs=4, lengths=c["lengths"],
+                        chunk_size=64)
+    per_token = 2 * 16 * 128 * 2 + 2 * 32 * 128 * 2 + 2 * 32 * 4
+    state = 32 * 128 * 128 * 4
+    want = 35576 * per_token + 4 * state + 140 * state
+    got, flops = bench.gdn_work(w, 140)
+    assert got == want == 1_185_413_120
+    # flops: 138 full chunks and one of 62 tokens per sequence; the full chunk's count
+    # by hand (lower triangles of 2080 entries)
+    full = 2 * 32 * (2 * 2080 * 128 + 2 * 64 * 128 * 128 + 2 * 2080 * 128 + 64 * 128 * 128)
+    assert full == 269_484_032
+    tail = 2 * 32 * (2 * 1953 * 128 + 2 * 62 * 128 * 128 + 2 * 1953 * 128 + 62 * 128 * 128)
+    assert flops == 4 * (138 * full + tail)
