@@ -120,3 +120,28 @@ def test_gdn_algorithmic_bytes():
     assert full == 269_484_032
     tail = 2 * 32 * (2 * 1953 * 128 + 2 * 62 * 128 * 128 + 2 * 1953 * 128 + 62 * 128 * 128)
     assert flops == 4 * (138 * full + tail)
+
+
+def test_other_prefill_workloads_algorithmic_bytes():
+    """The 8-sequence layer: 15843 tokens, per token x and y (80 heads x 64 bf16
+    each), dt (80 float32), B and C (1 group x 128 bf16 each); 4 initial and 8
+    final states of 80 x 64 x 128 float32. The 64-sequence batch: 17252 tokens,
+    per token x and y (128 x 64 bf16), dt (128 float32), B and C (8 x 128 bf16);
+    64 initial and 64 final states of 128 x 64 x 128 float32. Shapes only, from
+    the workload table, so nothing is drawn."""
+    from types import SimpleNamespace
+
+    from selective_state_space_cu_amd.workloads import CONFIGS
+
+    def shapes(i):
+        c = CONFIGS[i]
+        has = np.zeros(len(c["lengths"]), dtype=bool)
+        has[c["init_seqs"]] = True
+        return SimpleNamespace(total_tokens=sum(c["lengths"]), nheads=c["nheads"], headdim=c["headdim"],
+                               dstate=c["dstate"], ngroups=c["ngroups"], dtype=c["dtype"], has_initial_state=has,
+                               nseqs=len(c["lengths"]), lengths=c["lengths"], chunk_size=c["chunk_size"])
+
+    want2 = 15843 * (2 * 80 * 64 * 2 + 80 * 4 + 2 * 128 * 2) + (4 + 8) * 80 * 64 * 128 * 4
+    assert bench.algorithmic_work(shapes(2), 0)[0] == want2 == 369_103_296
+    want3 = 17252 * (2 * 128 * 64 * 2 + 128 * 4 + 2 * 8 * 128 * 2) + (64 + 64) * 128 * 64 * 128 * 4
+    assert bench.algorithmic_work(shapes(3), 0)[0] == want3 == 1_181_681_664
