@@ -124,7 +124,12 @@ def scan_kernel_name(config):
 
 
 def algorithmic_work(w, n_ckpt):
-    """Bytes the method must move and flops it must do for one pass."""
+    """Bytes the method must move and flops it must do for one pass. Bytes: x and
+    y once per token and head, dt once per token and head (float32), B and C once
+    per token and group, each flagged initial state read, each final state and
+    block checkpoint written, once. Flops: per chunk of Lc tokens, the C B^T lower
+    triangle per group and its application to x per head, and the two Lc x P x N
+    products per head (chunk state and the inter-chunk output term)."""
     T, H, P, N, G = w.total_tokens, w.nheads, w.headdim, w.dstate, w.ngroups
     sx = 2 if w.dtype == "bf16" else 4
     n_init = int(w.has_initial_state.sum())
@@ -560,8 +565,9 @@ def main():
                                          workload=args.workload)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(see DESIGN.md for how the scan would shard)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (sequences and "
+              "head groups are independent in the scan, so a batch would shard by either "
+              "across GPUs with no collective inside the step)", file=sys.stderr)
         sys.exit(2)
 
     if args.workload == "decode":
